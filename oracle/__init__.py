@@ -1,0 +1,214 @@
+"""fp64 CPU oracle for differential softmax attention.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+cpu_baseline leg are the only callers. The product path never imports this
+package, and this package imports nothing from the product.
+
+It wraps ``diffattn_oracle.c`` (plain loops in double) and arranges numpy
+arrays into the per-head blocks the C code takes. Layouts follow the product's
+token-major convention: ``[batch, tokens, heads, dim]``.
+
+What it computes, with the pages it follows:
+  - ``lambda_init``, ``lam``: "Differential Transformer: Noise-Canceling
+    Attention by Subtraction", section "Making lambda learnable and stable".
+  - ``v1_forward``, ``decode``: the DiffAttn formula of "The mechanism" on the
+    same page and of "softmax can't say zero, so it subtracts", section
+    "The mechanism, exactly"; the epilogue of "The row no longer sums to one".
+  - ``v2_forward``: "softmax can't say zero, so it subtracts", section
+    "DIFF V2: what the authors changed", and the "Differential Transformer V2"
+    write-up (paired heads of one GQA group, contiguous group heads).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build(force=True)
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_lambda_init.restype = ctypes.c_double
+        lib.oracle_lambda_init.argtypes = [ctypes.c_int]
+        lib.oracle_lambda.restype = None
+        lib.oracle_lambda.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
+        lib.oracle_diff_head.restype = ctypes.c_int
+        lib.oracle_diff_head.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, dp, ctypes.c_int,
+                                         ctypes.c_double, ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.c_int, dp]
+        lib.oracle_rmsnorm_scale.restype = None
+        lib.oracle_rmsnorm_scale.argtypes = [dp, ctypes.c_int, ctypes.c_int, dp,
+                                             ctypes.c_double, ctypes.c_double]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def lambda_init(layer: int) -> float:
+    """0.8 - 0.6 exp(-0.3 (l - 1)), l counted from 1."""
+    return float(_load().oracle_lambda_init(int(layer)))
+
+
+def lam(lq1, lk1, lq2, lk2, layer: int) -> np.ndarray:
+    """exp(lq1.lk1) - exp(lq2.lk2) + lambda_init(layer), per row of [n, dim]."""
+    a = [_f64(x) for x in (lq1, lk1, lq2, lk2)]
+    if a[0].ndim == 1:
+        a = [x[None, :] for x in a]
+    n, dim = a[0].shape
+    out = np.empty(n, dtype=np.float64)
+    _load().oracle_lambda(*(_ptr(x) for x in a), n, dim, int(layer), _ptr(out))
+    return out
+
+
+def _head(q1, q2, k1, k2, v, lam_rows, causal, scale, rows):
+    """q1, q2: [nq, d]; k1, k2: [nk, d]; v: [nk, dv]; lam_rows: [nq]."""
+    q1, q2, k1, k2, v, lam_rows = (_f64(x) for x in (q1, q2, k1, k2, v, lam_rows))
+    nq, d = q1.shape
+    nk, dv = v.shape
+    if rows is None:
+        nrows, rp = nq, None
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        nrows, rp = rows.size, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    out = np.empty((nrows, dv), dtype=np.float64)
+    rc = _load().oracle_diff_head(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), nq, nk, d, dv,
+                                  _ptr(lam_rows), int(bool(causal)), float(scale), rp, nrows,
+                                  _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle: a requested row sees no key (or allocation failed)")
+    return out
+
+
+def _epilogue(o, g, eps, lambda_init_value):
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    nrows, dv = o.shape
+    gkeep = None if g is None else _f64(g)   # keep the buffer alive across the call
+    gp = None if gkeep is None else _ptr(gkeep)
+    _load().oracle_rmsnorm_scale(_ptr(o), nrows, dv, gp, float(eps), float(lambda_init_value))
+    return o
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / np.sqrt(d)
+
+
+def v1_forward(q1, q2, k1, k2, v, lam_heads, causal=True, epilogue=True, lambda_init_value=0.8,
+               g=None, eps=1e-5, scale=None, rows=None):
+    """DIFF V1 forward.
+
+    q1, q2: [B, Nq, H, d]; k1, k2: [B, Nk, H, d]; v: [B, Nk, H, dv]; lam_heads: [H].
+    rows: None for every output, else an int array [n, 3] of (b, h, i).
+    Returns [B, Nq, H, dv] (rows is None) or [n, dv].
+    """
+    q1, q2, k1, k2, v = (np.asarray(x) for x in (q1, q2, k1, k2, v))
+    B, Nq, H, d = q1.shape
+    dv = v.shape[3]
+    s = default_scale(d) if scale is None else float(scale)
+    lam_heads = np.asarray(lam_heads, dtype=np.float64).reshape(-1)
+    if rows is None:
+        out = np.empty((B, Nq, H, dv), dtype=np.float64)
+        for b in range(B):
+            for h in range(H):
+                o = _head(q1[b, :, h], q2[b, :, h], k1[b, :, h], k2[b, :, h], v[b, :, h],
+                          np.full(Nq, lam_heads[h]), causal, s, None)
+                if epilogue:
+                    o = _epilogue(o, g, eps, lambda_init_value)
+                out[b, :, h] = o
+        return out
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    out = np.empty((rows.shape[0], dv), dtype=np.float64)
+    for b in np.unique(rows[:, 0]):
+        for h in np.unique(rows[rows[:, 0] == b, 1]):
+            sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == h))[0]
+            o = _head(q1[b, :, h], q2[b, :, h], k1[b, :, h], k2[b, :, h], v[b, :, h],
+                      np.full(Nq, lam_heads[h]), causal, s, rows[sel, 2])
+            if epilogue:
+                o = _epilogue(o, g, eps, lambda_init_value)
+            out[sel] = o
+    return out
+
+
+def decode(q1, q2, k1c, k2c, vc, lam_heads, cache_lens=None, epilogue=True, lambda_init_value=0.8,
+           g=None, eps=1e-5, scale=None, pairs=None):
+    """DIFF V1 decode: one query per (b, h) against the first cache_lens[b] cached keys.
+
+    q1, q2: [B, H, d]; k1c, k2c: [B, L, H, d]; vc: [B, L, H, dv].
+    pairs: None for every (b, h), else an int array [n, 2] of (b, h); returns [B, H, dv] or [n, dv].
+    """
+    q1, q2 = np.asarray(q1), np.asarray(q2)
+    B, H, d = q1.shape
+    L = k1c.shape[1]
+    dv = vc.shape[3]
+    s = default_scale(d) if scale is None else float(scale)
+    lens = np.full(B, L, dtype=np.int64) if cache_lens is None else np.asarray(cache_lens, np.int64)
+    lam_heads = np.asarray(lam_heads, dtype=np.float64).reshape(-1)
+    if pairs is None:
+        pairs = np.array([(b, h) for b in range(B) for h in range(H)], dtype=np.int64)
+        full = True
+    else:
+        pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+        full = False
+    out = np.empty((pairs.shape[0], dv), dtype=np.float64)
+    for n, (b, h) in enumerate(pairs):
+        n_b = int(lens[b])
+        o = _head(q1[b, h][None], q2[b, h][None], k1c[b, :n_b, h], k2c[b, :n_b, h],
+                  vc[b, :n_b, h], np.array([lam_heads[h]]), False, s, None)
+        if epilogue:
+            o = _epilogue(o, g, eps, lambda_init_value)
+        out[n] = o[0]
+    return out.reshape(B, H, dv) if full else out
+
+
+def v2_forward(q, k, v, lam_tok, causal=True, scale=None, rows=None):
+    """DIFF V2 forward (no per-head norm).
+
+    q: [B, N, 2h, d]; k, v: [B, N, h_kv, d]; lam_tok: [B, N, h] (used as given).
+    Pair p takes query heads 2p (map 1) and 2p+1 (map 2); both read KV head
+    2p // (2h / h_kv), since the heads of one GQA group are contiguous.
+    rows: None, or an int array [n, 3] of (b, p, i). Returns [B, N, h, d] or [n, d].
+    """
+    q, k, v, lam_tok = (np.asarray(x) for x in (q, k, v, lam_tok))
+    B, N, H2, d = q.shape
+    h = H2 // 2
+    hkv = k.shape[2]
+    group = H2 // hkv
+    s = default_scale(d) if scale is None else float(scale)
+    if rows is None:
+        out = np.empty((B, N, h, v.shape[3]), dtype=np.float64)
+        for b in range(B):
+            for p in range(h):
+                g = (2 * p) // group
+                out[b, :, p] = _head(q[b, :, 2 * p], q[b, :, 2 * p + 1], k[b, :, g], k[b, :, g],
+                                     v[b, :, g], lam_tok[b, :, p], causal, s, None)
+        return out
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    out = np.empty((rows.shape[0], v.shape[3]), dtype=np.float64)
+    for b in np.unique(rows[:, 0]):
+        for p in np.unique(rows[rows[:, 0] == b, 1]):
+            sel = np.nonzero((rows[:, 0] == b) & (rows[:, 1] == p))[0]
+            g = (2 * p) // group
+            out[sel] = _head(q[b, :, 2 * p], q[b, :, 2 * p + 1], k[b, :, g], k[b, :, g],
+                             v[b, :, g], lam_tok[b, :, p], causal, s, rows[sel, 2])
+    return out
