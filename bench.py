@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the differential-attention hot path on one MI355X.
+
+A step is one pass of the path over the V1 prefill workload (B=4, H=16, N=2048, d=64, dv=128,
+causal, RMSNorm * (1 - lambda_init) epilogue): the lambda kernel for the layer, then the fused
+forward. Inputs are synthetic (seeded) and resident in HBM before timing starts. Prints ONE JSON
+line on stdout; progress goes to stderr.
+
+Also measured in the same run (reported under "secondary"): the 32K-token prefill with a planted
+needle, the 64K-entry decode (GB/s against HBM) and the V2 GQA prefill; and the fp64 oracle on a
+bounded sample of the main workload, timed on the host cores ("cpu_baseline").
+
+Throughput counts algorithmic work only: 768 flop per visible (query, key) pair for V1 (two
+QK^T products of width 64 and two PV products of width 128), 512 per visible pair and query head
+for V2, and for decode the bytes of K1, K2 and V read once (512 B per cached token per head).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "diff-attn fwd TFLOP/s (bf16, N=2K/32K) + decode GB/s; % of MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+FLOP_PER_PAIR_V1 = 768
+FLOP_PER_PAIR_V2 = 512
+DECODE_BYTES_PER_TOKEN = 2 * (64 + 64 + 128)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(n):
+    return n * (n + 1) // 2
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "differential_softmax_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, files):
+    """HBM traffic per launch from committed rocprofv3 PMC summaries, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash(files):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, reps, torch):
+    """Average device time per call of fn, from events around each call on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return sum(ms) / len(ms), min(ms)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--secondary", default="32k,decode,v2",
+                    help="comma list of extra workloads to time (32k, decode, v2) or 'none'")
+    ap.add_argument("--secondary-reps", type=int, default=10)
+    ap.add_argument("--cpu-baseline", type=int, default=1, help="time the fp64 oracle on a sample (1) or not (0)")
+    ap.add_argument("--copy-calibration", type=int, default=1,
+                    help="run a 1 GiB device copy (reference kernel for HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
+              "the differential-attention path here has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import differential_softmax_attention_amd as da
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = da.lib()
+
+    # ---------------- main workload: V1 prefill 2K ----------------
+    cfg = W.V1_PREFILL_2K
+    log(f"[bench] generating inputs: {cfg.name}")
+    x = W.v1_inputs(cfg, device=dev)
+    vecs = [x[k].to(dev).contiguous() for k in ("lq1", "lk1", "lq2", "lk2")]
+    lam = torch.empty(cfg.H, dtype=torch.float32, device=dev)
+    out = torch.empty((cfg.B, cfg.N, cfg.H, cfg.dv), dtype=torch.bfloat16, device=dev)
+    li = da.lambda_init(cfg.layer)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    # marshal the C-ABI arguments once; each step is two library calls
+    lam_args = (*(v.data_ptr() for v in vecs), cfg.H, cfg.d, cfg.layer, lam.data_ptr(), stream)
+    fwd_args = (da.DIFFATTN_BF16, *(da._t4(x[k]) for k in ("q1", "q2", "k1", "k2", "v")), cfg.B, cfg.H,
+                cfg.N, cfg.N, cfg.d, cfg.dv, lam.data_ptr(), li, 1, da.EPI_RMSNORM_SCALE, None, 1e-5, 0.0,
+                da._t4(out), stream)
+
+    def lam_step():
+        da._check(L.diffattn_lambda(*lam_args))
+
+    def fwd_step():
+        da._check(L.diffattn_fwd(*fwd_args))
+
+    for _ in range(args.warmup):
+        lam_step()
+        fwd_step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        lam_step()
+        a.record()
+        fwd_step()
+        b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = [a.elapsed_time(b) for a, b in evs]
+    fwd_avg_ms = sum(fwd_ms) / len(fwd_ms)
+    flops = FLOP_PER_PAIR_V1 * cfg.B * cfg.H * causal_pairs(cfg.N)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (fwd_avg_ms * 1e-3) / 1e12
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us, fused forward kernel {fwd_avg_ms * 1e3:.1f} us "
+        f"(min {min(fwd_ms) * 1e3:.1f}) -> {achieved:.1f} TFLOP/s")
+    traffic = load_traffic("v1_prefill_2k", ["fwd_mfma.hip", "common.hpp"])
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded torch generators; iid N(0,1) inputs, lambda vectors N(0, 0.1^2))",
+        "config": {"workload": cfg.name, "batch": cfg.B, "heads": cfg.H, "seq_len": cfg.N, "d": cfg.d,
+                   "dv": cfg.dv, "causal": True, "epilogue": "rmsnorm*(1-lambda_init)", "layer": cfg.layer,
+                   "step": "diffattn_lambda + diffattn_fwd",
+                   "flop_per_step": flops, "flop_per_visible_pair": FLOP_PER_PAIR_V1},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "fwd_mfma_kernel<64,V1,causal,epilogue>",
+                     "kernel_avg_us": round(fwd_avg_ms * 1e3, 2)},
+    }
+    del x
+
+    # ---------------- secondary workloads ----------------
+    secondary = {}
+    which = [] if args.secondary == "none" else args.secondary.split(",")
+    if "32k" in which:
+        c3 = W.V1_PREFILL_32K
+        log(f"[bench] {c3.name}")
+        x3 = W.v1_inputs(c3, device=dev)
+        lam3 = da.diffattn_lambda(*(x3[k].to(dev) for k in ("lq1", "lk1", "lq2", "lk2")), c3.layer)
+        o3 = torch.empty((c3.B, c3.N, c3.H, c3.dv), dtype=torch.bfloat16, device=dev)
+        f3 = lambda: da.diffattn_fwd(x3["q1"], x3["q2"], x3["k1"], x3["k2"], x3["v"], lam3, causal=True,
+                                     epilogue=True, lambda_init_value=da.lambda_init(c3.layer), out=o3)
+        f3()
+        torch.cuda.synchronize()
+        avg, mn = time_launches(f3, args.secondary_reps, torch)
+        fl3 = FLOP_PER_PAIR_V1 * c3.B * c3.H * causal_pairs(c3.N)
+        tf = fl3 / (avg * 1e-3) / 1e12
+        secondary["v1_prefill_32k"] = {"workload": c3.name, "kernel_avg_ms": round(avg, 4),
+                                       "kernel_min_ms": round(mn, 4), "flop": fl3, "TFLOP/s": round(tf, 2),
+                                       "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s")
+        del x3, o3
+    if "v2" in which:
+        c5 = W.V2_GQA_8K
+        log(f"[bench] {c5.name}")
+        x5 = W.v2_inputs(c5, device=dev)
+        o5 = torch.empty((c5.B, c5.N, c5.hq // 2, c5.d), dtype=torch.bfloat16, device=dev)
+        f5 = lambda: da.diffattn_v2_fwd(x5["q"], x5["k"], x5["v"], x5["lam"], causal=True, out=o5)
+        f5()
+        torch.cuda.synchronize()
+        avg, mn = time_launches(f5, args.secondary_reps, torch)
+        fl5 = FLOP_PER_PAIR_V2 * c5.B * c5.hq * causal_pairs(c5.N)
+        tf = fl5 / (avg * 1e-3) / 1e12
+        secondary["v2_gqa_8k"] = {"workload": c5.name, "kernel_avg_ms": round(avg, 4), "kernel_min_ms": round(mn, 4),
+                                  "flop": fl5, "TFLOP/s": round(tf, 2),
+                                  "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s")
+        del x5, o5
+    if "decode" in which:
+        c4 = W.V1_DECODE_64K
+        log(f"[bench] {c4.name} (generating the cache on the device)")
+        x4 = W.decode_inputs(c4, device=dev)
+        lam4 = x4["lam"].to(dev)
+        ws = torch.empty(da.diffattn_decode_workspace_size(c4.B, c4.H, c4.L, c4.dv), dtype=torch.uint8, device=dev)
+        o4 = torch.empty((c4.B, c4.H, c4.dv), dtype=torch.bfloat16, device=dev)
+        f4 = lambda: da.diffattn_decode(x4["q1"], x4["q2"], x4["k1"], x4["k2"], x4["v"], lam4, epilogue=True,
+                                        lambda_init_value=c4.lambda_init, workspace=ws, out=o4)
+        f4()
+        torch.cuda.synchronize()
+        avg, mn = time_launches(f4, args.secondary_reps, torch)
+        nbytes = DECODE_BYTES_PER_TOKEN * c4.B * c4.H * c4.L
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        secondary["v1_decode_64k"] = {"workload": c4.name, "split_plus_reduce_avg_ms": round(avg, 4),
+                                      "min_ms": round(mn, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+                                      "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench]   {avg:.3f} ms -> {gbs:.0f} GB/s")
+        del x4, ws, o4
+    if secondary:
+        result["secondary"] = secondary
+
+    if args.copy_calibration:
+        # a plain 1 GiB device-to-device copy: the reference kernel for HBM byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------- CPU baseline: the fp64 oracle on a bounded sample ----------------
+    if args.cpu_baseline:
+        import oracle
+        x = W.v1_inputs(cfg, device="cpu")
+        host = {k: x[k].float().numpy() for k in ("q1", "q2", "k1", "k2", "v")}
+        lam_ref = oracle.lam(*(x[k].double().numpy() for k in ("lq1", "lk1", "lq2", "lk2")), cfg.layer)
+        units_done, t_cpu, pairs = 0, 0.0, 0
+        for b in range(cfg.B):
+            for h in range(cfg.H):
+                rows = np.array([(b, h, i) for i in range(cfg.N)])
+                s = time.perf_counter()
+                oracle.v1_forward(host["q1"], host["q2"], host["k1"], host["k2"], host["v"], lam_ref,
+                                  causal=True, epilogue=True,
+                                  lambda_init_value=oracle.lambda_init(cfg.layer), rows=rows)
+                t_cpu += time.perf_counter() - s
+                units_done += 1
+                pairs += causal_pairs(cfg.N)
+                if t_cpu > 20.0:
+                    break
+            if t_cpu > 20.0:
+                break
+        cpu_tf = FLOP_PER_PAIR_V1 * pairs / t_cpu / 1e12
+        result["cpu_baseline"] = {"value": round(cpu_tf, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{units_done} of {cfg.B * cfg.H} (batch, head) units of the main "
+                                            f"workload, every row ({pairs} visible pairs), fp64, "
+                                            f"{t_cpu:.1f} s (capped at 20 s)"}
+        log(f"[bench] oracle: {units_done} units in {t_cpu:.1f} s -> {cpu_tf * 1e3:.3f} GFLOP/s "
+            f"on {oracle.num_threads()} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+"""Python binding of libdiffattn: differential softmax attention on MI355X (gfx950).
+
+Argument marshalling only. Every function builds the C-ABI argument list from torch tensors
+(device pointer, element strides) and calls the library of the same name; all arithmetic runs in
+the library's HIP kernels on the tensors' device, on torch's current stream. Tensors use the
+token-major layout [batch, tokens, heads, dim] with a contiguous last dimension.
+
+The library must be built (``python -m differential_softmax_attention_amd.build`` or
+``__graft_entry__.build()``); nothing here falls back to another implementation, and calling an
+op without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdiffattn.so")
+
+DIFFATTN_OK = 0
+DIFFATTN_ERR_ARG = 1
+DIFFATTN_ERR_UNSUPPORTED = 2
+DIFFATTN_ERR_WORKSPACE = 3
+DIFFATTN_ERR_HIP = 4
+_STATUS_NAMES = {1: "ERR_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE", 4: "ERR_HIP"}
+
+DIFFATTN_F32 = 0
+DIFFATTN_BF16 = 1
+EPI_NONE = 0
+EPI_RMSNORM_SCALE = 1
+
+# Every symbol the header declares (tests check the library exports all of them).
+EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "diffattn_lambda",
+            "diffattn_fwd", "diffattn_decode_workspace_size", "diffattn_decode", "diffattn_v2_fwd")
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Tensor(ctypes.Structure):
+    """diffattn_tensor: base pointer and batch / token / head strides in elements."""
+    _fields_ = [("ptr", ctypes.c_void_p), ("s_batch", ctypes.c_int64), ("s_seq", ctypes.c_int64),
+                ("s_head", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdiffattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m differential_softmax_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        T, vp, i, f, sz = Tensor, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.diffattn_last_error.restype = ctypes.c_char_p
+        L.diffattn_last_error.argtypes = []
+        L.diffattn_version.restype = i
+        L.diffattn_version.argtypes = []
+        L.diffattn_lambda_init.restype = ctypes.c_double
+        L.diffattn_lambda_init.argtypes = [i]
+        L.diffattn_lambda.restype = i
+        L.diffattn_lambda.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp]
+        L.diffattn_fwd.restype = i
+        L.diffattn_fwd.argtypes = [i, T, T, T, T, T, i, i, i, i, i, i, vp, f, i, i, vp, f, f, T, vp]
+        L.diffattn_decode_workspace_size.restype = sz
+        L.diffattn_decode_workspace_size.argtypes = [i, i, i, i]
+        L.diffattn_decode.restype = i
+        L.diffattn_decode.argtypes = [i, T, T, T, T, T, vp, i, i, i, i, i, vp, f, i, vp, f, f, T, vp,
+                                      sz, vp]
+        L.diffattn_v2_fwd.restype = i
+        L.diffattn_v2_fwd.argtypes = [i, T, T, T, vp, i, i, i, i, i, i, f, T, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != DIFFATTN_OK:
+        raise DiffAttnError(status, lib().diffattn_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DIFFATTN_BF16
+    if t.dtype == torch.float32:
+        return DIFFATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _t4(x: torch.Tensor) -> Tensor:
+    """A [B, N, H, dim] tensor (last dim contiguous) as a diffattn_tensor."""
+    if x.dim() != 4:
+        raise ValueError(f"expected a 4-d [batch, tokens, heads, dim] tensor, got shape {tuple(x.shape)}")
+    if x.stride(3) != 1 and x.shape[3] > 1:
+        raise ValueError("the last dimension must be contiguous")
+    return Tensor(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def lambda_init(layer: int) -> float:
+    """0.8 - 0.6 exp(-0.3 (layer - 1)); NaN for layer < 1."""
+    return float(lib().diffattn_lambda_init(int(layer)))
+
+
+def diffattn_lambda(lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """lambda per row of four fp32 [n, dim] device tensors: exp(lq1.lk1) - exp(lq2.lk2) + lambda_init."""
+    vecs = [t if t.dim() == 2 else t.reshape(1, -1) for t in (lq1, lk1, lq2, lk2)]
+    for t in vecs:
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("lambda vectors must be contiguous float32")
+    n, dim = vecs[0].shape
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=vecs[0].device)
+    _check(lib().diffattn_lambda(*(v.data_ptr() for v in vecs), n, dim, int(layer), out.data_ptr(),
+                                 _stream(out.device)))
+    return out
+
+
+def diffattn_fwd(q1, q2, k1, k2, v, lam: torch.Tensor, causal: bool = True, epilogue: bool = True,
+                 lambda_init_value: float = 0.8, norm_w: torch.Tensor | None = None, eps: float = 1e-5,
+                 scale: float = 0.0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """DIFF V1 forward. q1, q2: [B, Nq, H, d]; k1, k2: [B, Nk, H, d]; v: [B, Nk, H, dv];
+    lam: fp32 [H] on the device. Returns [B, Nq, H, dv] in the input dtype."""
+    B, Nq, H, d = q1.shape
+    Nk, dv = k1.shape[1], v.shape[3]
+    if out is None:
+        out = torch.empty((B, Nq, H, dv), dtype=q1.dtype, device=q1.device)
+    _check(lib().diffattn_fwd(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1), _t4(k2), _t4(v), B, H, Nq, Nk,
+                              d, dv, lam.data_ptr(), float(lambda_init_value), int(bool(causal)),
+                              EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
+                              float(scale), _t4(out), _stream(q1.device)))
+    return out
+
+
+def diffattn_decode_workspace_size(batch: int, heads: int, cache_len: int, dv: int) -> int:
+    return int(lib().diffattn_decode_workspace_size(batch, heads, cache_len, dv))
+
+
+def diffattn_decode(q1, q2, k1c, k2c, vc, lam: torch.Tensor, cache_lens: torch.Tensor | None = None,
+                    epilogue: bool = True, lambda_init_value: float = 0.8,
+                    norm_w: torch.Tensor | None = None, eps: float = 1e-5, scale: float = 0.0,
+                    workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """DIFF V1 decode. q1, q2: [B, H, d] (or [B, 1, H, d]); caches [B, L, H, d|dv];
+    cache_lens: int32 [B] on the device or None. Returns [B, H, dv]."""
+    if q1.dim() == 3:
+        q1, q2 = q1.unsqueeze(1), q2.unsqueeze(1)
+    B, _, H, d = q1.shape
+    L, dv = k1c.shape[1], vc.shape[3]
+    if out is None:
+        out = torch.empty((B, 1, H, dv), dtype=q1.dtype, device=q1.device)
+    elif out.dim() == 3:
+        out = out.unsqueeze(1)
+    need = diffattn_decode_workspace_size(B, H, L, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q1.device)
+    if cache_lens is not None and cache_lens.dtype != torch.int32:
+        raise ValueError("cache_lens must be int32")
+    _check(lib().diffattn_decode(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1c), _t4(k2c), _t4(vc),
+                                 _ptr(cache_lens), B, H, L, d, dv, lam.data_ptr(),
+                                 float(lambda_init_value),
+                                 EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
+                                 float(scale), _t4(out), workspace.data_ptr(), workspace.numel(),
+                                 _stream(q1.device)))
+    return out.squeeze(1)
+
+
+def diffattn_v2_fwd(q, k, v, lam: torch.Tensor, causal: bool = True, scale: float = 0.0,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """DIFF V2 forward. q: [B, N, 2h, d]; k, v: [B, N, h_kv, d]; lam: fp32 [B, N, h] contiguous.
+    Returns [B, N, h, d]."""
+    B, N, H2, d = q.shape
+    hkv = k.shape[2]
+    h = H2 // 2
+    if H2 % 2:
+        raise ValueError("q must hold an even number of heads (2h)")
+    if not (lam.is_contiguous() and lam.dtype == torch.float32 and tuple(lam.shape) == (B, N, h)):
+        raise ValueError("lam must be a contiguous float32 [B, N, h] tensor")
+    if out is None:
+        out = torch.empty((B, N, h, d), dtype=q.dtype, device=q.device)
+    _check(lib().diffattn_v2_fwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), lam.data_ptr(), B, N, h, hkv,
+                                 d, int(bool(causal)), float(scale), _t4(out), _stream(q.device)))
+    return out
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+diffattn_lambda_init = lambda_init

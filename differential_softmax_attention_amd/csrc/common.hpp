@@ -1,0 +1,60 @@
+// Device-side helpers shared by the libdiffattn kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace diffattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Value held by lane (lane ^ mask), through the LDS crossbar. `addr` = (lane ^ mask) * 4.
+__device__ __forceinline__ float lane_xor(float x, int addr) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
+}
+
+// Butterfly reductions over all 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+    const int l = lane_id();
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, lane_xor(x, (l ^ m) << 2));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    const int l = lane_id();
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += lane_xor(x, (l ^ m) << 2);
+    return x;
+}
+
+// 2^x on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// gfx950 transposing LDS read: within each group of 16 lanes, lane L supplies the address of
+// four consecutive 16-bit elements (row L of a 16x4 block M); lane i receives
+// M[4j + i/4][i%4] for j = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const bf16* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+}  // namespace diffattn

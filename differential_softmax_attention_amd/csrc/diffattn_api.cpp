@@ -1,0 +1,267 @@
+// C ABI of libdiffattn: argument validation (before any HIP call) and kernel dispatch.
+// The operations and their argument conventions are documented in include/diffattn.h.
+#include "../../include/diffattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+diffattn_status fail(diffattn_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+diffattn_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return DIFFATTN_OK;
+    return fail(DIFFATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_size(diffattn_dtype dt) { return dt == DIFFATTN_BF16 ? 2 : 4; }
+
+bool valid_dtype(diffattn_dtype dt) { return dt == DIFFATTN_F32 || dt == DIFFATTN_BF16; }
+
+// Pointer non-null and aligned to its element size; strides non-negative.
+diffattn_status check_tensor(const diffattn_tensor& t, const char* name, diffattn_dtype dt) {
+    if (!t.ptr) return fail(DIFFATTN_ERR_ARG, "%s: null pointer", name);
+    if (((uintptr_t)t.ptr) % elem_size(dt) != 0)
+        return fail(DIFFATTN_ERR_ARG, "%s: pointer not aligned to its %zu-byte element", name, elem_size(dt));
+    if (t.s_batch < 0 || t.s_seq < 0 || t.s_head < 0)
+        return fail(DIFFATTN_ERR_ARG, "%s: negative stride", name);
+    return DIFFATTN_OK;
+}
+
+// What the MFMA kernels read as 16-byte vectors: base 16-byte aligned, strides multiples of 8.
+bool vec16_ok(const diffattn_tensor& t) {
+    return ((uintptr_t)t.ptr) % 16 == 0 && t.s_batch % 8 == 0 && t.s_seq % 8 == 0 && t.s_head % 8 == 0;
+}
+
+void copy_strides(int64_t* dst, const diffattn_tensor& t) {
+    dst[0] = t.s_batch;
+    dst[1] = t.s_seq;
+    dst[2] = t.s_head;
+}
+
+float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)d); }
+
+}  // namespace
+
+extern "C" {
+
+const char* diffattn_last_error(void) { return g_last_error.c_str(); }
+
+int diffattn_version(void) { return 100; }
+
+double diffattn_lambda_init(int layer) {
+    if (layer < 1) return NAN;
+    return 0.8 - 0.6 * std::exp(-0.3 * ((double)layer - 1.0));
+}
+
+diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int n,
+                                int dim, int layer, float* lambda_out, void* stream) {
+    if (!lq1 || !lk1 || !lq2 || !lk2 || !lambda_out) return fail(DIFFATTN_ERR_ARG, "diffattn_lambda: null pointer");
+    if (n < 1 || dim < 1) return fail(DIFFATTN_ERR_ARG, "diffattn_lambda: n=%d dim=%d must be >= 1", n, dim);
+    if (layer < 1) return fail(DIFFATTN_ERR_ARG, "diffattn_lambda: layer=%d must be >= 1", layer);
+    const float li = (float)diffattn_lambda_init(layer);
+    return hip_status(diffattn::launch_lambda(lq1, lk1, lq2, lk2, n, dim, li, lambda_out, (hipStream_t)stream),
+                      "diffattn_lambda launch");
+}
+
+diffattn_status diffattn_fwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,
+                             diffattn_tensor k2, diffattn_tensor v, int batch, int heads, int seq_q, int seq_k,
+                             int d, int dv, const float* lambda, float lambda_init, int causal,
+                             diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                             diffattn_tensor out, void* stream) {
+    if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: unknown dtype %d", (int)dtype);
+    const diffattn_tensor* ts[6] = {&q1, &q2, &k1, &k2, &v, &out};
+    const char* names[6] = {"q1", "q2", "k1", "k2", "v", "out"};
+    for (int i = 0; i < 6; ++i)
+        if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
+    if (!lambda) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: lambda is null");
+    if (batch < 1 || heads < 1 || seq_q < 1 || seq_k < 1 || d < 1 || dv < 1)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: sizes must be >= 1 (batch=%d heads=%d seq_q=%d seq_k=%d d=%d dv=%d)",
+                    batch, heads, seq_q, seq_k, d, dv);
+    if (heads > 65535 || batch > 65535) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: batch and heads must be <= 65535");
+    if (causal && seq_q > seq_k)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: causal needs seq_q (%d) <= seq_k (%d)", seq_q, seq_k);
+    if (epi != DIFFATTN_EPI_NONE && epi != DIFFATTN_EPI_RMSNORM_SCALE)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: unknown epilogue %d", (int)epi);
+    if (epi == DIFFATTN_EPI_RMSNORM_SCALE && !(std::isfinite(eps) && eps >= 0.f && std::isfinite(lambda_init)))
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: eps must be finite and >= 0, lambda_init finite");
+    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: scale must be finite");
+    if (d > 256 || dv > 512)
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_fwd: d=%d dv=%d exceed the supported d <= 256, dv <= 512", d, dv);
+    const float sc = resolve_scale(scale, d);
+    hipStream_t st = (hipStream_t)stream;
+
+    const bool mfma = dtype == DIFFATTN_BF16 && d == 64 && dv == 128 && vec16_ok(q1) && vec16_ok(q2) &&
+                      vec16_ok(k1) && vec16_ok(k2) && vec16_ok(v) && vec16_ok(out);
+    if (mfma) {
+        diffattn::MfmaFwdArgs a{};
+        a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.out = out.ptr;
+        copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1); copy_strides(a.k2s, k2);
+        copy_strides(a.vs, v); copy_strides(a.os, out);
+        a.lam = lambda;
+        a.lams[0] = 0; a.lams[1] = 0; a.lams[2] = 1;
+        a.norm_w = norm_w;
+        a.batch = batch; a.heads = heads; a.seq_q = seq_q; a.seq_k = seq_k;
+        a.kv_group = 1;
+        a.causal = causal ? 1 : 0;
+        a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
+        a.eps = eps; a.lambda_init = lambda_init;
+        a.scale_log2 = sc * 1.4426950408889634f;
+        return hip_status(diffattn::launch_v1_fwd_mfma(a, st), "diffattn_fwd launch");
+    }
+    diffattn::GenericArgs a{};
+    a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.out = out.ptr;
+    copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1); copy_strides(a.k2s, k2);
+    copy_strides(a.vs, v); copy_strides(a.os, out);
+    a.q_hmul = 1; a.q1_hoff = 0; a.q2_hoff = 0; a.kv_hdiv = 1;
+    a.lam = lambda;
+    a.lams[0] = 0; a.lams[1] = 0; a.lams[2] = 1;
+    a.key_lens = nullptr;
+    a.seq_q = seq_q; a.seq_k = seq_k; a.d = d; a.dv = dv;
+    a.causal = causal ? 1 : 0;
+    a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
+    a.norm_w = norm_w; a.eps = eps; a.lambda_init = lambda_init; a.scale = sc;
+    return hip_status(diffattn::launch_generic(a, batch, heads, dtype == DIFFATTN_BF16, st), "diffattn_fwd launch");
+}
+
+size_t diffattn_decode_workspace_size(int batch, int heads, int cache_len, int dv) {
+    if (batch < 1 || heads < 1 || cache_len < 1 || dv < 1) return 0;
+    return diffattn::decode_workspace_bytes(batch, heads, cache_len, dv);
+}
+
+diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1c,
+                                diffattn_tensor k2c, diffattn_tensor vc, const int32_t* cache_lens, int batch,
+                                int heads, int cache_len, int d, int dv, const float* lambda, float lambda_init,
+                                diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                                diffattn_tensor out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_decode: unknown dtype %d", (int)dtype);
+    const diffattn_tensor* ts[6] = {&q1, &q2, &k1c, &k2c, &vc, &out};
+    const char* names[6] = {"q1", "q2", "k1c", "k2c", "vc", "out"};
+    for (int i = 0; i < 6; ++i)
+        if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
+    if (!lambda) return fail(DIFFATTN_ERR_ARG, "diffattn_decode: lambda is null");
+    if (batch < 1 || heads < 1 || cache_len < 1 || d < 1 || dv < 1)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_decode: sizes must be >= 1 (batch=%d heads=%d cache_len=%d d=%d dv=%d)",
+                    batch, heads, cache_len, d, dv);
+    if (heads > 65535 || batch > 65535) return fail(DIFFATTN_ERR_ARG, "diffattn_decode: batch and heads must be <= 65535");
+    if (epi != DIFFATTN_EPI_NONE && epi != DIFFATTN_EPI_RMSNORM_SCALE)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_decode: unknown epilogue %d", (int)epi);
+    if (epi == DIFFATTN_EPI_RMSNORM_SCALE && !(std::isfinite(eps) && eps >= 0.f && std::isfinite(lambda_init)))
+        return fail(DIFFATTN_ERR_ARG, "diffattn_decode: eps must be finite and >= 0, lambda_init finite");
+    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "diffattn_decode: scale must be finite");
+    if (d > 256 || dv > 512)
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_decode: d=%d dv=%d exceed the supported d <= 256, dv <= 512", d, dv);
+    const size_t need = diffattn_decode_workspace_size(batch, heads, cache_len, dv);
+    if (workspace_bytes < need)
+        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_decode: workspace of %zu bytes < required %zu", workspace_bytes, need);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace) % 256 != 0))
+        return fail(DIFFATTN_ERR_ARG, "diffattn_decode: workspace must be non-null and 256-byte aligned");
+    const float sc = resolve_scale(scale, d);
+    hipStream_t st = (hipStream_t)stream;
+
+    const bool split = dtype == DIFFATTN_BF16 && d == 64 && dv == 128 && vec16_ok(q1) && vec16_ok(q2) &&
+                       vec16_ok(k1c) && vec16_ok(k2c) && vec16_ok(vc);
+    if (split) {
+        diffattn::DecodeArgs a{};
+        a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1c.ptr; a.k2 = k2c.ptr; a.v = vc.ptr; a.out = out.ptr;
+        copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1c); copy_strides(a.k2s, k2c);
+        copy_strides(a.vs, vc); copy_strides(a.os, out);
+        a.cache_lens = cache_lens;
+        a.lam = lambda;
+        a.norm_w = norm_w;
+        a.ws = (float*)workspace;
+        a.batch = batch; a.heads = heads; a.cache_len = cache_len;
+        a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
+        a.eps = eps; a.lambda_init = lambda_init;
+        a.scale_log2 = sc * 1.4426950408889634f;
+        return hip_status(diffattn::launch_decode(a, st), "diffattn_decode launch");
+    }
+    diffattn::GenericArgs a{};
+    a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1c.ptr; a.k2 = k2c.ptr; a.v = vc.ptr; a.out = out.ptr;
+    copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1c); copy_strides(a.k2s, k2c);
+    copy_strides(a.vs, vc); copy_strides(a.os, out);
+    a.q_hmul = 1; a.q1_hoff = 0; a.q2_hoff = 0; a.kv_hdiv = 1;
+    a.lam = lambda;
+    a.lams[0] = 0; a.lams[1] = 0; a.lams[2] = 1;
+    a.key_lens = cache_lens;
+    a.seq_q = 1; a.seq_k = cache_len; a.d = d; a.dv = dv;
+    a.causal = 0;
+    a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
+    a.norm_w = norm_w; a.eps = eps; a.lambda_init = lambda_init; a.scale = sc;
+    return hip_status(diffattn::launch_generic(a, batch, heads, dtype == DIFFATTN_BF16, st), "diffattn_decode launch");
+}
+
+diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k, diffattn_tensor v,
+                                const float* lam, int batch, int seq, int h, int h_kv, int d, int causal, float scale,
+                                diffattn_tensor out, void* stream) {
+    if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: unknown dtype %d", (int)dtype);
+    const diffattn_tensor* ts[4] = {&q, &k, &v, &out};
+    const char* names[4] = {"q", "k", "v", "out"};
+    for (int i = 0; i < 4; ++i)
+        if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
+    if (!lam) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: lam is null");
+    if (batch < 1 || seq < 1 || h < 1 || h_kv < 1 || d < 1)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: sizes must be >= 1 (batch=%d seq=%d h=%d h_kv=%d d=%d)", batch,
+                    seq, h, h_kv, d);
+    if (batch > 65535 || h > 65535) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: batch and h must be <= 65535");
+    if ((2 * h) % h_kv != 0 || ((2 * h) / h_kv) % 2 != 0)
+        return fail(DIFFATTN_ERR_ARG,
+                    "diffattn_v2_fwd: 2h=%d query heads must split into h_kv=%d groups of an even size (a pair may not "
+                    "straddle two groups)", 2 * h, h_kv);
+    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: scale must be finite");
+    if (d > 256) return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_v2_fwd: d=%d exceeds the supported d <= 256", d);
+    const float sc = resolve_scale(scale, d);
+    hipStream_t st = (hipStream_t)stream;
+    const int group = (2 * h) / h_kv;
+    const int ppg = group / 2;
+
+    const bool mfma = dtype == DIFFATTN_BF16 && d == 128 && (ppg == 1 || ppg == 2 || ppg == 4 || ppg == 8) &&
+                      vec16_ok(q) && vec16_ok(k) && vec16_ok(v) && vec16_ok(out);
+    if (mfma) {
+        diffattn::MfmaFwdArgs a{};
+        a.q1 = q.ptr; a.q2 = q.ptr; a.k1 = k.ptr; a.k2 = k.ptr; a.v = v.ptr; a.out = out.ptr;
+        copy_strides(a.q1s, q); copy_strides(a.q2s, q); copy_strides(a.k1s, k); copy_strides(a.k2s, k);
+        copy_strides(a.vs, v); copy_strides(a.os, out);
+        a.lam = lam;
+        a.lams[0] = (int64_t)seq * h; a.lams[1] = h; a.lams[2] = 1;
+        a.norm_w = nullptr;
+        a.batch = batch; a.heads = h; a.seq_q = seq; a.seq_k = seq;
+        a.kv_group = group;
+        a.causal = causal ? 1 : 0;
+        a.epi = 0;
+        a.eps = 0.f; a.lambda_init = 0.f;
+        a.scale_log2 = sc * 1.4426950408889634f;
+        return hip_status(diffattn::launch_v2_fwd_mfma(a, st), "diffattn_v2_fwd launch");
+    }
+    diffattn::GenericArgs a{};
+    a.q1 = q.ptr; a.q2 = q.ptr; a.k1 = k.ptr; a.k2 = k.ptr; a.v = v.ptr; a.out = out.ptr;
+    copy_strides(a.q1s, q); copy_strides(a.q2s, q); copy_strides(a.k1s, k); copy_strides(a.k2s, k);
+    copy_strides(a.vs, v); copy_strides(a.os, out);
+    a.q_hmul = 2; a.q1_hoff = 0; a.q2_hoff = 1; a.kv_hdiv = group;
+    a.lam = lam;
+    a.lams[0] = (int64_t)seq * h; a.lams[1] = h; a.lams[2] = 1;
+    a.key_lens = nullptr;
+    a.seq_q = seq; a.seq_k = seq; a.d = d; a.dv = d;
+    a.causal = causal ? 1 : 0;
+    a.epi = 0;
+    a.norm_w = nullptr; a.eps = 0.f; a.lambda_init = 0.f; a.scale = sc;
+    return hip_status(diffattn::launch_generic(a, batch, h, dtype == DIFFATTN_BF16, st), "diffattn_v2_fwd launch");
+}
+
+}  // extern "C"

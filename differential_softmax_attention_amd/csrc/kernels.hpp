@@ -1,0 +1,70 @@
+// Kernel argument blocks and launchers (internal to libdiffattn; not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace diffattn {
+
+// Generic kernel: one output row per wave. Head mapping for output head h:
+//   query head of map 1 = h * q_hmul + q1_hoff, of map 2 = h * q_hmul + q2_hoff,
+//   KV head = (h * q_hmul) / kv_hdiv.
+// V1: q_hmul = 1, offsets 0, kv_hdiv = 1 (Q1/Q2 and K1/K2 are separate tensors).
+// V2: q_hmul = 2, q1_hoff = 0, q2_hoff = 1, kv_hdiv = 2h / h_kv, K1 = K2 = K.
+// lambda for (b, i, h) is lam[b * lams[0] + i * lams[1] + h * lams[2]].
+struct GenericArgs {
+    const void *q1, *q2, *k1, *k2, *v;
+    void* out;
+    int64_t q1s[3], q2s[3], k1s[3], k2s[3], vs[3], os[3];  // batch, token, head strides
+    int q_hmul, q1_hoff, q2_hoff, kv_hdiv;
+    const float* lam;
+    int64_t lams[3];
+    const int32_t* key_lens;  // per-batch key count (decode) or null
+    int seq_q, seq_k, d, dv, causal, epi;
+    const float* norm_w;
+    float eps, lambda_init, scale;
+};
+
+hipError_t launch_generic(const GenericArgs& a, int batch, int heads, bool bf16_io, hipStream_t stream);
+
+// MFMA forward kernels (bf16 in, fp32 accumulate, bf16 out).
+// V1: separate Q1/Q2/K1/K2 tensors, d = 64, dv = 128, lambda per head, optional epilogue.
+// V2: query heads 2p / 2p+1 of one tensor, shared K and V of the pair's KV head, d = dv = 128,
+//     lambda per (b, token, pair), no epilogue.
+struct MfmaFwdArgs {
+    const void *q1, *q2, *k1, *k2, *v;
+    void* out;
+    int64_t q1s[3], q2s[3], k1s[3], k2s[3], vs[3], os[3];
+    const float* lam;
+    int64_t lams[3];
+    const float* norm_w;
+    int batch, heads, seq_q, seq_k;
+    int kv_group;     // V2: query heads per KV head (2h / h_kv); V1: unused
+    int causal, epi;
+    float eps, lambda_init, scale_log2;  // softmax scale * log2(e)
+};
+
+hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
+hipError_t launch_v2_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
+
+// Split-K decode (bf16, d = 64, dv = 128).
+struct DecodeArgs {
+    const void *q1, *q2, *k1, *k2, *v;
+    void* out;
+    int64_t q1s[3], q2s[3], k1s[3], k2s[3], vs[3], os[3];
+    const int32_t* cache_lens;
+    const float* lam;
+    const float* norm_w;
+    float* ws;  // workspace: partials
+    int batch, heads, cache_len, n_splits, split_len;
+    int epi;
+    float eps, lambda_init, scale_log2;
+};
+
+int decode_num_splits(int batch, int heads, int cache_len);
+size_t decode_workspace_bytes(int batch, int heads, int cache_len, int dv);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
+                         int n, int dim, float lambda_init, float* out, hipStream_t stream);
+
+}  // namespace diffattn

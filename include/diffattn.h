@@ -1,0 +1,171 @@
+/*
+ * diffattn.h — C ABI of libdiffattn, differential softmax attention on MI355X (gfx950).
+ *
+ * The operation (DIFF Transformer attention head):
+ *
+ *   O = ( softmax(Q1 K1^T * s) - lambda * softmax(Q2 K2^T * s) ) V,   s = 1/sqrt(d) by default,
+ *
+ * with Q1, Q2, K1, K2 of width d and V of width dv (2d in the DIFF V1 model), as defined in
+ * "Differential Transformer: Noise-Canceling Attention by Subtraction", section "The mechanism",
+ * and in "Differential Transformer: softmax can't say zero, so it subtracts", section
+ * "The mechanism, exactly" (both maps are ordinary causal maps reading the same values).
+ * The V1 epilogue is a per-head RMSNorm over the dv channels times an optional weight, then a
+ * fixed multiply by (1 - lambda_init) ("softmax can't say zero", section "The row no longer sums
+ * to one"). DIFF V2 pairs query heads 2p and 2p+1 of one GQA group, takes lambda per token and
+ * pair, and drops the norm ("softmax can't say zero", section "DIFF V2: what the authors
+ * changed"; "Differential Transformer V2").
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are token-major: logical shape [batch, tokens, heads, dim]. A diffattn_tensor gives
+ *    the base pointer and the batch / token / head strides IN ELEMENTS; the dim stride is 1.
+ *    Any such strided view works (e.g. Q1 and Q2 as two halves of one packed [B,N,H,2,d] tensor).
+ *  - Pointers passed to compute entry points are DEVICE pointers on the current HIP device,
+ *    except where stated. bf16 tensors must be 16-byte aligned, and every stride a multiple of 8
+ *    elements, for the bf16 MFMA kernels; other layouts are served by the generic kernel.
+ *  - Output dtype equals input dtype. `out` must not alias any input.
+ *  - Ownership: the caller owns every buffer, the workspace and the stream. The library allocates
+ *    no device memory and keeps no state beyond a per-device properties cache.
+ *  - Execution is asynchronous on `stream` (a hipStream_t; NULL = the default stream). Results are
+ *    valid after the stream is synchronised. No entry point synchronises.
+ *  - Errors: every argument is validated BEFORE any HIP call, so a non-OK return has launched
+ *    nothing and written nothing. diffattn_last_error() returns a thread-local description of the
+ *    last non-OK status. DIFFATTN_ERR_HIP reports a failed kernel launch.
+ *  - All entry points are reentrant; calls on one stream execute in order.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DIFFATTN_OK = 0,
+    DIFFATTN_ERR_ARG = 1,          /* invalid argument: null pointer, bad size or stride */
+    DIFFATTN_ERR_UNSUPPORTED = 2,  /* valid math that no kernel of this build serves */
+    DIFFATTN_ERR_WORKSPACE = 3,    /* workspace smaller than diffattn_decode_workspace_size() */
+    DIFFATTN_ERR_HIP = 4           /* a HIP call or kernel launch failed */
+} diffattn_status;
+
+typedef enum { DIFFATTN_F32 = 0, DIFFATTN_BF16 = 1 } diffattn_dtype;
+
+typedef enum {
+    DIFFATTN_EPI_NONE = 0,          /* O as defined above */
+    DIFFATTN_EPI_RMSNORM_SCALE = 1  /* O <- O / sqrt(mean_c O_c^2 + eps) * w_c * (1 - lambda_init) */
+} diffattn_epilogue;
+
+/* A strided [batch, tokens, heads, dim] view; strides in elements, dim stride 1. */
+typedef struct {
+    void* ptr;
+    int64_t s_batch;
+    int64_t s_seq;
+    int64_t s_head;
+} diffattn_tensor;
+
+/* Thread-local text for the last non-OK status returned on this thread ("" if none). */
+const char* diffattn_last_error(void);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int diffattn_version(void);
+
+/*
+ * lambda_init(l) = 0.8 - 0.6 * exp(-0.3 * (l - 1)), layer index l >= 1 (about 0.2 at l = 1,
+ * tending to 0.8). "Noise-Canceling Attention by Subtraction", section "Making lambda learnable
+ * and stable". Host function; returns NaN for layer < 1.
+ */
+double diffattn_lambda_init(int layer);
+
+/*
+ * lambda_out[r] = exp(lq1[r] . lk1[r]) - exp(lq2[r] . lk2[r]) + lambda_init(layer), r < n.
+ * "Noise-Canceling Attention by Subtraction", section "Making lambda learnable and stable".
+ *  lq1, lk1, lq2, lk2: DEVICE fp32 [n, dim] row-major (one row per head; n = 1 for one lambda
+ *                      per layer). lambda_out: DEVICE fp32 [n].
+ *  Dot products accumulate in fp32 and exp is evaluated in fp32.
+ *  Errors: ERR_ARG if a pointer is NULL, n < 1, dim < 1 or layer < 1.
+ */
+diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float* lq2,
+                                const float* lk2, int n, int dim, int layer, float* lambda_out,
+                                void* stream);
+
+/*
+ * DIFF V1 forward (prefill), one output row per query token and head.
+ *  q1, q2: [batch, seq_q, heads, d];  k1, k2: [batch, seq_k, heads, d];  v: [batch, seq_k, heads, dv]
+ *  out:    [batch, seq_q, heads, dv], same dtype as the inputs.
+ *  lambda: DEVICE fp32 [heads] (per-layer lambda: pass equal entries). Any real value is accepted.
+ *  causal: nonzero masks key j for query i unless j <= i + (seq_k - seq_q) (aligned to the last
+ *          key; the ordinary j <= i when seq_q == seq_k). Masked keys drop out of both maps'
+ *          normalisers. Requires seq_q <= seq_k so that every row sees at least one key.
+ *  epi, norm_w, eps, lambda_init: the epilogue; norm_w is DEVICE fp32 [dv] or NULL for ones.
+ *  scale:  softmax scale; <= 0 selects 1/sqrt(d).
+ *  Kernels: bf16 with d = 64, dv = 128 and aligned strides runs the MFMA kernel (one pass over
+ *  K/V tiles, two online softmax states, fused epilogue); every other case (fp32, or bf16 of
+ *  another width, d <= 256 and dv <= 512) runs the generic kernel.
+ *  Errors: ERR_ARG for NULL pointers, non-positive sizes, causal with seq_q > seq_k, or non-finite
+ *  eps/lambda_init; ERR_UNSUPPORTED for d > 256 or dv > 512; ERR_HIP if the launch fails.
+ */
+diffattn_status diffattn_fwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,
+                             diffattn_tensor k1, diffattn_tensor k2, diffattn_tensor v, int batch,
+                             int heads, int seq_q, int seq_k, int d, int dv, const float* lambda,
+                             float lambda_init, int causal, diffattn_epilogue epi,
+                             const float* norm_w, float eps, float scale, diffattn_tensor out,
+                             void* stream);
+
+/*
+ * Bytes of device workspace diffattn_decode needs for these sizes (0 on invalid sizes).
+ * The workspace holds per-split partial results of both maps (running max, sum and a dv-wide
+ * accumulator per map) in fp32.
+ */
+size_t diffattn_decode_workspace_size(int batch, int heads, int cache_len, int dv);
+
+/*
+ * DIFF V1 decode: one new query per (batch, head) against a KV cache; the query's own key and
+ * value are expected to be in the cache already, so it attends to cache entries 0..len-1.
+ *  q1, q2: [batch, 1, heads, d] (the token stride is unused);
+ *  k1c, k2c: [batch, cache_len, heads, d];  vc: [batch, cache_len, heads, dv]
+ *  cache_lens: DEVICE int32 [batch] with 1 <= len <= cache_len, or NULL (every len = cache_len).
+ *  lambda, lambda_init, epi, norm_w, eps, scale: as in diffattn_fwd.
+ *  out: [batch, 1, heads, dv].
+ *  workspace: DEVICE buffer of at least diffattn_decode_workspace_size(...) bytes, 256-byte
+ *  aligned; its contents on entry do not matter.
+ *  Kernels: bf16 with d = 64, dv = 128 runs a split-K kernel (each split streams its cache slice
+ *  once with 16-byte loads, V read once for both maps) and a reduction kernel that merges the
+ *  splits and applies the epilogue; the result does not depend on the split count's timing
+ *  (fixed-order merge, no atomics). Other shapes run the generic kernel.
+ *  Errors: ERR_ARG (NULL pointers, cache_len < 1, ...), ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP.
+ *  A cache_lens entry outside 1..cache_len is clamped into that range on the device.
+ */
+diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,
+                                diffattn_tensor k1c, diffattn_tensor k2c, diffattn_tensor vc,
+                                const int32_t* cache_lens, int batch, int heads, int cache_len,
+                                int d, int dv, const float* lambda, float lambda_init,
+                                diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                                diffattn_tensor out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * DIFF V2 forward: out[b, i, p] = O_{2p} - lam[b, i, p] * O_{2p+1}, where O_j is ordinary softmax
+ * attention of query head j over KV head j / (2h / h_kv) (the heads of one GQA group are
+ * contiguous, and a differenced pair sits in one group). No norm, no rescale.
+ *  q: [batch, seq, 2h, d];  k, v: [batch, seq, h_kv, d];  out: [batch, seq, h, d]
+ *  lam: DEVICE fp32 [batch, seq, h] contiguous, used as given (a caller that learns it as
+ *       sigmoid(W x) applies the sigmoid before the call).
+ *  causal: as in diffattn_fwd with seq_q = seq_k = seq.
+ *  Requires 2h divisible by h_kv with an even group size (so no pair straddles two groups).
+ *  Kernels: bf16 with d = 128 and aligned strides runs the MFMA kernel, in which one block owns a
+ *  KV group and a query tile of all its query heads, so each K/V tile is read once per group;
+ *  other cases run the generic kernel.
+ *  Errors: ERR_ARG, ERR_UNSUPPORTED (d > 256), ERR_HIP.
+ */
+diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k,
+                                diffattn_tensor v, const float* lam, int batch, int seq, int h,
+                                int h_kv, int d, int causal, float scale, diffattn_tensor out,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

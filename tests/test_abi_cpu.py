@@ -1,0 +1,151 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and every invalid
+argument is rejected with its status code before any HIP call (so these run on a CPU-only host)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import differential_softmax_attention_amd as da
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+T = da.Tensor
+FAKE = 0x10000          # never dereferenced: each call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(da.LIB_PATH):
+        from differential_softmax_attention_amd import build
+        build.build()
+    return da.lib()
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "diffattn.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffattn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert set(declared) == set(da.EXPORTED), declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.diffattn_version() >= 100
+
+
+def test_lambda_init_matches_schedule(L):
+    for layer in (1, 2, 4, 8, 12, 16, 24, 28):
+        assert da.lambda_init(layer) == pytest.approx(oracle.lambda_init(layer), abs=1e-15)
+    assert math.isnan(da.lambda_init(0))
+
+
+def _t(ptr=FAKE, sb=0, ss=0, sh=0):
+    return T(ptr, sb, ss, sh)
+
+
+def _fwd(L, dtype=1, tensors=None, B=1, H=1, Nq=4, Nk=4, d=64, dv=128, lam=FAKE, li=0.8, causal=1,
+         epi=1, w=None, eps=1e-5, scale=0.0):
+    ts = tensors or [_t(FAKE, 4096, 512, 64) for _ in range(6)]
+    return L.diffattn_fwd(dtype, ts[0], ts[1], ts[2], ts[3], ts[4], B, H, Nq, Nk, d, dv, lam, li, causal,
+                          epi, w, eps, scale, ts[5], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), da.DIFFATTN_ERR_ARG),
+    (dict(lam=None), da.DIFFATTN_ERR_ARG),
+    (dict(B=0), da.DIFFATTN_ERR_ARG),
+    (dict(Nq=0), da.DIFFATTN_ERR_ARG),
+    (dict(d=0), da.DIFFATTN_ERR_ARG),
+    (dict(dv=-1), da.DIFFATTN_ERR_ARG),
+    (dict(Nq=8, Nk=4, causal=1), da.DIFFATTN_ERR_ARG),
+    (dict(epi=5), da.DIFFATTN_ERR_ARG),
+    (dict(eps=float("nan")), da.DIFFATTN_ERR_ARG),
+    (dict(eps=-1.0), da.DIFFATTN_ERR_ARG),
+    (dict(li=float("inf")), da.DIFFATTN_ERR_ARG),
+    (dict(scale=float("nan")), da.DIFFATTN_ERR_ARG),
+    (dict(d=300), da.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(dv=1024), da.DIFFATTN_ERR_UNSUPPORTED),
+    (dict(H=70000), da.DIFFATTN_ERR_ARG),
+])
+def test_fwd_rejects(L, kw, status):
+    assert _fwd(L, **kw) == status
+    assert L.diffattn_last_error().decode() != ""
+
+
+def test_fwd_rejects_bad_tensors(L):
+    good = [_t(FAKE, 4096, 512, 64) for _ in range(6)]
+    for i in range(6):
+        ts = list(good)
+        ts[i] = _t(0, 4096, 512, 64)                       # null
+        assert _fwd(L, tensors=ts) == da.DIFFATTN_ERR_ARG
+        ts[i] = _t(FAKE + 1, 4096, 512, 64)                # bf16 element misaligned
+        assert _fwd(L, tensors=ts) == da.DIFFATTN_ERR_ARG
+        ts[i] = _t(FAKE + 2, 4096, 512, 64)                # fp32 element misaligned
+        assert _fwd(L, dtype=0, tensors=ts) == da.DIFFATTN_ERR_ARG
+        ts[i] = _t(FAKE, 4096, -512, 64)                   # negative stride
+        assert _fwd(L, tensors=ts) == da.DIFFATTN_ERR_ARG
+    assert "q1" in (_fwd(L, tensors=[_t(0)] + good[1:]) and L.diffattn_last_error().decode())
+
+
+def _decode(L, B=2, H=2, Lc=100, d=64, dv=128, ws=FAKE, ws_bytes=1 << 30, epi=1, lens=None, lam=FAKE):
+    ts = [_t(FAKE, 4096, 512, 64) for _ in range(6)]
+    return L.diffattn_decode(1, ts[0], ts[1], ts[2], ts[3], ts[4], lens, B, H, Lc, d, dv, lam, 0.8, epi,
+                             None, 1e-5, 0.0, ts[5], ws, ws_bytes, None)
+
+
+def test_decode_rejects(L):
+    assert _decode(L, Lc=0) == da.DIFFATTN_ERR_ARG
+    assert _decode(L, B=0) == da.DIFFATTN_ERR_ARG
+    assert _decode(L, lam=None) == da.DIFFATTN_ERR_ARG
+    assert _decode(L, epi=3) == da.DIFFATTN_ERR_ARG
+    need = L.diffattn_decode_workspace_size(2, 2, 100, 128)
+    assert need > 0
+    assert _decode(L, ws_bytes=need - 1) == da.DIFFATTN_ERR_WORKSPACE
+    assert _decode(L, ws=None) == da.DIFFATTN_ERR_ARG
+    assert _decode(L, ws=FAKE + 16) == da.DIFFATTN_ERR_ARG     # not 256-byte aligned
+    assert _decode(L, d=512) == da.DIFFATTN_ERR_UNSUPPORTED
+
+
+def test_decode_workspace_size(L):
+    assert L.diffattn_decode_workspace_size(0, 16, 100, 128) == 0
+    assert L.diffattn_decode_workspace_size(32, 16, 0, 128) == 0
+    small = L.diffattn_decode_workspace_size(1, 1, 1, 128)
+    big = L.diffattn_decode_workspace_size(32, 16, 65536, 128)
+    assert 0 < small < big < 64 << 20      # partials only: a few MB even for a 17 GB cache
+
+
+def _v2(L, B=1, N=8, h=4, hkv=2, d=128, lam=FAKE, causal=1, dtype=1, scale=0.0):
+    ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(4)]
+    return L.diffattn_v2_fwd(dtype, ts[0], ts[1], ts[2], lam, B, N, h, hkv, d, causal, scale, ts[3], None)
+
+
+def test_v2_rejects(L):
+    assert _v2(L, hkv=3) == da.DIFFATTN_ERR_ARG          # 8 query heads into 3 groups
+    assert _v2(L, h=3, hkv=2) == da.DIFFATTN_ERR_ARG     # groups of 3: a pair would straddle groups
+    assert _v2(L, lam=None) == da.DIFFATTN_ERR_ARG
+    assert _v2(L, N=0) == da.DIFFATTN_ERR_ARG
+    assert _v2(L, d=512) == da.DIFFATTN_ERR_UNSUPPORTED
+    assert _v2(L, dtype=9) == da.DIFFATTN_ERR_ARG
+
+
+def test_lambda_rejects(L):
+    assert L.diffattn_lambda(FAKE, FAKE, FAKE, FAKE, 0, 64, 12, FAKE, None) == da.DIFFATTN_ERR_ARG
+    assert L.diffattn_lambda(FAKE, FAKE, FAKE, FAKE, 16, 0, 12, FAKE, None) == da.DIFFATTN_ERR_ARG
+    assert L.diffattn_lambda(FAKE, FAKE, FAKE, FAKE, 16, 64, 0, FAKE, None) == da.DIFFATTN_ERR_ARG
+    assert L.diffattn_lambda(None, FAKE, FAKE, FAKE, 16, 64, 12, FAKE, None) == da.DIFFATTN_ERR_ARG
+    assert L.diffattn_lambda(FAKE, FAKE, FAKE, FAKE, 16, 64, 12, None, None) == da.DIFFATTN_ERR_ARG
+
+
+def test_product_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "differential_softmax_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    src = f.read()
+                assert "oracle" not in src, fn
