@@ -32,34 +32,68 @@ namespace {
 
 constexpr int kBN = 32;          // keys per tile
 constexpr int kDV = 128;         // value width
-constexpr int kVP = kDV + 16;    // LDS pitch of a V row (elements)
 constexpr float kRescaleThreshold = 8.0f;
+
+// LDS tiles are unpadded rows of 16-byte chunks, XOR-swizzled per row so that the MFMA operand
+// reads below hit distinct banks. A stage holds K1 (and K2 for V1) then V, 32 rows each, and is
+// filled by global_load_lds (16 bytes per lane, lane i of a wave writing base + 16 i): each lane
+// fetches the global chunk that belongs in its LDS slot, so no registers stage the tile.
+//  K, d = 64  (8 chunks per row):  phys = c ^ ((row & 7) ^ ((row >> 3) & 1))
+//  K, d = 128 (16 chunks per row): phys = c ^ (row & 15)
+//  V, 128 wide (16 chunks per row): phys = c ^ ((row & 3) << 1) ^ ((c & 2) << 2)
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+    return D == 64 ? ((row & 7) ^ ((row >> 3) & 1)) : (row & 15);
+}
+__device__ __forceinline__ int v_phys(int row, int c) { return c ^ ((row & 3) << 1) ^ ((c & 2) << 2); }
+__device__ __forceinline__ int v_logical(int row, int p) {
+    const int y = p ^ ((row & 3) << 1);
+    return y ^ ((y & 2) << 2);
+}
 
 template <int D, bool V2>
 struct Cfg {
     static constexpr int NW = V2 ? 8 : 4;              // waves per block
     static constexpr int NT = NW * 64;
-    static constexpr int KP = D + 8;                    // LDS pitch of a K row (elements)
     static constexpr int NK = V2 ? 1 : 2;               // K tiles per stage (V2 shares K)
-    static constexpr int K_ELEMS = kBN * KP;
-    static constexpr int V_ELEMS = kBN * kVP;
-    static constexpr int STAGE = NK * K_ELEMS + V_ELEMS;
-    static constexpr int KCH = kBN * D / 8;             // 16-byte chunks per K tile
-    static constexpr int VCH = kBN * kDV / 8;
-    static constexpr int TOT = NK * KCH + VCH;
-    static_assert(TOT % NT == 0, "tile chunks must divide evenly");
-    static constexpr int PER = TOT / NT;
+    static constexpr int K_CPR = D / 8;                 // 16-byte chunks per K row
+    static constexpr int V_CPR = kDV / 8;
+    static constexpr int K_BYTES = kBN * D * 2;
+    static constexpr int V_BYTES = kBN * kDV * 2;
+    static constexpr int STAGE_BYTES = NK * K_BYTES + V_BYTES;
+    static constexpr int K_LOADS = kBN * K_CPR / NT;    // DMA loads per thread per K tile
+    static constexpr int V_LOADS = kBN * V_CPR / NT;
+    static_assert(K_LOADS >= 1 && V_LOADS >= 1, "tile must cover every thread");
 };
 
-__device__ __forceinline__ u32x4 ld_global16(const bf16* p) { return *(const u32x4*)p; }
-__device__ __forceinline__ void st_lds16(bf16* p, u32x4 x) { *(u32x4*)p = x; }
-__device__ __forceinline__ bf16x8 ld_lds16(const bf16* p) { return *(const bf16x8*)p; }
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+
+// 16-byte global -> LDS DMA for one wave: lane i's chunk lands at lds_wave_base + 16 i.
+// Issued from inline asm so that the compiler does not track it as an LDS store: its generic
+// tracking would otherwise wait for the next tile's prefetch before every read of the current
+// tile. Completion is ordered explicitly: s_waitcnt vmcnt(0) and a barrier before a stage is read.
+__device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds_wave_base) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8_t*)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ bf16x8 lds16(const unsigned char* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ bf16x8 ld_global_bf16x8(const bf16* p) { return *(const bf16x8*)p; }
+
+// value of x held by lane l ^ 32 combined with x: both halves of the wave get the same result
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D, bool V2, bool CAUSAL, bool EPI>
-__global__ __launch_bounds__(V2 ? 512 : 256) void fwd_mfma_kernel(MfmaFwdArgs a) {
+__global__ __launch_bounds__(V2 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(V2 ? 1 : 2, 2)))
+void fwd_mfma_kernel(MfmaFwdArgs a) {
     using C = Cfg<D, V2>;
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    bf16* smem = (bf16*)smem_raw;
+    extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -98,7 +132,6 @@ __global__ __launch_bounds__(V2 ? 512 : 256) void fwd_mfma_kernel(MfmaFwdArgs a)
     const int qrow = qw0 + n;
     const int off = a.seq_k - a.seq_q;    // causal alignment to the last key
 
-    // heads read by this wave
     int hq1, hq2, hout, kvh;
     if (V2) {
         hout = grp * pairs_per_block + pair_in_grp;   // output pair index p
@@ -113,14 +146,15 @@ __global__ __launch_bounds__(V2 ? 512 : 256) void fwd_mfma_kernel(MfmaFwdArgs a)
     constexpr int NKK = D / 16;
     bf16x8 bq1[NKK], bq2[NKK];
     {
-        const bf16* q1p = (const bf16*)a.q1 + b * a.q1s[0] + (int64_t)qrow * a.q1s[1] + (int64_t)hq1 * a.q1s[2] + 8 * h2;
-        const bf16* q2p = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)qrow * a.q2s[1] + (int64_t)hq2 * a.q2s[2] + 8 * h2;
         const bool ok = qrow < a.seq_q;
+        const int qr = ok ? qrow : 0;
+        const bf16* q1p = (const bf16*)a.q1 + b * a.q1s[0] + (int64_t)qr * a.q1s[1] + (int64_t)hq1 * a.q1s[2] + 8 * h2;
+        const bf16* q2p = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)qr * a.q2s[1] + (int64_t)hq2 * a.q2s[2] + 8 * h2;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            bf16x8 z = {};
-            bq1[kk] = ok ? ld_lds16(q1p + 16 * kk) : z;   // (plain 16-byte global loads)
-            bq2[kk] = ok ? ld_lds16(q2p + 16 * kk) : z;
+            const bf16x8 z = {};
+            bq1[kk] = ok ? ld_global_bf16x8(q1p + 16 * kk) : z;
+            bq2[kk] = ok ? ld_global_bf16x8(q2p + 16 * kk) : z;
         }
     }
 
@@ -134,52 +168,71 @@ __global__ __launch_bounds__(V2 ? 512 : 256) void fwd_mfma_kernel(MfmaFwdArgs a)
     const int wave_qlast = min(qw0 + 31, a.seq_q - 1);
     const bool wave_active = qw0 < a.seq_q;
 
-    // ---- cooperative tile loader: chunk c of a stage = (tensor, row, 16-byte column)
+    // ---- tile DMA: thread tid fills K slots tid + j*NT and V slots tid + j*NT of a stage
     const bf16* kbase1 = (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)kvh * a.k1s[2];
     const bf16* kbase2 = (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)kvh * a.k2s[2];
     const bf16* vbase = (const bf16*)a.v + b * a.vs[0] + (int64_t)kvh * a.vs[2];
-    u32x4 stage_regs[C::PER];
+    const int wave_slot0 = wave * 64;   // first slot written by this wave in a load
 
-    auto load_tile = [&](int kt) {
+    auto issue_tile = [&](int kt, int stage) {
+        unsigned char* st = smem + stage * C::STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < C::PER; ++i) {
-            const int c = tid + i * C::NT;
-            const bf16* src;
-            int row;
-            if (c < C::NK * C::KCH) {
-                const int cc = c % C::KCH;
-                row = cc / (D / 8);
-                const int col = (cc % (D / 8)) * 8;
-                const bf16* kb = (c < C::KCH) ? kbase1 : kbase2;
-                const int64_t rs = (c < C::KCH) ? a.k1s[1] : a.k2s[1];
-                src = kb + (int64_t)(kt * kBN + row) * rs + col;
-            } else {
-                const int cc = c - C::NK * C::KCH;
-                row = cc / (kDV / 8);
-                const int col = (cc % (kDV / 8)) * 8;
-                src = vbase + (int64_t)(kt * kBN + row) * a.vs[1] + col;
+        for (int t = 0; t < C::NK; ++t) {
+            const bf16* kb = t == 0 ? kbase1 : kbase2;
+            const int64_t rs = t == 0 ? a.k1s[1] : a.k2s[1];
+#pragma unroll
+            for (int j = 0; j < C::K_LOADS; ++j) {
+                const int s = tid + j * C::NT;
+                const int row = s / C::K_CPR;
+                const int c = (s % C::K_CPR) ^ k_swz<D>(row);
+                const int grow = min(kt * kBN + row, a.seq_k - 1);
+                dma16(kb + (int64_t)grow * rs + c * 8, st + t * C::K_BYTES + (j * C::NT + wave_slot0) * 16);
             }
-            u32x4 z = {0u, 0u, 0u, 0u};
-            stage_regs[i] = (kt * kBN + row < a.seq_k) ? ld_global16(src) : z;
+        }
+#pragma unroll
+        for (int j = 0; j < C::V_LOADS; ++j) {
+            const int s = tid + j * C::NT;
+            const int row = s / C::V_CPR;
+            const int c = v_logical(row, s % C::V_CPR);
+            const int grow = min(kt * kBN + row, a.seq_k - 1);
+            dma16(vbase + (int64_t)grow * a.vs[1] + c * 8, st + C::NK * C::K_BYTES + (j * C::NT + wave_slot0) * 16);
         }
     };
-    auto store_tile = [&](int stage) {
-        bf16* st = smem + stage * C::STAGE;
+    // rows past the last key were fetched from a clamped address; zero them once the DMA landed
+    // (only the last tile can have such rows)
+    auto zero_tail = [&](int kt, int stage) {
+        unsigned char* st = smem + stage * C::STAGE_BYTES;
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < C::PER; ++i) {
-            const int c = tid + i * C::NT;
-            bf16* dst;
-            if (c < C::NK * C::KCH) {
-                const int which = c / C::KCH;
-                const int cc = c % C::KCH;
-                dst = st + which * C::K_ELEMS + (cc / (D / 8)) * C::KP + (cc % (D / 8)) * 8;
-            } else {
-                const int cc = c - C::NK * C::KCH;
-                dst = st + C::NK * C::K_ELEMS + (cc / (kDV / 8)) * kVP + (cc % (kDV / 8)) * 8;
+        for (int t = 0; t < C::NK; ++t)
+#pragma unroll
+            for (int j = 0; j < C::K_LOADS; ++j) {
+                const int s = tid + j * C::NT;
+                if (kt * kBN + s / C::K_CPR >= a.seq_k) *(u32x4*)(st + t * C::K_BYTES + s * 16) = z;
             }
-            st_lds16(dst, stage_regs[i]);
+#pragma unroll
+        for (int j = 0; j < C::V_LOADS; ++j) {
+            const int s = tid + j * C::NT;
+            if (kt * kBN + s / C::V_CPR >= a.seq_k) *(u32x4*)(st + C::NK * C::K_BYTES + s * 16) = z;
         }
     };
+
+    // ---- per-lane LDS offsets of the MFMA operands
+    // K (A operand of S^T): row n, logical chunk 2kk + h2
+    int koff[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) koff[kk] = n * (D * 2) + (((2 * kk + h2) ^ k_swz<D>(n)) * 16);
+    // V^T (A operand of O^T) through the transposing read: 16-lane group G = lane/16 covers
+    // channels ct*32 + (G&1)*16 .. +15 and key half h2 = G>>1; lane L supplies row
+    // key0 + L/4 (key0 = 16kb + 8t + 4h2) and channels cbase + 4(L%4) .. +3.
+    const int G = lane >> 4, L = lane & 15;
+    int voff[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        const int row = 4 * (G >> 1) + (L >> 2);
+        const int c = ct * 4 + (G & 1) * 2 + ((L >> 1) & 1);
+        voff[ct] = row * (kDV * 2) + v_phys(row, c) * 16 + (L & 1) * 8;
+    }
 
     // ---- accumulators and softmax state (per lane = per query n, this lane's half of keys)
     f32x16 o1[4], o2[4];
@@ -187,112 +240,102 @@ __global__ __launch_bounds__(V2 ? 512 : 256) void fwd_mfma_kernel(MfmaFwdArgs a)
     for (int ct = 0; ct < 4; ++ct) { o1[ct] = f32x16{}; o2[ct] = f32x16{}; }
     float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
     const float c2 = a.scale_log2;
-    const int xaddr = (lane ^ 32) << 2;
 
-    // V^T operand addressing for the transposing read (see the layout note above):
-    // 16-lane group G = lane/16 covers channels ct*32 + (G&1)*16 .. +15 and key half h2 = G>>1;
-    // lane L in the group supplies row key0 + L/4, channels cbase + 4(L%4).
-    const int G = lane >> 4, L = lane & 15;
-    const int v_lane_off = ((G >> 1) * 4 + (L >> 2)) * kVP + (G & 1) * 16 + 4 * (L & 3);
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    issue_tile(0, 0);
 
     for (int kt = 0; kt < nkt; ++kt) {
-        const bool has_next = kt + 1 < nkt;
-        if (has_next) load_tile(kt + 1);
+        const int stage = kt & 1;
+        __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this thread's DMA landed
+        if ((kt + 1) * kBN > a.seq_k) zero_tail(kt, stage);
+        __syncthreads();                                    // every DMA of tile kt landed; stage^1 free
+        if (kt + 1 < nkt) issue_tile(kt + 1, stage ^ 1);    // prefetch overlaps this tile's compute
 
         const int k0 = kt * kBN;
         const bool wave_needs = wave_active && (!CAUSAL || k0 <= wave_qlast + off);
-        if (wave_needs) {
-            const bf16* st = smem + (kt & 1) * C::STAGE;
-            const bf16* Ks1 = st;
-            const bf16* Ks2 = st + (C::NK - 1) * C::K_ELEMS;
-            const bf16* Vs = st + C::NK * C::K_ELEMS;
+        if (!wave_needs) continue;
+        const unsigned char* st = smem + stage * C::STAGE_BYTES;
+        const unsigned char* Ks1 = st;
+        const unsigned char* Ks2 = st + (C::NK - 1) * C::K_BYTES;
+        const unsigned char* Vs = st + C::NK * C::K_BYTES;
 
-            // S^T = K Q^T for both maps (fp32 accumulate)
-            f32x16 s1 = f32x16{}, s2 = f32x16{};
+        // S^T = K Q^T for both maps (fp32 accumulate)
+        f32x16 s1 = f32x16{}, s2 = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const bf16x8 ka = ld_lds16(Ks1 + n * C::KP + 16 * kk + 8 * h2);
-                s1 = mfma32x32x16(ka, bq1[kk], s1);
-                if (V2) {
-                    s2 = mfma32x32x16(ka, bq2[kk], s2);
-                } else {
-                    const bf16x8 kb2 = ld_lds16(Ks2 + n * C::KP + 16 * kk + 8 * h2);
-                    s2 = mfma32x32x16(kb2, bq2[kk], s2);
-                }
-            }
-
-            // mask keys past the end, and (causal) keys after the query's diagonal
-            const bool need_mask = (k0 + kBN > a.seq_k) || (CAUSAL && k0 + kBN - 1 > qw0 + off);
-            if (need_mask) {
-                const int qlim = CAUSAL ? min(qrow + off, a.seq_k - 1) : a.seq_k - 1;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + (r >> 2) * 8 + h2 * 4 + (r & 3);
-                    if (key > qlim) { s1[r] = -INFINITY; s2[r] = -INFINITY; }
-                }
-            }
-
-            // tile maxima (raw score units), shared by lanes n and n+32
-            float mx1 = s1[0], mx2 = s2[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) { mx1 = fmaxf(mx1, s1[r]); mx2 = fmaxf(mx2, s2[r]); }
-            mx1 = fmaxf(mx1, lane_xor(mx1, xaddr)) * c2;
-            mx2 = fmaxf(mx2, lane_xor(mx2, xaddr)) * c2;
-            const bool need = (mx1 > m1 + kRescaleThreshold) || (mx2 > m2 + kRescaleThreshold);
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                const float mn1 = fmaxf(m1, mx1), mn2 = fmaxf(m2, mx2);
-                const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
-                m1 = mn1;
-                m2 = mn2;
-                l1 *= al1;
-                l2 *= al2;
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) { o1[ct] *= al1; o2[ct] *= al2; }
-            }
-
-            // unnormalised weights, their sums, and the bf16 P^T operands
-            bf16x8 p1[2], p2[2];
-            float ls1 = 0.f, ls2 = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e1 = fast_exp2(fmaf(s1[r], c2, -m1));
-                const float e2 = fast_exp2(fmaf(s2[r], c2, -m2));
-                ls1 += e1;
-                ls2 += e2;
-                p1[r >> 3][r & 7] = (bf16)e1;
-                p2[r >> 3][r & 7] = (bf16)e2;
-            }
-            l1 += ls1;
-            l2 += ls2;
-
-            // O^T += V^T P^T for both maps; each V^T fragment feeds both
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16* vp = Vs + (kb * 16) * kVP + ct * 32 + v_lane_off;
-                    const i16x4 lo = lds_read_tr16(vp);
-                    const i16x4 hi = lds_read_tr16(vp + 8 * kVP);
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o1[ct] = mfma32x32x16(va, p1[kb], o1[ct]);
-                    o2[ct] = mfma32x32x16(va, p2[kb], o2[ct]);
-                }
+        for (int kk = 0; kk < NKK; ++kk) {
+            const bf16x8 ka = lds16(Ks1 + koff[kk]);
+            s1 = mfma32x32x16(ka, bq1[kk], s1);
+            if (V2) {
+                s2 = mfma32x32x16(ka, bq2[kk], s2);
+            } else {
+                const bf16x8 kb2 = lds16(Ks2 + koff[kk]);
+                s2 = mfma32x32x16(kb2, bq2[kk], s2);
             }
         }
 
-        if (has_next) store_tile((kt + 1) & 1);
-        __syncthreads();
+        // mask keys past the end, and (causal) keys after the query's diagonal
+        const bool need_mask = (k0 + kBN > a.seq_k) || (CAUSAL && k0 + kBN - 1 > qw0 + off);
+        if (need_mask) {
+            const int qlim = CAUSAL ? min(qrow + off, a.seq_k - 1) : a.seq_k - 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + (r >> 2) * 8 + h2 * 4 + (r & 3);
+                if (key > qlim) { s1[r] = -INFINITY; s2[r] = -INFINITY; }
+            }
+        }
+
+        // tile maxima (raw score units), shared by lanes n and n+32
+        float mx1 = s1[0], mx2 = s2[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) { mx1 = fmaxf(mx1, s1[r]); mx2 = fmaxf(mx2, s2[r]); }
+        mx1 = max_halves(mx1) * c2;
+        mx2 = max_halves(mx2) * c2;
+        const bool need = (mx1 > m1 + kRescaleThreshold) || (mx2 > m2 + kRescaleThreshold);
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float mn1 = fmaxf(m1, mx1), mn2 = fmaxf(m2, mx2);
+            const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
+            m1 = mn1;
+            m2 = mn2;
+            l1 *= al1;
+            l2 *= al2;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) { o1[ct] *= al1; o2[ct] *= al2; }
+        }
+
+        // unnormalised weights, their sums, and the bf16 P^T operands
+        bf16x8 p1[2], p2[2];
+        float ls1 = 0.f, ls2 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float e1 = fast_exp2(fmaf(s1[r], c2, -m1));
+            const float e2 = fast_exp2(fmaf(s2[r], c2, -m2));
+            ls1 += e1;
+            ls2 += e2;
+            p1[r >> 3][r & 7] = (bf16)e1;
+            p2[r >> 3][r & 7] = (bf16)e2;
+        }
+        l1 += ls1;
+        l2 += ls2;
+
+        // O^T += V^T P^T for both maps; each V^T fragment feeds both
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16* vp = (const bf16*)(Vs + voff[ct] + kb * 16 * (kDV * 2));
+                const i16x4 lo = lds_read_tr16(vp);
+                const i16x4 hi = lds_read_tr16(vp + 8 * kDV);
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                o1[ct] = mfma32x32x16(va, p1[kb], o1[ct]);
+                o2[ct] = mfma32x32x16(va, p2[kb], o2[ct]);
+            }
+        }
     }
 
     if (!wave_active) return;
 
     // ---- epilogue: O = O1/l1 - lambda O2/l2 (+ RMSNorm * w * (1 - lambda_init))
-    l1 += lane_xor(l1, xaddr);
-    l2 += lane_xor(l2, xaddr);
+    l1 = sum_halves(l1);
+    l2 = sum_halves(l2);
     float lam;
     if (V2) {
         lam = (qrow < a.seq_q) ? a.lam[b * a.lams[0] + (int64_t)qrow * a.lams[1] + (int64_t)hout * a.lams[2]] : 0.f;
@@ -315,7 +358,7 @@ __global__ __launch_bounds__(V2 ? 512 : 256) void fwd_mfma_kernel(MfmaFwdArgs a)
         }
     }
     if (EPI) {
-        ss += lane_xor(ss, xaddr);
+        ss = sum_halves(ss);
         const float inv = (1.f / sqrtf(ss * (1.f / kDV) + a.eps)) * (1.f - a.lambda_init);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
@@ -350,7 +393,7 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
     const int n_units = V2 ? a.batch * (a.heads * 2 / a.kv_group) : a.batch * a.heads;
     const int nqt = (a.seq_q + BM - 1) / BM;
     const dim3 grid((unsigned)(nqt * n_units));
-    const size_t smem = 2 * C::STAGE * sizeof(bf16);
+    const size_t smem = 2 * C::STAGE_BYTES;
     if (a.causal) {
         if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, true>), grid, dim3(C::NT), smem, stream, a);
         else hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, false>), grid, dim3(C::NT), smem, stream, a);
