@@ -75,8 +75,8 @@ def time_launches(fn, reps, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--secondary", default="32k,decode,v2",
                     help="comma list of extra workloads to time (32k, decode, v2) or 'none'")
     ap.add_argument("--secondary-reps", type=int, default=10)

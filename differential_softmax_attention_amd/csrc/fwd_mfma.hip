@@ -34,6 +34,22 @@ constexpr int kBN = 32;          // keys per tile
 constexpr int kDV = 128;         // value width
 constexpr float kRescaleThreshold = 8.0f;
 
+// Per-tile instruction scheduling (see the PV section): explicit MFMA / VALU interleave and
+// raised wave priority while issuing MFMAs. Both help the V1 kernel (4 waves, no spills); the
+// V2 kernel (8 waves of 256 registers) runs best without them.
+#ifndef DA_SCHED_V1
+#define DA_SCHED_V1 1
+#endif
+#ifndef DA_PRIO_V1
+#define DA_PRIO_V1 1
+#endif
+#ifndef DA_SCHED_V2
+#define DA_SCHED_V2 0
+#endif
+#ifndef DA_PRIO_V2
+#define DA_PRIO_V2 0
+#endif
+
 // LDS tiles are unpadded rows of 16-byte chunks, XOR-swizzled per row so that the MFMA operand
 // reads below hit distinct banks. A stage holds K1 (and K2 for V1) then V, 32 rows each, and is
 // filled by global_load_lds (16 bytes per lane, lane i of a wave writing base + 16 i): each lane
@@ -68,21 +84,25 @@ struct Cfg {
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
-// 16-byte global -> LDS DMA for one wave: lane i's chunk lands at lds_wave_base + 16 i.
-// Issued from inline asm so that the compiler does not track it as an LDS store: its generic
-// tracking would otherwise wait for the next tile's prefetch before every read of the current
-// tile. Completion is ordered explicitly: s_waitcnt vmcnt(0) and a barrier before a stage is read.
-__device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds_wave_base) {
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8_t*)lds_wave_base);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "s"(lds) : "memory", "m0");
+// 16-byte global -> LDS DMA for one wave: lane i reads sbase + voff (voff per lane) and the
+// chunk lands at LDS address lds_wave_base + 16 i. Issued from inline asm so that the compiler
+// does not track it as an LDS store: its generic tracking would otherwise wait for the next
+// tile's prefetch before every read of the current tile. Completion is ordered explicitly:
+// s_waitcnt vmcnt(0) and a barrier before a stage is read.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 : : "v"(voff), "s"(sbase), "s"(lds_wave_base) : "memory", "m0");
 }
+
+__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ bf16x8 lds16(const unsigned char* p) { return *(const bf16x8*)p; }
 __device__ __forceinline__ bf16x8 ld_global_bf16x8(const bf16* p) { return *(const bf16x8*)p; }
 
 // value of x held by lane l ^ 32 combined with x: both halves of the wave get the same result
 __device__ __forceinline__ float max_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -168,34 +188,51 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     const int wave_qlast = min(qw0 + 31, a.seq_q - 1);
     const bool wave_active = qw0 < a.seq_q;
 
-    // ---- tile DMA: thread tid fills K slots tid + j*NT and V slots tid + j*NT of a stage
+    // ---- tile DMA: thread tid fills K slots tid + j*NT and V slots tid + j*NT of a stage.
+    //      Per-lane byte offsets within a tile are fixed; the tile base advances in SGPRs.
     const bf16* kbase1 = (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)kvh * a.k1s[2];
     const bf16* kbase2 = (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)kvh * a.k2s[2];
     const bf16* vbase = (const bf16*)a.v + b * a.vs[0] + (int64_t)kvh * a.vs[2];
-    const int wave_slot0 = wave * 64;   // first slot written by this wave in a load
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
+    int krow[C::K_LOADS], kcol[C::K_LOADS], vrow[C::V_LOADS], vcol[C::V_LOADS];
+    uint32_t koff1[C::K_LOADS], koff2[C::K_LOADS], voffg[C::V_LOADS];
+#pragma unroll
+    for (int j = 0; j < C::K_LOADS; ++j) {
+        const int s = tid + j * C::NT;
+        krow[j] = s / C::K_CPR;
+        kcol[j] = (s % C::K_CPR) ^ k_swz<D>(krow[j]);
+        koff1[j] = (uint32_t)(krow[j] * a.k1s[1] + kcol[j] * 8) * 2u;
+        koff2[j] = (uint32_t)(krow[j] * a.k2s[1] + kcol[j] * 8) * 2u;
+    }
+#pragma unroll
+    for (int j = 0; j < C::V_LOADS; ++j) {
+        const int s = tid + j * C::NT;
+        vrow[j] = s / C::V_CPR;
+        vcol[j] = v_logical(vrow[j], s % C::V_CPR);
+        voffg[j] = (uint32_t)(vrow[j] * a.vs[1] + vcol[j] * 8) * 2u;
+    }
 
     auto issue_tile = [&](int kt, int stage) {
-        unsigned char* st = smem + stage * C::STAGE_BYTES;
+        const uint32_t st = smem_lds + stage * C::STAGE_BYTES + wave_u * 64 * 16;
+        const bool full = (kt + 1) * kBN <= a.seq_k;
+        const int rows_left = a.seq_k - 1 - kt * kBN;   // last valid row within this tile
 #pragma unroll
         for (int t = 0; t < C::NK; ++t) {
-            const bf16* kb = t == 0 ? kbase1 : kbase2;
+            const bf16* tb = (t == 0 ? kbase1 : kbase2) + (int64_t)kt * kBN * (t == 0 ? a.k1s[1] : a.k2s[1]);
             const int64_t rs = t == 0 ? a.k1s[1] : a.k2s[1];
 #pragma unroll
             for (int j = 0; j < C::K_LOADS; ++j) {
-                const int s = tid + j * C::NT;
-                const int row = s / C::K_CPR;
-                const int c = (s % C::K_CPR) ^ k_swz<D>(row);
-                const int grow = min(kt * kBN + row, a.seq_k - 1);
-                dma16(kb + (int64_t)grow * rs + c * 8, st + t * C::K_BYTES + (j * C::NT + wave_slot0) * 16);
+                const uint32_t off = full ? (t == 0 ? koff1[j] : koff2[j])
+                                          : (uint32_t)(min(krow[j], rows_left) * rs + kcol[j] * 8) * 2u;
+                dma16(tb, off, st + t * C::K_BYTES + j * C::NT * 16);
             }
         }
+        const bf16* vb = vbase + (int64_t)kt * kBN * a.vs[1];
 #pragma unroll
         for (int j = 0; j < C::V_LOADS; ++j) {
-            const int s = tid + j * C::NT;
-            const int row = s / C::V_CPR;
-            const int c = v_logical(row, s % C::V_CPR);
-            const int grow = min(kt * kBN + row, a.seq_k - 1);
-            dma16(vbase + (int64_t)grow * a.vs[1] + c * 8, st + C::NK * C::K_BYTES + (j * C::NT + wave_slot0) * 16);
+            const uint32_t off = full ? voffg[j] : (uint32_t)(min(vrow[j], rows_left) * a.vs[1] + vcol[j] * 8) * 2u;
+            dma16(vb, off, st + C::NK * C::K_BYTES + j * C::NT * 16);
         }
     };
     // rows past the last key were fetched from a clamped address; zero them once the DMA landed
@@ -208,12 +245,12 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
 #pragma unroll
             for (int j = 0; j < C::K_LOADS; ++j) {
                 const int s = tid + j * C::NT;
-                if (kt * kBN + s / C::K_CPR >= a.seq_k) *(u32x4*)(st + t * C::K_BYTES + s * 16) = z;
+                if (kt * kBN + krow[j] >= a.seq_k) *(u32x4*)(st + t * C::K_BYTES + s * 16) = z;
             }
 #pragma unroll
         for (int j = 0; j < C::V_LOADS; ++j) {
             const int s = tid + j * C::NT;
-            if (kt * kBN + s / C::V_CPR >= a.seq_k) *(u32x4*)(st + C::NK * C::K_BYTES + s * 16) = z;
+            if (kt * kBN + vrow[j] >= a.seq_k) *(u32x4*)(st + C::NK * C::K_BYTES + s * 16) = z;
         }
     };
 
@@ -286,12 +323,12 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         // tile maxima (raw score units), shared by lanes n and n+32
         float mx1 = s1[0], mx2 = s2[0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) { mx1 = fmaxf(mx1, s1[r]); mx2 = fmaxf(mx2, s2[r]); }
+        for (int r = 1; r < 16; ++r) { mx1 = fmax_nc(mx1, s1[r]); mx2 = fmax_nc(mx2, s2[r]); }
         mx1 = max_halves(mx1) * c2;
         mx2 = max_halves(mx2) * c2;
         const bool need = (mx1 > m1 + kRescaleThreshold) || (mx2 > m2 + kRescaleThreshold);
         if (__builtin_amdgcn_ballot_w64(need)) {
-            const float mn1 = fmaxf(m1, mx1), mn2 = fmaxf(m2, mx2);
+            const float mn1 = fmax_nc(m1, mx1), mn2 = fmax_nc(m2, mx2);
             const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
             m1 = mn1;
             m2 = mn2;
@@ -301,33 +338,75 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
             for (int ct = 0; ct < 4; ++ct) { o1[ct] *= al1; o2[ct] *= al2; }
         }
 
-        // unnormalised weights, their sums, and the bf16 P^T operands
+        // Per half of the tile's keys (kb): unnormalised weights exp2(s*c - m) rounded to bf16
+        // (the P^T operand), their row sums taken from the same bf16 values (v_dot2 with ones, so
+        // numerator and normaliser use identical weights), then O^T += V^T P^T for both maps with
+        // each V^T fragment feeding both. The MFMAs of the first half are interleaved with the
+        // exponentials of the second half.
+        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
         bf16x8 p1[2], p2[2];
-        float ls1 = 0.f, ls2 = 0.f;
+        float la1 = 0.f, lb1 = 0.f, la2 = 0.f, lb2 = 0.f;
+        auto softmax_half = [&](int kb) {
+            bf16x2 q1p[4], q2p[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float e1 = fast_exp2(fmaf(s1[r], c2, -m1));
-            const float e2 = fast_exp2(fmaf(s2[r], c2, -m2));
-            ls1 += e1;
-            ls2 += e2;
-            p1[r >> 3][r & 7] = (bf16)e1;
-            p2[r >> 3][r & 7] = (bf16)e2;
-        }
-        l1 += ls1;
-        l2 += ls2;
-
-        // O^T += V^T P^T for both maps; each V^T fragment feeds both
+            for (int j = 0; j < 4; ++j) {
+                const int r = kb * 8 + 2 * j;
+                q1p[j] = bf16x2{(bf16)fast_exp2(fmaf(s1[r], c2, -m1)), (bf16)fast_exp2(fmaf(s1[r + 1], c2, -m1))};
+                q2p[j] = bf16x2{(bf16)fast_exp2(fmaf(s2[r], c2, -m2)), (bf16)fast_exp2(fmaf(s2[r + 1], c2, -m2))};
+                if (j & 1) {
+                    lb1 = __builtin_amdgcn_fdot2_f32_bf16(q1p[j], ones, lb1, false);
+                    lb2 = __builtin_amdgcn_fdot2_f32_bf16(q2p[j], ones, lb2, false);
+                } else {
+                    la1 = __builtin_amdgcn_fdot2_f32_bf16(q1p[j], ones, la1, false);
+                    la2 = __builtin_amdgcn_fdot2_f32_bf16(q2p[j], ones, la2, false);
+                }
+            }
+            p1[kb] = __builtin_shufflevector(__builtin_shufflevector(q1p[0], q1p[1], 0, 1, 2, 3),
+                                             __builtin_shufflevector(q1p[2], q1p[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+            p2[kb] = __builtin_shufflevector(__builtin_shufflevector(q2p[0], q2p[1], 0, 1, 2, 3),
+                                             __builtin_shufflevector(q2p[2], q2p[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 va[2][4];
+        auto read_v = [&](int kb) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int ct = 0; ct < 4; ++ct) {
                 const bf16* vp = (const bf16*)(Vs + voff[ct] + kb * 16 * (kDV * 2));
                 const i16x4 lo = lds_read_tr16(vp);
                 const i16x4 hi = lds_read_tr16(vp + 8 * kDV);
-                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o1[ct] = mfma32x32x16(va, p1[kb], o1[ct]);
-                o2[ct] = mfma32x32x16(va, p2[kb], o2[ct]);
+                va[kb][ct] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
+        };
+        auto pv = [&](int kb) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                o1[ct] = mfma32x32x16(va[kb][ct], p1[kb], o1[ct]);
+                o2[ct] = mfma32x32x16(va[kb][ct], p2[kb], o2[ct]);
+            }
+        };
+        read_v(0);
+        softmax_half(0);
+        constexpr bool kPrio = V2 ? DA_PRIO_V2 : DA_PRIO_V1;
+        constexpr bool kSched = V2 ? DA_SCHED_V2 : DA_SCHED_V1;
+        if (kPrio) __builtin_amdgcn_s_setprio(1);
+        pv(0);
+        softmax_half(1);
+        read_v(1);
+        pv(1);
+        if (kPrio) __builtin_amdgcn_s_setprio(0);
+        l1 += la1 + lb1;
+        l2 += la2 + lb2;
+        if (kSched) {
+        // 8 V reads, the first half's softmax, then each first-half MFMA followed by a sixth of
+        // the second half's softmax, the second half's V reads, and its MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
     }
 
