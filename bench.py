@@ -225,7 +225,8 @@ def main():
         gbs = nbytes / (avg * 1e-3) / 1e9
         secondary["v1_decode_64k"] = {"workload": c4.name, "split_plus_reduce_avg_ms": round(avg, 4),
                                       "min_ms": round(mn, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
-                                      "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+                                      "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                                      "traffic": load_traffic("v1_decode_64k", ["decode.hip", "common.hpp"])}
         log(f"[bench]   {avg:.3f} ms -> {gbs:.0f} GB/s")
         del x4, ws, o4
     if secondary:

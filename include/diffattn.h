@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
     DIFFATTN_OK = 0,
     DIFFATTN_ERR_ARG = 1,          /* invalid argument: null pointer, bad size or stride */
-    DIFFATTN_ERR_UNSUPPORTED = 2,  /* valid math that no kernel of this build serves */
+    DIFFATTN_ERR_UNSUPPORTED = 2,  /* valid math that no kernel of the library serves */
     DIFFATTN_ERR_WORKSPACE = 3,    /* workspace smaller than diffattn_decode_workspace_size() */
     DIFFATTN_ERR_HIP = 4           /* a HIP call or kernel launch failed */
 } diffattn_status;
