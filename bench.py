@@ -146,7 +146,7 @@ def main():
     achieved = flops / (fwd_avg_ms * 1e-3) / 1e12
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, fused forward kernel {fwd_avg_ms * 1e3:.1f} us "
         f"(min {min(fwd_ms) * 1e3:.1f}) -> {achieved:.1f} TFLOP/s")
-    traffic = load_traffic("v1_prefill_2k", ["fwd_mfma.hip", "common.hpp"])
+    traffic = load_traffic("v1_prefill_2k", ["fwd_v1.hip", "mfma_tile.hpp", "common.hpp"])
 
     result = {
         "metric": METRIC,
@@ -167,7 +167,7 @@ def main():
                    "flop_per_step": flops, "flop_per_visible_pair": FLOP_PER_PAIR_V1},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "fwd_mfma_kernel<64,V1,causal,epilogue>",
+                     "kernel": "fwd_v1_kernel<causal,epilogue>",
                      "kernel_avg_us": round(fwd_avg_ms * 1e3, 2)},
     }
     del x

@@ -1,17 +1,17 @@
-// Fused differential-attention forward on bf16 MFMA (gfx950), V1 and V2.
+// Fused differential-attention forward on bf16 MFMA (gfx950), one K/V tile at a time; serves
+// DIFF V2 (the V1 path runs the software-pipelined kernel of fwd_v1.hip, and the template's V1
+// layout, two K tiles per stage, is not instantiated).
 //
 // Computes, per query row, O = softmax(s Q1 K1^T) V - lambda softmax(s Q2 K2^T) V, which equals
 // (A1 - lambda A2) V exactly ("Differential Transformer: softmax can't say zero, so it subtracts",
 // section "What it costs": a fused kernel computes A1 V and A2 V because the maps are never
-// materialised). V1 follows "Noise-Canceling Attention by Subtraction", sections "The mechanism"
-// and "Making lambda learnable and stable" (RMSNorm * (1 - lambda_init) epilogue); V2 follows
-// "softmax can't say zero", section "DIFF V2: what the authors changed" (query heads 2p, 2p+1 of
-// one GQA group share K and V; lambda per token and pair; no norm).
+// materialised). V2 follows "softmax can't say zero", section "DIFF V2: what the authors changed"
+// (query heads 2p, 2p+1 of one GQA group share K and V; lambda per token and pair; no norm).
 //
 // Design (one pass over K/V, both maps at once):
-//  - A block owns a tile of query rows of one head (V1) or of every pair of one KV group (V2).
-//    Each wave owns 32 query rows of one pair. K/V tiles of 32 keys are staged through LDS,
-//    double buffered, so every tile is read from memory once per block and V once for both maps.
+//  - A block owns a tile of query rows of every pair of one KV group. Each wave owns 32 query
+//    rows of one pair. K/V tiles of 32 keys are staged through LDS, double buffered, so every tile
+//    is read from memory once per block and once for all query heads of the group.
 //  - Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane (n, h)
 //    then holds 16 keys of query n, so the running max and sum of each map are per-lane values
 //    (one exchange between lanes n and n+32 per tile).
@@ -21,10 +21,10 @@
 //  - Online softmax per map in base 2 (scale * log2 e folded into one FMA). The running maximum
 //    is only raised when a tile's maximum exceeds it by more than 8 (so unnormalised weights stay
 //    below 2^8); the final normalisation uses the same maximum, so the result is unchanged.
-//  - Epilogue in registers: O1/l1 - lambda O2/l2, then (V1) RMSNorm over the 128 channels and the
-//    (1 - lambda_init) multiply, stored as bf16.
+//  - Epilogue in registers: O1/l1 - lambda O2/l2, stored as bf16.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma_tile.hpp"
 
 namespace diffattn {
 
@@ -50,23 +50,6 @@ constexpr float kRescaleThreshold = 8.0f;
 #define DA_PRIO_V2 0
 #endif
 
-// LDS tiles are unpadded rows of 16-byte chunks, XOR-swizzled per row so that the MFMA operand
-// reads below hit distinct banks. A stage holds K1 (and K2 for V1) then V, 32 rows each, and is
-// filled by global_load_lds (16 bytes per lane, lane i of a wave writing base + 16 i): each lane
-// fetches the global chunk that belongs in its LDS slot, so no registers stage the tile.
-//  K, d = 64  (8 chunks per row):  phys = c ^ ((row & 7) ^ ((row >> 3) & 1))
-//  K, d = 128 (16 chunks per row): phys = c ^ (row & 15)
-//  V, 128 wide (16 chunks per row): phys = c ^ ((row & 3) << 1) ^ ((c & 2) << 2)
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-    return D == 64 ? ((row & 7) ^ ((row >> 3) & 1)) : (row & 15);
-}
-__device__ __forceinline__ int v_phys(int row, int c) { return c ^ ((row & 3) << 1) ^ ((c & 2) << 2); }
-__device__ __forceinline__ int v_logical(int row, int p) {
-    const int y = p ^ ((row & 3) << 1);
-    return y ^ ((y & 2) << 2);
-}
-
 template <int D, bool V2>
 struct Cfg {
     static constexpr int NW = V2 ? 8 : 4;              // waves per block
@@ -81,33 +64,6 @@ struct Cfg {
     static constexpr int V_LOADS = kBN * V_CPR / NT;
     static_assert(K_LOADS >= 1 && V_LOADS >= 1, "tile must cover every thread");
 };
-
-typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
-
-// 16-byte global -> LDS DMA for one wave: lane i reads sbase + voff (voff per lane) and the
-// chunk lands at LDS address lds_wave_base + 16 i. Issued from inline asm so that the compiler
-// does not track it as an LDS store: its generic tracking would otherwise wait for the next
-// tile's prefetch before every read of the current tile. Completion is ordered explicitly:
-// s_waitcnt vmcnt(0) and a barrier before a stage is read.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 : : "v"(voff), "s"(sbase), "s"(lds_wave_base) : "memory", "m0");
-}
-
-__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-
-__device__ __forceinline__ bf16x8 lds16(const unsigned char* p) { return *(const bf16x8*)p; }
-__device__ __forceinline__ bf16x8 ld_global_bf16x8(const bf16* p) { return *(const bf16x8*)p; }
-
-// value of x held by lane l ^ 32 combined with x: both halves of the wave get the same result
-__device__ __forceinline__ float max_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int D, bool V2, bool CAUSAL, bool EPI>
 __global__ __launch_bounds__(V2 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(V2 ? 1 : 2, 2)))
@@ -485,7 +441,6 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream) { return launch_fwd<64, false>(a, stream); }
 hipError_t launch_v2_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream) { return launch_fwd<128, true>(a, stream); }
 
 }  // namespace diffattn
