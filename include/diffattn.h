@@ -24,7 +24,7 @@
  *    elements, for the bf16 MFMA kernels; other layouts are served by the generic kernel.
  *  - Output dtype equals input dtype. `out` must not alias any input.
  *  - Ownership: the caller owns every buffer, the workspace and the stream. The library allocates
- *    no device memory and keeps no state beyond a per-device properties cache.
+ *    no device memory and keeps no state between calls except the thread-local error text.
  *  - Execution is asynchronous on `stream` (a hipStream_t; NULL = the default stream). Results are
  *    valid after the stream is synchronised. No entry point synchronises.
  *  - Errors: every argument is validated BEFORE any HIP call, so a non-OK return has launched
