@@ -7,12 +7,13 @@ forward. Inputs are synthetic (seeded) and resident in HBM before timing starts.
 line on stdout; progress goes to stderr.
 
 Also measured in the same run (reported under "secondary"): the 32K-token prefill with a planted
-needle, the 64K-entry decode (GB/s against HBM) and the V2 GQA prefill; and the fp64 oracle on a
-bounded sample of the main workload, timed on the host cores ("cpu_baseline").
+needle, the 64K-entry V1 decode and the V2 decode (GB/s against HBM) and the V2 GQA prefill; and
+the fp64 oracle on a bounded sample of the main workload, timed on the host cores ("cpu_baseline").
 
 Throughput counts algorithmic work only: 768 flop per visible (query, key) pair for V1 (two
 QK^T products of width 64 and two PV products of width 128), 512 per visible pair and query head
-for V2, and for decode the bytes of K1, K2 and V read once (512 B per cached token per head).
+for V2, and for decode the bytes of the cache read once (V1: K1, K2 and V, 512 B per cached token
+per head; V2: K and V, 512 B per cached token per KV head, shared by the group's query heads).
 """
 import argparse
 import hashlib
@@ -77,8 +78,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--secondary", default="32k,decode,v2",
-                    help="comma list of extra workloads to time (32k, decode, v2) or 'none'")
+    ap.add_argument("--secondary", default="32k,decode,v2,v2decode",
+                    help="comma list of extra workloads to time (32k, decode, v2, v2decode) or 'none'")
     ap.add_argument("--secondary-reps", type=int, default=10)
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the fp64 oracle on a sample (1) or not (0)")
     ap.add_argument("--copy-calibration", type=int, default=1,
@@ -154,7 +155,7 @@ def main():
     achieved = flops / (fwd_avg_ms * 1e-3) / 1e12
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, fused forward kernel {fwd_avg_ms * 1e3:.1f} us "
         f"(min {min(fwd_ms) * 1e3:.1f}) -> {achieved:.1f} TFLOP/s")
-    traffic = load_traffic("v1_prefill_2k", ["fwd_v1.hip", "mfma_tile.hpp", "common.hpp"])
+    traffic = load_traffic("v1_prefill_2k", ["fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"])
 
     result = {
         "metric": METRIC,
@@ -175,7 +176,7 @@ def main():
                    "flop_per_step": flops, "flop_per_visible_pair": FLOP_PER_PAIR_V1},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "fwd_v1_kernel<causal,epilogue>",
+                     "kernel": "fwd_mfma_kernel<64,V1,causal,epilogue>",
                      "kernel_avg_us": round(fwd_avg_ms * 1e3, 2),
                      "kernel_timing": f"{args.steps} back-to-back launches between two HIP events on the launch "
                                       "stream, right after the timed steps",
@@ -241,6 +242,27 @@ def main():
                                       "traffic": load_traffic("v1_decode_64k", ["decode.hip", "common.hpp"])}
         log(f"[bench]   {avg:.3f} ms -> {gbs:.0f} GB/s")
         del x4, ws, o4
+    if "v2decode" in which:
+        c6 = W.V2_DECODE_64K
+        log(f"[bench] {c6.name} (generating the cache on the device)")
+        x6 = W.v2_decode_inputs(c6, device=dev)
+        lam6 = x6["lam"].to(dev)
+        ws6 = torch.empty(da.diffattn_v2_decode_workspace_size(c6.B, c6.hq // 2, c6.hkv, c6.L), dtype=torch.uint8,
+                          device=dev)
+        o6 = torch.empty((c6.B, c6.hq // 2, c6.d), dtype=torch.bfloat16, device=dev)
+        f6 = lambda: da.diffattn_v2_decode(x6["q"], x6["k"], x6["v"], lam6, workspace=ws6, out=o6)
+        f6()
+        torch.cuda.synchronize()
+        avg, mn = time_launches(f6, args.secondary_reps, torch)
+        nbytes = 2 * c6.d * 2 * c6.B * c6.hkv * c6.L     # K and V rows read once per KV head
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        secondary["v2_decode_64k"] = {"workload": c6.name, "split_plus_reduce_avg_ms": round(avg, 4),
+                                      "min_ms": round(mn, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+                                      "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                                      "traffic": load_traffic("v2_decode_64k", ["decode_v2.hip", "mfma_tile.hpp",
+                                                                                "common.hpp"])}
+        log(f"[bench]   {avg:.3f} ms -> {gbs:.0f} GB/s")
+        del x6, ws6, o6
     if secondary:
         result["secondary"] = secondary
 

@@ -34,7 +34,8 @@ EPI_RMSNORM_SCALE = 1
 
 # Every symbol the header declares (tests check the library exports all of them).
 EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "diffattn_lambda",
-            "diffattn_fwd", "diffattn_decode_workspace_size", "diffattn_decode", "diffattn_v2_fwd")
+            "diffattn_fwd", "diffattn_decode_workspace_size", "diffattn_decode", "diffattn_v2_fwd",
+            "diffattn_v2_decode_workspace_size", "diffattn_v2_decode")
 
 
 class DiffAttnError(RuntimeError):
@@ -77,6 +78,10 @@ def lib():
                                       sz, vp]
         L.diffattn_v2_fwd.restype = i
         L.diffattn_v2_fwd.argtypes = [i, T, T, T, vp, i, i, i, i, i, i, f, T, vp]
+        L.diffattn_v2_decode_workspace_size.restype = sz
+        L.diffattn_v2_decode_workspace_size.argtypes = [i, i, i, i]
+        L.diffattn_v2_decode.restype = i
+        L.diffattn_v2_decode.argtypes = [i, T, T, T, vp, vp, i, i, i, i, i, f, T, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -194,6 +199,39 @@ def diffattn_v2_fwd(q, k, v, lam: torch.Tensor, causal: bool = True, scale: floa
     _check(lib().diffattn_v2_fwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), lam.data_ptr(), B, N, h, hkv,
                                  d, int(bool(causal)), float(scale), _t4(out), _stream(q.device)))
     return out
+
+
+def diffattn_v2_decode_workspace_size(batch: int, h: int, h_kv: int, cache_len: int) -> int:
+    return int(lib().diffattn_v2_decode_workspace_size(batch, h, h_kv, cache_len))
+
+
+def diffattn_v2_decode(q, kc, vc, lam: torch.Tensor, cache_lens: torch.Tensor | None = None,
+                       scale: float = 0.0, workspace: torch.Tensor | None = None,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """DIFF V2 decode. q: [B, 2h, d] (or [B, 1, 2h, d]); caches kc, vc: [B, L, h_kv, d];
+    lam: fp32 [B, h] contiguous; cache_lens: int32 [B] on the device or None. Returns [B, h, d]."""
+    if q.dim() == 3:
+        q = q.unsqueeze(1)
+    B, _, H2, d = q.shape
+    L, hkv = kc.shape[1], kc.shape[2]
+    h = H2 // 2
+    if H2 % 2:
+        raise ValueError("q must hold an even number of heads (2h)")
+    if not (lam.is_contiguous() and lam.dtype == torch.float32 and tuple(lam.shape) == (B, h)):
+        raise ValueError("lam must be a contiguous float32 [B, h] tensor")
+    if out is None:
+        out = torch.empty((B, 1, h, d), dtype=q.dtype, device=q.device)
+    elif out.dim() == 3:
+        out = out.unsqueeze(1)
+    need = diffattn_v2_decode_workspace_size(B, h, hkv, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if cache_lens is not None and cache_lens.dtype != torch.int32:
+        raise ValueError("cache_lens must be int32")
+    _check(lib().diffattn_v2_decode(_dtype_code(q), _t4(q), _t4(kc), _t4(vc), _ptr(cache_lens), lam.data_ptr(),
+                                    B, h, hkv, L, d, float(scale), _t4(out), workspace.data_ptr(),
+                                    workspace.numel(), _stream(q.device)))
+    return out.squeeze(1)
 
 
 def default_scale(d: int) -> float:

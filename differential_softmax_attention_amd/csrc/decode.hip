@@ -194,11 +194,13 @@ __global__ __launch_bounds__(kDV) void decode_reduce_kernel(DecodeArgs a) {
     const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
     const float* base = a.ws + ((int64_t)b * a.heads + h) * a.n_splits * kPartial;
     float M1 = -INFINITY, M2 = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < a.n_splits; ++s) {
         M1 = fmaxf(M1, base[s * kPartial + 0]);
         M2 = fmaxf(M2, base[s * kPartial + 2]);
     }
     float L1 = 0.f, L2 = 0.f, O1 = 0.f, O2 = 0.f;
+#pragma unroll 8
     for (int s = 0; s < a.n_splits; ++s) {
         const float* p = base + s * kPartial;
         const float f1 = (p[0] == -INFINITY) ? 0.f : fast_exp2(p[0] - M1);

@@ -264,4 +264,70 @@ diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
     return hip_status(diffattn::launch_generic(a, batch, h, dtype == DIFFATTN_BF16, st), "diffattn_v2_fwd launch");
 }
 
+size_t diffattn_v2_decode_workspace_size(int batch, int h, int h_kv, int cache_len) {
+    if (batch < 1 || h < 1 || h_kv < 1 || cache_len < 1) return 0;
+    if ((2 * h) % h_kv != 0) return 0;
+    return diffattn::v2_decode_workspace_bytes(batch, h, h_kv, cache_len);
+}
+
+diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor kc, diffattn_tensor vc,
+                                   const int32_t* cache_lens, const float* lam, int batch, int h, int h_kv,
+                                   int cache_len, int d, float scale, diffattn_tensor out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: unknown dtype %d", (int)dtype);
+    const diffattn_tensor* ts[4] = {&q, &kc, &vc, &out};
+    const char* names[4] = {"q", "kc", "vc", "out"};
+    for (int i = 0; i < 4; ++i)
+        if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
+    if (!lam) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: lam is null");
+    if (batch < 1 || h < 1 || h_kv < 1 || cache_len < 1 || d < 1)
+        return fail(DIFFATTN_ERR_ARG,
+                    "diffattn_v2_decode: sizes must be >= 1 (batch=%d h=%d h_kv=%d cache_len=%d d=%d)", batch, h,
+                    h_kv, cache_len, d);
+    if (batch > 65535 || h > 65535) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: batch and h must be <= 65535");
+    if ((2 * h) % h_kv != 0 || ((2 * h) / h_kv) % 2 != 0)
+        return fail(DIFFATTN_ERR_ARG,
+                    "diffattn_v2_decode: 2h=%d query heads must split into h_kv=%d groups of an even size (a pair may "
+                    "not straddle two groups)", 2 * h, h_kv);
+    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: scale must be finite");
+    if (d > 256) return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_v2_decode: d=%d exceeds the supported d <= 256", d);
+    const size_t need = diffattn_v2_decode_workspace_size(batch, h, h_kv, cache_len);
+    if (workspace_bytes < need)
+        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_v2_decode: workspace of %zu bytes < required %zu",
+                    workspace_bytes, need);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace) % 256 != 0))
+        return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: workspace must be non-null and 256-byte aligned");
+    const float sc = resolve_scale(scale, d);
+    hipStream_t st = (hipStream_t)stream;
+    const int group = (2 * h) / h_kv;
+
+    const bool split = dtype == DIFFATTN_BF16 && d == 128 && diffattn::v2_decode_group_ok(group) && vec16_ok(q) &&
+                       vec16_ok(kc) && vec16_ok(vc);
+    if (split) {
+        diffattn::V2DecodeArgs a{};
+        a.q = q.ptr; a.k = kc.ptr; a.v = vc.ptr; a.out = out.ptr;
+        copy_strides(a.qs, q); copy_strides(a.kcs, kc); copy_strides(a.vcs, vc); copy_strides(a.os, out);
+        a.cache_lens = cache_lens;
+        a.lam = lam;
+        a.lam_bs = h;
+        a.ws = (float*)workspace;
+        a.batch = batch; a.h = h; a.h_kv = h_kv; a.group = group; a.cache_len = cache_len;
+        a.scale_log2 = sc * 1.4426950408889634f;
+        return hip_status(diffattn::launch_v2_decode(a, st), "diffattn_v2_decode launch");
+    }
+    diffattn::GenericArgs a{};
+    a.q1 = q.ptr; a.q2 = q.ptr; a.k1 = kc.ptr; a.k2 = kc.ptr; a.v = vc.ptr; a.out = out.ptr;
+    copy_strides(a.q1s, q); copy_strides(a.q2s, q); copy_strides(a.k1s, kc); copy_strides(a.k2s, kc);
+    copy_strides(a.vs, vc); copy_strides(a.os, out);
+    a.q_hmul = 2; a.q1_hoff = 0; a.q2_hoff = 1; a.kv_hdiv = group;
+    a.lam = lam;
+    a.lams[0] = h; a.lams[1] = 0; a.lams[2] = 1;
+    a.key_lens = cache_lens;
+    a.seq_q = 1; a.seq_k = cache_len; a.d = d; a.dv = d;
+    a.causal = 0;
+    a.epi = 0;
+    a.norm_w = nullptr; a.eps = 0.f; a.lambda_init = 0.f; a.scale = sc;
+    return hip_status(diffattn::launch_generic(a, batch, h, dtype == DIFFATTN_BF16, st), "diffattn_v2_decode launch");
+}
+
 }  // extern "C"

@@ -1,27 +1,32 @@
-// Fused differential-attention forward on bf16 MFMA (gfx950), one K/V tile at a time; serves
-// DIFF V2 (the V1 path runs the software-pipelined kernel of fwd_v1.hip, and the template's V1
-// layout, two K tiles per stage, is not instantiated).
+// Fused differential-attention forward on bf16 MFMA (gfx950), V1 and V2.
 //
 // Computes, per query row, O = softmax(s Q1 K1^T) V - lambda softmax(s Q2 K2^T) V, which equals
 // (A1 - lambda A2) V exactly ("Differential Transformer: softmax can't say zero, so it subtracts",
 // section "What it costs": a fused kernel computes A1 V and A2 V because the maps are never
-// materialised). V2 follows "softmax can't say zero", section "DIFF V2: what the authors changed"
-// (query heads 2p, 2p+1 of one GQA group share K and V; lambda per token and pair; no norm).
+// materialised). V1 follows "Noise-Canceling Attention by Subtraction", sections "The mechanism"
+// and "Making lambda learnable and stable" (RMSNorm * (1 - lambda_init) epilogue); V2 follows
+// "softmax can't say zero", section "DIFF V2: what the authors changed" (query heads 2p, 2p+1 of
+// one GQA group share K and V; lambda per token and pair; no norm).
 //
 // Design (one pass over K/V, both maps at once):
-//  - A block owns a tile of query rows of every pair of one KV group. Each wave owns 32 query
-//    rows of one pair. K/V tiles of 32 keys are staged through LDS, double buffered, so every tile
-//    is read from memory once per block and once for all query heads of the group.
+//  - A block owns a tile of query rows of one head (V1) or of every pair of one KV group (V2).
+//    Each wave owns 32 query rows of one pair. K/V tiles of 32 keys are staged through LDS,
+//    double buffered, so every tile is read from memory once per block and V once for both maps.
 //  - Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane (n, h)
 //    then holds 16 keys of query n, so the running max and sum of each map are per-lane values
 //    (one exchange between lanes n and n+32 per tile).
 //  - The output is accumulated transposed, O^T += V^T P^T: P^T comes straight from the score
 //    registers (rounded to bf16), V^T is read from the row-major V tile with the gfx950
 //    transposing LDS read (ds_read_b64_tr_b16), so V is never transposed in registers.
-//  - Online softmax per map in base 2 (scale * log2 e folded into one FMA). The running maximum
-//    is only raised when a tile's maximum exceeds it by more than 8 (so unnormalised weights stay
-//    below 2^8); the final normalisation uses the same maximum, so the result is unchanged.
-//  - Epilogue in registers: O1/l1 - lambda O2/l2, stored as bf16.
+//  - Online softmax per map in base 2, the scale * log2 e applied to the fp32 scores in the same
+//    FMA that subtracts the running maximum (Q is used as given, so the logits carry no extra
+//    rounding). The running maximum is only raised when a tile's maximum exceeds it by more than
+//    8 (so unnormalised weights stay below 2^8); the final normalisation uses the same maximum,
+//    so the result is unchanged.
+//  - Each tile's softmax is split by key half so that the first half's MFMAs overlap the second
+//    half's exponentials; V1 raises the wave priority while it issues MFMAs.
+//  - Epilogue in registers: O1/l1 - lambda O2/l2, then (V1) RMSNorm over the 128 channels and the
+//    (1 - lambda_init) multiply, stored as bf16.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
@@ -441,6 +446,7 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream) { return launch_fwd<64, false>(a, stream); }
 hipError_t launch_v2_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream) { return launch_fwd<128, true>(a, stream); }
 
 }  // namespace diffattn

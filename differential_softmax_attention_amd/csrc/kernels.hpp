@@ -64,6 +64,25 @@ int decode_num_splits(int batch, int heads, int cache_len);
 size_t decode_workspace_bytes(int batch, int heads, int cache_len, int dv);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// V2 split-K decode (bf16, d = 128, 2 <= group <= 32): q [batch, 1, 2h, d], caches
+// [batch, L, h_kv, d], lambda [batch, h] at lam[b * lam_bs + p], out [batch, 1, h, d].
+struct V2DecodeArgs {
+    const void *q, *k, *v;
+    void* out;
+    int64_t qs[3], kcs[3], vcs[3], os[3];
+    const int32_t* cache_lens;
+    const float* lam;
+    int64_t lam_bs;
+    float* ws;  // workspace: per-slice partials
+    int batch, h, h_kv, group, cache_len, n_splits, split_len;
+    float scale_log2;
+};
+
+int v2_decode_num_splits(int batch, int h_kv, int cache_len);
+size_t v2_decode_workspace_bytes(int batch, int h, int h_kv, int cache_len);
+bool v2_decode_group_ok(int group);
+hipError_t launch_v2_decode(V2DecodeArgs a, hipStream_t stream);
+
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
                          int n, int dim, float lambda_init, float* out, hipStream_t stream);
 

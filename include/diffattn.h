@@ -164,6 +164,38 @@ diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
                                 int h_kv, int d, int causal, float scale, diffattn_tensor out,
                                 void* stream);
 
+/*
+ * Bytes of device workspace diffattn_v2_decode needs for these sizes (0 on invalid sizes). The
+ * workspace holds, per cache slice and query head, the slice's shift, weight sum and 128-wide
+ * accumulator in fp32.
+ */
+size_t diffattn_v2_decode_workspace_size(int batch, int h, int h_kv, int cache_len);
+
+/*
+ * DIFF V2 decode: the new token's 2h query heads against a GQA KV cache; output pair p is
+ * O_{2p} - lam[b, p] * O_{2p+1}, where O_j is ordinary softmax attention of query head j over the
+ * first len cache entries of KV head j / (2h / h_kv) ("softmax can't say zero", section "DIFF V2:
+ * what the authors changed"; "Differential Transformer V2": decode reads the cache as ordinary GQA
+ * attention does). The token's own key and value are expected to be in the cache already.
+ *  q: [batch, 1, 2h, d] (the token stride is unused);  kc, vc: [batch, cache_len, h_kv, d]
+ *  cache_lens: DEVICE int32 [batch] with 1 <= len <= cache_len, or NULL (every len = cache_len);
+ *              an entry outside that range is clamped into it on the device.
+ *  lam: DEVICE fp32 [batch, h] contiguous, used as given.   out: [batch, 1, h, d].
+ *  scale: softmax scale; <= 0 selects 1/sqrt(d).
+ *  workspace: DEVICE buffer of at least diffattn_v2_decode_workspace_size(...) bytes, 256-byte
+ *  aligned; its contents on entry do not matter.
+ *  Requires 2h divisible by h_kv with an even group size. Kernels: bf16 with d = 128, a group of
+ *  2..32 query heads and aligned strides runs a split-K MFMA kernel that reads each cached K and V
+ *  row once for the whole group, then a reduction that merges the slices in a fixed order (no
+ *  atomics); other cases run the generic kernel.
+ *  Errors: ERR_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED (d > 256), ERR_HIP.
+ */
+diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor kc,
+                                   diffattn_tensor vc, const int32_t* cache_lens, const float* lam,
+                                   int batch, int h, int h_kv, int cache_len, int d, float scale,
+                                   diffattn_tensor out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -212,3 +212,29 @@ def v2_forward(q, k, v, lam_tok, causal=True, scale=None, rows=None):
             out[sel] = _head(q[b, :, 2 * p], q[b, :, 2 * p + 1], k[b, :, g], k[b, :, g],
                              v[b, :, g], lam_tok[b, :, p], causal, s, rows[sel, 2])
     return out
+
+def v2_decode(q, kc, vc, lam_pairs, cache_lens=None, scale=None, pairs=None):
+    """DIFF V2 decode: the new token's query heads against the first cache_lens[b] cached keys.
+
+    Each pair p subtracts query head 2p+1's attention from head 2p's with the token's lambda, both
+    over the KV head of their GQA group ("softmax can't say zero", section "DIFF V2: what the
+    authors changed"); no norm. q: [B, 2h, d]; kc, vc: [B, L, h_kv, d]; lam_pairs: [B, h].
+    pairs: None for every (b, p), else an int array [n, 2] of (b, p); returns [B, h, d] or [n, d].
+    """
+    q, kc, vc, lam_pairs = (np.asarray(x) for x in (q, kc, vc, lam_pairs))
+    B, H2, d = q.shape
+    L, hkv = kc.shape[1], kc.shape[2]
+    group = H2 // hkv
+    s = default_scale(d) if scale is None else float(scale)
+    lens = np.full(B, L, dtype=np.int64) if cache_lens is None else np.asarray(cache_lens, np.int64)
+    full = pairs is None
+    if full:
+        pairs = np.array([(b, p) for b in range(B) for p in range(H2 // 2)], dtype=np.int64)
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    out = np.empty((pairs.shape[0], vc.shape[3]), dtype=np.float64)
+    for n, (b, p) in enumerate(pairs):
+        n_b = int(lens[b])
+        g = (2 * p) // group
+        out[n] = _head(q[b, 2 * p][None], q[b, 2 * p + 1][None], kc[b, :n_b, g], kc[b, :n_b, g],
+                       vc[b, :n_b, g], np.array([lam_pairs[b, p]]), False, s, None)[0]
+    return out.reshape(B, H2 // 2, -1) if full else out

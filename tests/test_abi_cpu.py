@@ -133,6 +133,36 @@ def test_v2_rejects(L):
     assert _v2(L, dtype=9) == da.DIFFATTN_ERR_ARG
 
 
+def _v2dec(L, B=2, h=8, hkv=2, Lc=300, d=128, lam=FAKE, ws=FAKE, ws_bytes=1 << 30, dtype=1, lens=None):
+    ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(4)]
+    return L.diffattn_v2_decode(dtype, ts[0], ts[1], ts[2], lens, lam, B, h, hkv, Lc, d, 0.0, ts[3], ws,
+                                ws_bytes, None)
+
+
+def test_v2_decode_rejects(L):
+    assert _v2dec(L, hkv=3) == da.DIFFATTN_ERR_ARG         # 16 query heads into 3 groups
+    assert _v2dec(L, h=3, hkv=2) == da.DIFFATTN_ERR_ARG    # groups of 3 heads
+    assert _v2dec(L, lam=None) == da.DIFFATTN_ERR_ARG
+    assert _v2dec(L, Lc=0) == da.DIFFATTN_ERR_ARG
+    assert _v2dec(L, B=0) == da.DIFFATTN_ERR_ARG
+    assert _v2dec(L, dtype=9) == da.DIFFATTN_ERR_ARG
+    need = L.diffattn_v2_decode_workspace_size(2, 8, 2, 300)
+    assert need > 0
+    assert _v2dec(L, ws_bytes=need - 1) == da.DIFFATTN_ERR_WORKSPACE
+    assert _v2dec(L, ws=None) == da.DIFFATTN_ERR_ARG
+    assert _v2dec(L, ws=FAKE + 64) == da.DIFFATTN_ERR_ARG      # not 256-byte aligned
+    assert _v2dec(L, d=512) == da.DIFFATTN_ERR_UNSUPPORTED
+
+
+def test_v2_decode_workspace_size(L):
+    assert L.diffattn_v2_decode_workspace_size(0, 32, 8, 100) == 0
+    assert L.diffattn_v2_decode_workspace_size(1, 32, 8, 0) == 0
+    assert L.diffattn_v2_decode_workspace_size(1, 3, 4, 100) == 0      # 6 heads do not split into 4
+    small = L.diffattn_v2_decode_workspace_size(1, 1, 1, 1)
+    big = L.diffattn_v2_decode_workspace_size(32, 32, 8, 65536)
+    assert 0 < small < big < 64 << 20      # slice partials only
+
+
 def test_lambda_rejects(L):
     assert L.diffattn_lambda(FAKE, FAKE, FAKE, FAKE, 0, 64, 12, FAKE, None) == da.DIFFATTN_ERR_ARG
     assert L.diffattn_lambda(FAKE, FAKE, FAKE, FAKE, 16, 0, 12, FAKE, None) == da.DIFFATTN_ERR_ARG

@@ -371,3 +371,42 @@ def test_v2_uniform_attention_rms():
     o = oracle.v2_forward(q, k, v, np.zeros((1, n, 1)), causal=True, rows=rows)
     rms = np.sqrt(np.mean(o ** 2))
     assert rms == pytest.approx(1 / math.sqrt(n), rel=0.25)
+
+
+def test_v2_decode_single_query_gqa_attention():
+    # V2 decode with lambda = 0 is one query of ordinary GQA attention over the cache prefix
+    # (a library routine), and with lambda = 1 it is the difference of the pair's two heads.
+    rng = np.random.default_rng(14)
+    B, L, hq, hkv, d = 3, 37, 8, 2, 6
+    q = rng.standard_normal((B, hq, d))
+    kc = rng.standard_normal((B, L, hkv, d))
+    vc = rng.standard_normal((B, L, hkv, d))
+    lens = np.array([L, 1, 20])
+    rep = hq // hkv
+    refs = []
+    for b in range(B):
+        n = lens[b]
+        qq = torch.from_numpy(q[b])[:, None, :]                               # [hq, 1, d]
+        kk = torch.from_numpy(kc[b, :n]).permute(1, 0, 2).repeat_interleave(rep, dim=0)
+        vv = torch.from_numpy(vc[b, :n]).permute(1, 0, 2).repeat_interleave(rep, dim=0)
+        refs.append(torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[:, 0].numpy())
+    ref = np.stack(refs)                                                       # [B, hq, d]
+    o0 = oracle.v2_decode(q, kc, vc, np.zeros((B, hq // 2)), cache_lens=lens)
+    assert np.allclose(o0, ref[:, 0::2], atol=1e-12, rtol=0)
+    o1 = oracle.v2_decode(q, kc, vc, np.ones((B, hq // 2)), cache_lens=lens)
+    assert np.allclose(o1, ref[:, 0::2] - ref[:, 1::2], atol=1e-12, rtol=0)
+    # a cache of length 1 returns that row's value for every head: weights are exactly 1
+    assert np.allclose(o0[1], vc[1, 0][[(2 * p) // rep for p in range(hq // 2)]], atol=1e-15, rtol=0)
+
+
+def test_v2_decode_is_last_causal_row():
+    # decoding the last token against the full cache is the last row of the causal V2 forward
+    rng = np.random.default_rng(15)
+    B, N, hq, hkv, d = 2, 29, 4, 2, 5
+    q = rng.standard_normal((B, N, hq, d))
+    k = rng.standard_normal((B, N, hkv, d))
+    v = rng.standard_normal((B, N, hkv, d))
+    lam = rng.uniform(0, 1, (B, N, hq // 2))
+    fwd = oracle.v2_forward(q, k, v, lam, causal=True)
+    dec = oracle.v2_decode(q[:, -1], k, v, lam[:, -1])
+    assert np.array_equal(dec, fwd[:, -1])

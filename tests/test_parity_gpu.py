@@ -153,6 +153,15 @@ def test_bf16_v1_large_logits(top):
     assert maxerr(out, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_v1_dense_large_logits(causal):
+    # every logit large: std 12 in natural units (17 in base 2), so each row's weights hinge on
+    # small logit differences between many competing keys
+    out, ref = v1_case(1, 900, 900, 2, 64, 128, torch.bfloat16, 650, causal=causal, epilogue=False,
+                       qscale=12.0)
+    assert maxerr(out, ref) <= TOL_BF16
+
+
 def test_bf16_generic_fallback_shape():
     out, ref = v1_case(2, 70, 70, 2, 32, 64, torch.bfloat16, 700, causal=True, epilogue=True)
     assert maxerr(out, ref) <= TOL_BF16
@@ -279,6 +288,79 @@ def test_v2_generic_fallback():
 
 
 # ------------------------------------------------------------------------------------------------
+# V2 decode
+# ------------------------------------------------------------------------------------------------
+
+def v2_decode_case(B, L, hq, hkv, d, seed, lens=None, dtype=torch.bfloat16, qscale=1.0):
+    q = rand((B, hq, d), seed, dtype, scale=qscale)
+    k = rand((B, L, hkv, d), seed + 1, dtype)
+    v = rand((B, L, hkv, d), seed + 2, dtype)
+    g = torch.Generator().manual_seed(seed + 3)
+    lam = torch.rand((B, hq // 2), generator=g)
+    lens_t = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    note(f"v2 decode case B={B} L={L} hq={hq} hkv={hkv} d={d} lens={lens} qscale={qscale}")
+    out = da.diffattn_v2_decode(q, k, v, lam.to(DEV), cache_lens=lens_t)
+    torch.cuda.synchronize()
+    ref = oracle.v2_decode(f64(q), f64(k), f64(v), lam.numpy(), cache_lens=lens)
+    return f64(out), ref
+
+
+@pytest.mark.parametrize("L", [1, 7, 32, 33, 300, 5000])
+def test_v2_decode_shapes(L):
+    out, ref = v2_decode_case(3, L, 16, 2, 128, 1300 + L)
+    assert maxerr(out, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (32, 1), (64, 8), (64, 2)])
+def test_v2_decode_groupings(hq, hkv):
+    out, ref = v2_decode_case(2, 700, hq, hkv, 128, 1400 + hq + hkv)
+    assert maxerr(out, ref) <= TOL_BF16
+
+
+def test_v2_decode_ragged_lengths():
+    out, ref = v2_decode_case(4, 3000, 16, 4, 128, 1500, lens=[3000, 1, 129, 2047])
+    assert maxerr(out, ref) <= TOL_BF16
+
+
+def test_v2_decode_large_logits():
+    # logits far outside +-60 (base 2) put the waves in shifted mode
+    out, ref = v2_decode_case(2, 900, 8, 2, 128, 1550, qscale=12.0)
+    assert maxerr(out, ref) <= TOL_BF16
+
+
+def test_v2_decode_generic_fallback():
+    out, ref = v2_decode_case(2, 300, 8, 2, 64, 1600)                  # d = 64
+    assert maxerr(out, ref) <= TOL_BF16
+    out, ref = v2_decode_case(1, 200, 48, 1, 128, 1601)                # a group of 48 heads
+    assert maxerr(out, ref) <= TOL_BF16
+    out, ref = v2_decode_case(2, 100, 8, 4, 16, 1602, dtype=torch.float32)
+    assert maxerr(out, ref) <= TOL_F32
+
+
+def test_v2_decode_equals_last_prefill_row():
+    B, N, hq, hkv = 2, 333, 16, 4
+    q = rand((B, N, hq, 128), 1700, torch.bfloat16)
+    k = rand((B, N, hkv, 128), 1701, torch.bfloat16)
+    v = rand((B, N, hkv, 128), 1702, torch.bfloat16)
+    lam = torch.rand((B, N, hq // 2), generator=torch.Generator().manual_seed(1703)).to(DEV)
+    fwd = da.diffattn_v2_fwd(q, k, v, lam, causal=True)
+    dec = da.diffattn_v2_decode(q[:, -1], k, v, lam[:, -1].contiguous())
+    torch.cuda.synchronize()
+    assert maxerr(f64(dec), f64(fwd[:, -1])) <= TOL_BF16
+
+
+def test_v2_decode_deterministic():
+    q = rand((2, 16, 128), 1800, torch.bfloat16)
+    k = rand((2, 4000, 2, 128), 1801, torch.bfloat16)
+    v = rand((2, 4000, 2, 128), 1802, torch.bfloat16)
+    lam = torch.rand((2, 8), generator=torch.Generator().manual_seed(1803)).to(DEV)
+    a = da.diffattn_v2_decode(q, k, v, lam)
+    b = da.diffattn_v2_decode(q, k, v, lam)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------------
 # full-size workloads, sampled rows (same launch configuration as the benchmark)
 # ------------------------------------------------------------------------------------------------
 
@@ -373,3 +455,28 @@ def test_full_v2_8k():
                             x["lam"].cpu().numpy(), causal=True, rows=rows)
     got = out.float().cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
     assert maxerr(got, ref) <= TOL_BF16
+
+
+def test_full_v2_decode_64k():
+    cfg = W.V2_DECODE_64K
+    note(f"full {cfg.name}: generating the 8.6 GB cache on the device")
+    x = W.v2_decode_inputs(cfg, device=DEV)
+    lam = x["lam"].to(DEV)
+    out = da.diffattn_v2_decode(x["q"], x["k"], x["v"], lam)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    h = cfg.hq // 2
+    pairs = [(0, 0), (cfg.B - 1, h - 1)] + [(int(b), int(p)) for b, p in
+                                             zip(rng.integers(0, cfg.B, 6), rng.integers(0, h, 6))]
+    got = out.float().cpu().numpy()
+    group = cfg.hq // cfg.hkv
+    for b, p in pairs:
+        g = (2 * p) // group
+        # the pair's KV head only: query heads 2p, 2p+1 of one group read KV head g
+        ref = oracle.v2_decode(x["q"][b:b + 1, 2 * p:2 * p + 2].float().cpu().numpy(),
+                               x["k"][b:b + 1, :, g:g + 1].float().cpu().numpy(),
+                               x["v"][b:b + 1, :, g:g + 1].float().cpu().numpy(),
+                               lam[b:b + 1, p:p + 1].cpu().numpy())
+        assert maxerr(got[b, p], ref[0, 0]) <= TOL_BF16, (b, p)
+    del x
+    torch.cuda.empty_cache()

@@ -82,6 +82,17 @@ class V2Config:
     seed: int
 
 
+@dataclass(frozen=True)
+class V2DecodeConfig:
+    name: str
+    B: int
+    L: int
+    hq: int               # query heads (2h)
+    hkv: int
+    d: int
+    seed: int
+
+
 FP32_SINGLE_HEAD = V1Config("fp32 single head N=64 d=8 dv=16", B=1, H=1, N=64, d=8, dv=16,
                             causal=False, epilogue=False, dtype="f32", seed=1, lam_fixed=0.8)
 V1_PREFILL_2K = V1Config("V1 prefill B=4 H=16 N=2048 d=64 dv=128 causal", B=4, H=16, N=2048, d=64,
@@ -93,6 +104,9 @@ V1_DECODE_64K = DecodeConfig("V1 decode B=32 H=16 L=65536 d=64 dv=128", B=32, H=
                              dv=128, seed=4)
 V2_GQA_8K = V2Config("V2 GQA prefill B=2 N=8192 64q/8kv heads d=128 causal", B=2, N=8192, hq=64,
                      hkv=8, d=128, causal=True, seed=5)
+# V2 decode: the V2 prefill's head layout against a 64K cache per sequence (as the V1 decode)
+V2_DECODE_64K = V2DecodeConfig("V2 decode B=32 L=65536 64q/8kv heads d=128", B=32, L=65536, hq=64,
+                               hkv=8, d=128, seed=6)
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -182,4 +196,18 @@ def v2_inputs(cfg: V2Config, device="cpu", B=None, N=None) -> dict:
     k = _normal((B, N, cfg.hkv, cfg.d), g, device, dt)
     v = _normal((B, N, cfg.hkv, cfg.d), g, device, dt)
     lam = torch.rand((B, N, cfg.hq // 2), generator=g, device=device, dtype=torch.float32)
+    return dict(q=q, k=k, v=v, lam=lam)
+
+
+def v2_decode_inputs(cfg: V2DecodeConfig, device="cpu", B=None, L=None) -> dict:
+    """q: [B, 2h, d]; K, V caches [B, L, h_kv, d]; lambda [B, h] ~ U[0, 1)."""
+    B = cfg.B if B is None else B
+    L = cfg.L if L is None else L
+    dt = torch.bfloat16
+    g = _gen(cfg.seed, device)
+    q = _normal((B, cfg.hq, cfg.d), g, device, dt)
+    k = _normal((B, L, cfg.hkv, cfg.d), g, device, dt, chunk_dim0=True)
+    v = _normal((B, L, cfg.hkv, cfg.d), g, device, dt, chunk_dim0=True)
+    gl = _gen(cfg.seed + 1000, "cpu")
+    lam = torch.rand((B, cfg.hq // 2), generator=gl, dtype=torch.float32)
     return dict(q=q, k=k, v=v, lam=lam)
