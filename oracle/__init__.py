@@ -48,6 +48,10 @@ def _load():
         lib.oracle_rmsnorm_scale.restype = None
         lib.oracle_rmsnorm_scale.argtypes = [dp, ctypes.c_int, ctypes.c_int, dp,
                                              ctypes.c_double, ctypes.c_double]
+        lib.oracle_diff_head_bwd.restype = ctypes.c_int
+        lib.oracle_diff_head_bwd.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, dp, ctypes.c_int,
+                                             ctypes.c_double, dp, dp, dp, dp, dp, dp, dp]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -238,3 +242,66 @@ def v2_decode(q, kc, vc, lam_pairs, cache_lens=None, scale=None, pairs=None):
         out[n] = _head(q[b, 2 * p][None], q[b, 2 * p + 1][None], kc[b, :n_b, g], kc[b, :n_b, g],
                        vc[b, :n_b, g], np.array([lam_pairs[b, p]]), False, s, None)[0]
     return out.reshape(B, H2 // 2, -1) if full else out
+
+
+def v1_backward(q1, q2, k1, k2, v, lam_heads, dy, causal=True, epilogue=True, lambda_init_value=0.8,
+                g=None, eps=1e-5, scale=None):
+    """Gradients of the DIFF V1 forward (v1_forward) with respect to every input, for L = sum(dy * y).
+
+    The RMSNorm part follows from y = k w o / r with r = sqrt(mean_c o_c^2 + eps), k = 1 - lambda_init
+    ("Noise-Canceling Attention by Subtraction", section "Making lambda learnable and stable"):
+    dL/dw_c = sum dy_c k o_c / r and dL/do = (du - u mean_c(du_c u_c)) / r with u = o / r,
+    du = k w dy. The map part is oracle_diff_head_bwd. Shapes as v1_forward; dy: [B, N, H, dv].
+    Returns a dict with dq1, dq2, dk1, dk2, dv (shaped like the inputs), dlam [H] and dg [dv]
+    (None without epilogue).
+    """
+    q1, q2, k1, k2, v, dy = (np.asarray(x, dtype=np.float64) for x in (q1, q2, k1, k2, v, dy))
+    B, Nq, H, d = q1.shape
+    Nk, dv = k1.shape[1], v.shape[3]
+    s = default_scale(d) if scale is None else float(scale)
+    lam_heads = np.asarray(lam_heads, dtype=np.float64).reshape(-1)
+    grads = {k: np.zeros_like(x) for k, x in (("dq1", q1), ("dq2", q2), ("dk1", k1), ("dk2", k2), ("dv", v))}
+    dlam = np.zeros(H)
+    dg = np.zeros(dv) if epilogue else None
+    w = np.ones(dv) if g is None else np.asarray(g, dtype=np.float64)
+    kappa = 1.0 - lambda_init_value
+    L = _load()
+    for b in range(B):
+        for h in range(H):
+            lam_rows = np.full(Nq, lam_heads[h])
+            args = [_f64(x[b, :, h]) for x in (q1, q2, k1, k2, v)]
+            o = _head(*args, lam_rows, causal, s, None)                 # [Nq, dv], pre-norm
+            gy = dy[b, :, h]
+            if epilogue:
+                r = np.sqrt(np.mean(o * o, axis=1, keepdims=True) + eps)
+                u = o / r
+                dg += np.sum(gy * kappa * u, axis=0)
+                du = kappa * w[None, :] * gy
+                go = (du - u * np.mean(du * u, axis=1, keepdims=True)) / r
+            else:
+                go = gy
+            go = _f64(go)
+            outs = [np.empty((Nq, d)), np.empty((Nq, d)), np.empty((Nk, d)), np.empty((Nk, d)),
+                    np.empty((Nk, dv)), np.empty(Nq)]
+            rc = L.oracle_diff_head_bwd(*(_ptr(x) for x in args), Nq, Nk, d, dv, _ptr(lam_rows),
+                                        int(bool(causal)), s, _ptr(go), *(_ptr(x) for x in outs))
+            if rc != 0:
+                raise ValueError("oracle_diff_head_bwd failed (a row with no visible key?)")
+            for key, x in zip(("dq1", "dq2", "dk1", "dk2", "dv"), outs[:5]):
+                grads[key][b, :, h] = x
+            dlam[h] += outs[5].sum()
+    grads["dlam"] = dlam
+    grads["dg"] = dg
+    return grads
+
+
+def lambda_backward(lq1, lk1, lq2, lk2, dlam):
+    """Gradients of lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init with respect to the four
+    vectors ("Noise-Canceling Attention by Subtraction", section "Making lambda learnable and
+    stable"), one row per head: d/dlq1 = dlam exp(lq1 . lk1) lk1, d/dlk1 = dlam exp(lq1 . lk1) lq1,
+    and the same with a minus sign for the second pair."""
+    lq1, lk1, lq2, lk2 = (np.atleast_2d(np.asarray(x, dtype=np.float64)) for x in (lq1, lk1, lq2, lk2))
+    dlam = np.asarray(dlam, dtype=np.float64).reshape(-1, 1)
+    e1 = np.exp(np.sum(lq1 * lk1, axis=1, keepdims=True))
+    e2 = np.exp(np.sum(lq2 * lk2, axis=1, keepdims=True))
+    return dict(dlq1=dlam * e1 * lk1, dlk1=dlam * e1 * lq1, dlq2=-dlam * e2 * lk2, dlk2=-dlam * e2 * lq2)

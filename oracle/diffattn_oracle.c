@@ -165,6 +165,78 @@ void oracle_rmsnorm_scale(double* o, int nrows, int dv, const double* g,
     }
 }
 
+/* Gradients of one head's differential map, taken by the chain rule through the
+ * definition that oracle_diff_head evaluates (no epilogue; the RMSNorm part is
+ * differentiated by the caller). Given go = dL/do for every row, with
+ * o_i = sum_j (A1_ij - lam_i A2_ij) v_j and A = softmax over the visible keys:
+ *   dL/dA1_ij = go_i . v_j,   dL/dA2_ij = -lam_i (go_i . v_j)
+ *   softmax:  dL/dS_ij = A_ij (dL/dA_ij - sum_k A_ik dL/dA_ik)
+ *   S = scale q K^T:  dq_i = scale sum_j dL/dS_ij k_j,  dk_j += scale dL/dS_ij q_i
+ *   dv_j += (A1_ij - lam_i A2_ij) go_i,   dlam_i = -go_i . (A2 V)_i
+ * Shapes as oracle_diff_head (rows are all nq rows); dk1, dk2, dvv are
+ * overwritten. Rows are taken in order on one thread (the key-side gradients
+ * accumulate over rows). Returns 0, or -1 if a row sees no key or on
+ * allocation failure. */
+int oracle_diff_head_bwd(const double* q1, const double* q2, const double* k1,
+                         const double* k2, const double* v, int nq, int nk, int d,
+                         int dv, const double* lam_rows, int causal, double scale,
+                         const double* go, double* dq1, double* dq2, double* dk1,
+                         double* dk2, double* dvv, double* dlam_rows) {
+    double* a1 = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+    double* a2 = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+    double* da = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+    if (!a1 || !a2 || !da) { free(a1); free(a2); free(da); return -1; }
+    memset(dk1, 0, sizeof(double) * (size_t)nk * d);
+    memset(dk2, 0, sizeof(double) * (size_t)nk * d);
+    memset(dvv, 0, sizeof(double) * (size_t)nk * dv);
+    int err = 0;
+    for (int i = 0; i < nq && !err; ++i) {
+        int n = visible_keys(i, nq, nk, causal);
+        if (n <= 0) { err = -1; break; }
+        const double* q1i = q1 + (int64_t)i * d;
+        const double* q2i = q2 + (int64_t)i * d;
+        const double* gi = go + (int64_t)i * dv;
+        double lam = lam_rows[i];
+        for (int j = 0; j < n; ++j) {
+            double s1 = 0.0, s2 = 0.0;
+            for (int c = 0; c < d; ++c) {
+                s1 += q1i[c] * k1[(int64_t)j * d + c];
+                s2 += q2i[c] * k2[(int64_t)j * d + c];
+            }
+            a1[j] = scale * s1;
+            a2[j] = scale * s2;
+        }
+        softmax_inplace(a1, n);
+        softmax_inplace(a2, n);
+        /* dL/dA (up to the map's factor): go_i . v_j, and the row sums of A * dL/dA */
+        double r1 = 0.0, r2 = 0.0, dl = 0.0;
+        for (int j = 0; j < n; ++j) {
+            double t = 0.0;
+            for (int c = 0; c < dv; ++c) t += gi[c] * v[(int64_t)j * dv + c];
+            da[j] = t;
+            r1 += a1[j] * t;
+            r2 += a2[j] * t;
+        }
+        dl = -r2;   /* go_i . (A2 V)_i = sum_j A2_ij (go_i . v_j) */
+        dlam_rows[i] = dl;
+        for (int c = 0; c < d; ++c) { dq1[(int64_t)i * d + c] = 0.0; dq2[(int64_t)i * d + c] = 0.0; }
+        for (int j = 0; j < n; ++j) {
+            double ds1 = a1[j] * (da[j] - r1);
+            double ds2 = -lam * a2[j] * (da[j] - r2);
+            for (int c = 0; c < d; ++c) {
+                dq1[(int64_t)i * d + c] += scale * ds1 * k1[(int64_t)j * d + c];
+                dq2[(int64_t)i * d + c] += scale * ds2 * k2[(int64_t)j * d + c];
+                dk1[(int64_t)j * d + c] += scale * ds1 * q1i[c];
+                dk2[(int64_t)j * d + c] += scale * ds2 * q2i[c];
+            }
+            double w = a1[j] - lam * a2[j];
+            for (int c = 0; c < dv; ++c) dvv[(int64_t)j * dv + c] += w * gi[c];
+        }
+    }
+    free(a1); free(a2); free(da);
+    return err;
+}
+
 /* Number of OpenMP threads the head loop will use. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
