@@ -35,7 +35,8 @@ EPI_RMSNORM_SCALE = 1
 # Every symbol the header declares (tests check the library exports all of them).
 EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "diffattn_lambda",
             "diffattn_fwd", "diffattn_decode_workspace_size", "diffattn_decode", "diffattn_v2_fwd",
-            "diffattn_v2_decode_workspace_size", "diffattn_v2_decode")
+            "diffattn_v2_decode_workspace_size", "diffattn_v2_decode", "diffattn_fwd_train",
+            "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd")
 
 
 class DiffAttnError(RuntimeError):
@@ -78,6 +79,15 @@ def lib():
                                       sz, vp]
         L.diffattn_v2_fwd.restype = i
         L.diffattn_v2_fwd.argtypes = [i, T, T, T, vp, i, i, i, i, i, i, f, T, vp]
+        L.diffattn_fwd_train.restype = i
+        L.diffattn_fwd_train.argtypes = [i, T, T, T, T, T, i, i, i, i, i, i, vp, f, i, i, vp, f, f, T, vp, vp, vp]
+        L.diffattn_bwd_workspace_size.restype = sz
+        L.diffattn_bwd_workspace_size.argtypes = [i, i, i]
+        L.diffattn_bwd.restype = i
+        L.diffattn_bwd.argtypes = [i, T, T, T, T, T, T, i, i, i, i, i, i, vp, f, i, i, vp, f, f, vp, vp,
+                                   T, T, T, T, T, vp, vp, vp, sz, vp]
+        L.diffattn_lambda_bwd.restype = i
+        L.diffattn_lambda_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, vp, vp, vp, vp, vp]
         L.diffattn_v2_decode_workspace_size.restype = sz
         L.diffattn_v2_decode_workspace_size.argtypes = [i, i, i, i]
         L.diffattn_v2_decode.restype = i
@@ -199,6 +209,63 @@ def diffattn_v2_fwd(q, k, v, lam: torch.Tensor, causal: bool = True, scale: floa
     _check(lib().diffattn_v2_fwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), lam.data_ptr(), B, N, h, hkv,
                                  d, int(bool(causal)), float(scale), _t4(out), _stream(q.device)))
     return out
+
+
+def diffattn_fwd_train(q1, q2, k1, k2, v, lam: torch.Tensor, causal: bool = True, epilogue: bool = True,
+                       lambda_init_value: float = 0.8, norm_w: torch.Tensor | None = None, eps: float = 1e-5,
+                       scale: float = 0.0, out: torch.Tensor | None = None):
+    """DIFF V1 training forward. Returns (out, lse [B, H, Nq, 2] fp32, maps [B, Nq, H, 2, dv] fp32)."""
+    B, Nq, H, d = q1.shape
+    Nk, dv = k1.shape[1], v.shape[3]
+    if out is None:
+        out = torch.empty((B, Nq, H, dv), dtype=q1.dtype, device=q1.device)
+    lse = torch.empty((B, H, Nq, 2), dtype=torch.float32, device=q1.device)
+    maps = torch.empty((B, Nq, H, 2, dv), dtype=torch.float32, device=q1.device)
+    _check(lib().diffattn_fwd_train(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1), _t4(k2), _t4(v), B, H, Nq, Nk, d,
+                                    dv, lam.data_ptr(), float(lambda_init_value), int(bool(causal)),
+                                    EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
+                                    float(scale), _t4(out), lse.data_ptr(), maps.data_ptr(), _stream(q1.device)))
+    return out, lse, maps
+
+
+def diffattn_bwd_workspace_size(batch: int, heads: int, seq_q: int) -> int:
+    return int(lib().diffattn_bwd_workspace_size(batch, heads, seq_q))
+
+
+def diffattn_bwd(q1, q2, k1, k2, v, dout, lam: torch.Tensor, lse: torch.Tensor, maps: torch.Tensor,
+                 causal: bool = True, epilogue: bool = True, lambda_init_value: float = 0.8,
+                 norm_w: torch.Tensor | None = None, eps: float = 1e-5, scale: float = 0.0,
+                 workspace: torch.Tensor | None = None) -> dict:
+    """DIFF V1 backward for L = sum(dout * out). Returns dq1, dq2, dk1, dk2, dv (like the inputs),
+    dlam [H] fp32 and dnorm_w [dv] fp32 (None without the epilogue)."""
+    B, Nq, H, d = q1.shape
+    Nk, dv = k1.shape[1], v.shape[3]
+    g = {k: torch.empty_like(x) for k, x in (("dq1", q1), ("dq2", q2), ("dk1", k1), ("dk2", k2), ("dv", v))}
+    dlam = torch.empty((H,), dtype=torch.float32, device=q1.device)
+    dnw = torch.empty((dv,), dtype=torch.float32, device=q1.device) if epilogue else None
+    need = diffattn_bwd_workspace_size(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q1.device)
+    _check(lib().diffattn_bwd(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1), _t4(k2), _t4(v), _t4(dout), B, H, Nq,
+                              Nk, d, dv, lam.data_ptr(), float(lambda_init_value), int(bool(causal)),
+                              EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps), float(scale),
+                              lse.data_ptr(), maps.data_ptr(), _t4(g["dq1"]), _t4(g["dq2"]), _t4(g["dk1"]),
+                              _t4(g["dk2"]), _t4(g["dv"]), dlam.data_ptr(), _ptr(dnw), workspace.data_ptr(),
+                              workspace.numel(), _stream(q1.device)))
+    g["dlam"] = dlam
+    g["dnorm_w"] = dnw
+    return g
+
+
+def diffattn_lambda_bwd(lq1, lk1, lq2, lk2, dlam) -> dict:
+    """Gradients of the lambda re-parameterisation; vectors fp32 [n, dim] (or [dim]) on the device."""
+    vecs = [x.reshape(-1, x.shape[-1]).contiguous() for x in (lq1, lk1, lq2, lk2)]
+    n, dim = vecs[0].shape
+    outs = [torch.empty_like(x) for x in vecs]
+    dl = dlam.reshape(-1).contiguous()
+    _check(lib().diffattn_lambda_bwd(*(x.data_ptr() for x in vecs), dl.data_ptr(), n, dim,
+                                     *(x.data_ptr() for x in outs), _stream(vecs[0].device)))
+    return dict(dlq1=outs[0], dlk1=outs[1], dlq2=outs[2], dlk2=outs[3])
 
 
 def diffattn_v2_decode_workspace_size(batch: int, h: int, h_kv: int, cache_len: int) -> int:

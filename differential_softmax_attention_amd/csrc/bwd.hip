@@ -1,0 +1,513 @@
+// DIFF V1 backward on bf16 MFMA (gfx950): d = 64 per map, dv = 128, optional RMSNorm epilogue.
+//
+// Gradients of y = (1 - lambda_init) w * o / rms(o), o = A1 V - lambda A2 V, A_k = softmax(s Q_k K_k^T)
+// ("Differential Transformer: Noise-Canceling Attention by Subtraction", sections "The mechanism"
+// and "Making lambda learnable and stable"), by the chain rule:
+//   RMSNorm:  u = o / r, du = (1 - lambda_init) w * dy,  go = dL/do = (du - u mean(du u)) / r,
+//             dL/dw = sum over rows of dy (1 - lambda_init) u
+//   maps:     dP = go V^T (shared by both maps), D_k = go . (A_k V) per row,
+//             dS1 = A1 (dP - D1),  dS2 = -lambda A2 (dP - D2),
+//             dQ_k = s dS_k K_k,  dK_k = s dS_k^T Q_k,  dV = (A1 - lambda A2)^T go,
+//             dlambda = -sum over rows of D2.
+// The forward's training outputs supply each map's log-sum-exp (so A_k is recomputed exactly
+// from the scores) and A_k V (for D_k and o).
+//
+// Kernels (no atomics; every sum is taken in a fixed order):
+//  - bwd_pre: one wave per row: o, go (stored bf16 as an MFMA operand), D1, D2, and per-block
+//    partial sums of dL/dw and dlambda.
+//  - bwd_dq: query-tile parallel like the forward (S^T = K Q^T, lane = query): K1, K2, V tiles of
+//    32 keys staged through LDS; dP^T = V go^T; dQ_k^T += K_k^T dS_k^T with K^T read by the
+//    transposing LDS read.
+//  - bwd_dkdv: key-tile parallel (S = Q K^T, lane = key): each wave keeps its 32 keys' K1, K2, V in
+//    LDS and walks the query tiles; dV^T += go^T (A1 - lambda A2) and dK_k^T += Q_k^T dS_k with the
+//    transposed operands again read by ds_read_b64_tr_b16.
+//  - bwd_reduce: dlambda per head and dL/dw per channel from the partials.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_tile.hpp"
+
+namespace diffattn {
+
+namespace {
+
+constexpr int kBN = 32;
+constexpr int kD = 64;
+constexpr int kDV = 128;
+constexpr int kKTile = kBN * kD * 2;    // bytes of one 32-row, 64-wide tile (K-layout)
+constexpr int kVTile = kBN * kDV * 2;   // bytes of one 32-row, 128-wide tile (V-layout)
+constexpr int kPreRows = 16;            // rows per bwd_pre block (4 waves x 4 rows)
+
+// ---- LDS operand addressing (tiles as in the forward: K-layout 64 wide, V-layout 128 wide)
+// Row operand: row `row`, 16-byte logical chunk 2kk + h2 (MFMA A rows or B columns).
+__device__ __forceinline__ int rowop_k(int row, int kk, int h2) { return row * (kD * 2) + (((2 * kk + h2) ^ k_swz<kD>(row)) * 16); }
+__device__ __forceinline__ int rowop_v(int row, int kk, int h2) { return row * (kDV * 2) + v_phys(row, 2 * kk + h2) * 16; }
+// Transposing read (A operand X^T of a row-major tile X whose rows are the MFMA k index): 16-lane
+// group G covers columns 32 mt + 16 (G & 1) .. +15 and rows 16 kb + 4 (G >> 1) + 0..3 (lo) and
+// +8 (hi); lane L supplies row + L/4 and columns + 4 (L % 4) .. +3.
+__device__ __forceinline__ int trop_k(int lane, int kb, int mt, int hi) {
+    const int G = lane >> 4, L = lane & 15;
+    const int row = 16 * kb + 4 * (G >> 1) + (L >> 2) + 8 * hi;
+    const int c = mt * 4 + (G & 1) * 2 + ((L >> 1) & 1);
+    return row * (kD * 2) + ((c ^ k_swz<kD>(row)) * 16) + (L & 1) * 8;
+}
+__device__ __forceinline__ int trop_v(int lane, int kb, int ct, int hi) {
+    const int G = lane >> 4, L = lane & 15;
+    const int row = 16 * kb + 4 * (G >> 1) + (L >> 2) + 8 * hi;
+    const int c = ct * 4 + (G & 1) * 2 + ((L >> 1) & 1);
+    return row * (kDV * 2) + v_phys(row, c) * 16 + (L & 1) * 8;
+}
+__device__ __forceinline__ bf16x8 tr_pair(const unsigned char* base, int lo, int hi) {
+    const i16x4 a = lds_read_tr16((const bf16*)(base + lo));
+    const i16x4 b = lds_read_tr16((const bf16*)(base + hi));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// C registers kb*8 .. kb*8+7 of a 32x32 tile as the bf16 B operand of the next MFMA whose k index
+// is the tile's row index (the k order matches the transposing read)
+__device__ __forceinline__ bf16x8 c_to_b(const f32x16& x, int kb) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (bf16)x[kb * 8 + j];
+    return r;
+}
+
+// Copy a 32-row tile from global (row stride rs elements) into LDS in the K- (W = 64) or
+// V-layout (W = 128), rows past `nrows` zeroed. All nt threads of the block take part.
+template <int W>
+__device__ __forceinline__ void stage_tile(unsigned char* dst, const bf16* src, int64_t rs, int nrows, int tid, int nt) {
+    constexpr int CPR = W / 8;   // chunks per row
+    for (int s = tid; s < kBN * CPR; s += nt) {
+        const int row = s / CPR, c = s % CPR;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < nrows) x = *(const u32x4*)(src + (int64_t)row * rs + c * 8);
+        const int phys = W == kD ? (c ^ k_swz<kD>(row)) : v_phys(row, c);
+        *(u32x4*)(dst + row * (W * 2) + phys * 16) = x;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const float lam = a.lam[h];
+    const float kappa = 1.f - a.lambda_init;
+    float w0 = 1.f, w1 = 1.f;
+    if (a.epi && a.norm_w) { w0 = a.norm_w[lane]; w1 = a.norm_w[lane + 64]; }
+    float gw0 = 0.f, gw1 = 0.f, glam = 0.f;   // this wave's partial dL/dw (2 channels) and dlambda
+    for (int k = 0; k < kPreRows / 4; ++k) {
+        const int i = blk * kPreRows + wave * (kPreRows / 4) + k;
+        if (i >= a.seq_q) break;
+        const int64_t row = ((int64_t)b * a.heads + h) * a.seq_q + i;
+        const float* mp = a.maps + (((int64_t)b * a.seq_q + i) * a.heads + h) * 2 * kDV;
+        const float a1x = mp[lane], a1y = mp[lane + 64];
+        const float a2x = mp[kDV + lane], a2y = mp[kDV + lane + 64];
+        const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)i * a.dos[1] + (int64_t)h * a.dos[2];
+        const float dy0 = (float)dyp[lane], dy1 = (float)dyp[lane + 64];
+        float g0 = dy0, g1 = dy1;
+        if (a.epi) {
+            float o0, o1;
+            {
+#pragma clang fp contract(off)
+                o0 = a1x - lam * a2x;
+                o1 = a1y - lam * a2y;
+            }
+            const float ms = wave_sum(o0 * o0 + o1 * o1) * (1.f / kDV);
+            const float inv = 1.f / sqrtf(ms + a.eps);
+            const float u0 = o0 * inv, u1 = o1 * inv;
+            const float du0 = kappa * w0 * dy0, du1 = kappa * w1 * dy1;
+            const float t = wave_sum(du0 * u0 + du1 * u1) * (1.f / kDV);
+            g0 = (du0 - u0 * t) * inv;
+            g1 = (du1 - u1 * t) * inv;
+            gw0 += dy0 * kappa * u0;
+            gw1 += dy1 * kappa * u1;
+        }
+        // dlambda takes go in fp32; go enters the MFMA kernels rounded to bf16, and D_k takes the
+        // same rounded values, so that each row of dS_k sums to zero as the softmax Jacobian's do
+        glam -= wave_sum(g0 * a2x + g1 * a2y);
+        const bf16 gb0 = (bf16)g0, gb1 = (bf16)g1;
+        g0 = (float)gb0;
+        g1 = (float)gb1;
+        const float D1 = wave_sum(g0 * a1x + g1 * a1y);
+        const float D2 = wave_sum(g0 * a2x + g1 * a2y);
+        bf16* gp = a.go + row * kDV;
+        gp[lane] = gb0;
+        gp[lane + 64] = gb1;
+        if (lane == 0) {
+            a.dd[2 * row] = D1;
+            a.dd[2 * row + 1] = D2;
+        }
+    }
+    // block partials in a fixed order: waves 0..3
+    __shared__ float sw[4][kDV];
+    __shared__ float sl[4];
+    sw[wave][lane] = gw0;
+    sw[wave][lane + 64] = gw1;
+    if (lane == 0) sl[wave] = glam;
+    __syncthreads();
+    const int64_t pb = ((int64_t)b * a.heads + h) * gridDim.x + blk;   // partial index
+    if (tid < kDV && a.epi) {
+        const float s = ((sw[0][tid] + sw[1][tid]) + sw[2][tid]) + sw[3][tid];
+        a.wpart[(int64_t)tid * a.n_part + pb] = s;
+    }
+    if (tid == 0) a.lampart[pb] = ((sl[0] + sl[1]) + sl[2]) + sl[3];
+}
+
+// dlambda[h] = sum of the partials of head h; dL/dw[c] = sum of channel c's partials
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+    const int j = blockIdx.x, tid = threadIdx.x;
+    __shared__ float red[256];
+    float s = 0.f;
+    if (j < a.heads) {
+        // partial index = (b * heads + h) * pre_blocks + blk
+        for (int k = tid; k < a.batch * a.pre_blocks; k += 256) {
+            const int bb = k / a.pre_blocks, blk = k % a.pre_blocks;
+            s += a.lampart[((int64_t)bb * a.heads + j) * a.pre_blocks + blk];
+        }
+    } else {
+        const int c = j - a.heads;
+        for (int k = tid; k < a.n_part; k += 256) s += a.wpart[(int64_t)c * a.n_part + k];
+    }
+    red[tid] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        if (j < a.heads) {
+            if (a.dlam) a.dlam[j] = red[0];
+        } else {
+            a.dnorm_w[j - a.heads] = red[0];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dQ: a block of 4 waves owns 128 queries of one head, 32 per wave, and walks the key tiles.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
+    __shared__ __align__(16) unsigned char smem[1][2 * kKTile + kVTile];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, h2 = lane >> 5;
+    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int q0 = qt * 128, qw0 = q0 + wave * 32, qrow = qw0 + n;
+    const int off = a.seq_k - a.seq_q;
+    const bool qok = qrow < a.seq_q;
+    const int qr = qok ? qrow : 0;
+    const int64_t row = ((int64_t)b * a.heads + h) * a.seq_q + qr;
+
+    // per-lane query operands (B operands, lane = query n): Q1, Q2 (for S^T) and go (for dP^T)
+    bf16x8 bq1[4], bq2[4], bg[8];
+    {
+        const bf16* q1p = (const bf16*)a.q1 + b * a.q1s[0] + (int64_t)qr * a.q1s[1] + (int64_t)h * a.q1s[2] + 8 * h2;
+        const bf16* q2p = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)qr * a.q2s[1] + (int64_t)h * a.q2s[2] + 8 * h2;
+        const bf16* gp = a.go + row * kDV + 8 * h2;
+        const bf16x8 z = {};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bq1[kk] = qok ? ld_global_bf16x8(q1p + 16 * kk) : z;
+            bq2[kk] = qok ? ld_global_bf16x8(q2p + 16 * kk) : z;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) bg[kk] = qok ? ld_global_bf16x8(gp + 16 * kk) : z;
+    }
+    const float lse1 = qok ? a.lse[2 * row] : 0.f, lse2 = qok ? a.lse[2 * row + 1] : 0.f;
+    const float D1 = qok ? a.dd[2 * row] : 0.f, D2 = qok ? a.dd[2 * row + 1] : 0.f;
+    const float lam = a.lam[h];
+    const float c = a.scale_log2;
+
+    int nkt = (a.seq_k + kBN - 1) / kBN;
+    if (a.causal) nkt = min(nkt, (min(q0 + 127, a.seq_q - 1) + off) / kBN + 1);
+    const bool wave_active = qw0 < a.seq_q;
+    const int wave_qlast = min(qw0 + 31, a.seq_q - 1);
+
+    const bf16* k1b = (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)h * a.k1s[2];
+    const bf16* k2b = (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)h * a.k2s[2];
+    const bf16* vb = (const bf16*)a.v + b * a.vs[0] + (int64_t)h * a.vs[2];
+
+    f32x16 dq1[2], dq2[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) { dq1[mt] = f32x16{}; dq2[mt] = f32x16{}; }
+
+    auto stage = [&](int kt, int st) {
+        const int nrows = min(kBN, a.seq_k - kt * kBN);
+        stage_tile<kD>(smem[st], k1b + (int64_t)kt * kBN * a.k1s[1], a.k1s[1], nrows, tid, 256);
+        stage_tile<kD>(smem[st] + kKTile, k2b + (int64_t)kt * kBN * a.k2s[1], a.k2s[1], nrows, tid, 256);
+        stage_tile<kDV>(smem[st] + 2 * kKTile, vb + (int64_t)kt * kBN * a.vs[1], a.vs[1], nrows, tid, 256);
+    };
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int st = 0;   // one stage: the block syncs before and after each tile
+        stage(kt, st);
+        __syncthreads();
+        const int k0 = kt * kBN;
+        if (wave_active && (!a.causal || k0 <= wave_qlast + off)) {
+            const unsigned char* K1s = smem[st];
+            const unsigned char* K2s = smem[st] + kKTile;
+            const unsigned char* Vs = smem[st] + 2 * kKTile;
+            // S^T = K Q^T (lane = query n, 16 keys), dP^T = V go^T
+            f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                s1 = mfma32x32x16(lds16(K1s + rowop_k(n, kk, h2)), bq1[kk], s1);
+                s2 = mfma32x32x16(lds16(K2s + rowop_k(n, kk, h2)), bq2[kk], s2);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Vs + rowop_v(n, kk, h2)), bg[kk], dp);
+            const int qlim = a.causal ? min(qrow + off, a.seq_k - 1) : a.seq_k - 1;
+            f32x16 ds1, ds2;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + (r >> 2) * 8 + h2 * 4 + (r & 3);
+                const bool vis = qok && key <= qlim;
+                const float p1 = vis ? fast_exp2(fmaf(s1[r], c, -lse1)) : 0.f;
+                const float p2 = vis ? fast_exp2(fmaf(s2[r], c, -lse2)) : 0.f;
+                ds1[r] = p1 * (dp[r] - D1);
+                ds2[r] = -lam * p2 * (dp[r] - D2);
+            }
+            // dQ_k^T += K_k^T dS_k^T (k index = keys)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 b1 = c_to_b(ds1, kb), b2 = c_to_b(ds2, kb);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    dq1[mt] = mfma32x32x16(tr_pair(K1s, trop_k(lane, kb, mt, 0), trop_k(lane, kb, mt, 1)), b1, dq1[mt]);
+                    dq2[mt] = mfma32x32x16(tr_pair(K2s, trop_k(lane, kb, mt, 0), trop_k(lane, kb, mt, 1)), b2, dq2[mt]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (!qok) return;
+    // dQ_k = s dS_k K_k; lane (n, h2) holds d = 32 mt + (r / 4) * 8 + 4 h2 + r % 4 of query n
+    bf16* o1p = (bf16*)a.dq1 + b * a.dq1s[0] + (int64_t)qrow * a.dq1s[1] + (int64_t)h * a.dq1s[2];
+    bf16* o2p = (bf16*)a.dq2 + b * a.dq2s[0] + (int64_t)qrow * a.dq2s[1] + (int64_t)h * a.dq2s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 x1, x2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x1[j] = (bf16)(dq1[mt][g * 4 + j] * a.scale);
+                x2[j] = (bf16)(dq2[mt][g * 4 + j] * a.scale);
+            }
+            *(bf16x4*)(o1p + mt * 32 + g * 8 + h2 * 4) = x1;
+            *(bf16x4*)(o2p + mt * 32 + g * 8 + h2 * 4) = x2;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dK, dV: a block of 4 waves owns 128 keys of one head, 32 per wave, and walks the query tiles.
+// (82 KB of LDS allow one block per CU, so the waves may use the whole register file)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs a) {
+    // the wave's own K1 | K2 | V (read as B operands every step) and the shared query tile
+    __shared__ __align__(16) unsigned char skv[4][2 * kKTile + kVTile];
+    __shared__ __align__(16) unsigned char sq[2 * kKTile + kVTile];
+    __shared__ __align__(16) float sv[4][kBN];   // lse1, lse2, D1, D2 of the query tile
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, h2 = lane >> 5;
+    const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int k0 = kt * 128, kw0 = k0 + wave * 32, key = kw0 + n;
+    const int off = a.seq_k - a.seq_q;
+    const float lam = a.lam[h];
+    const float c = a.scale_log2;
+
+    {
+        const int nrows = max(0, min(kBN, a.seq_k - kw0));
+        const int64_t t = tid & 63;
+        stage_tile<kD>(skv[wave], (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)h * a.k1s[2] + (int64_t)kw0 * a.k1s[1],
+                       a.k1s[1], nrows, (int)t, 64);
+        stage_tile<kD>(skv[wave] + kKTile, (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)h * a.k2s[2] + (int64_t)kw0 * a.k2s[1],
+                       a.k2s[1], nrows, (int)t, 64);
+        stage_tile<kDV>(skv[wave] + 2 * kKTile, (const bf16*)a.v + b * a.vs[0] + (int64_t)h * a.vs[2] + (int64_t)kw0 * a.vs[1],
+                        a.vs[1], nrows, (int)t, 64);
+    }
+    const unsigned char* K1s = skv[wave];
+    const unsigned char* K2s = skv[wave] + kKTile;
+    const unsigned char* Vs = skv[wave] + 2 * kKTile;
+
+    f32x16 dk1[2], dk2[2], dv[4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) { dk1[mt] = f32x16{}; dk2[mt] = f32x16{}; }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) dv[ct] = f32x16{};
+
+    // query tiles that see any of the block's keys
+    const int nqt = (a.seq_q + kBN - 1) / kBN;
+    int qt0 = 0;
+    if (a.causal) qt0 = max(0, (k0 - off) / kBN);
+    const bool wave_active = kw0 < a.seq_k;
+    const bf16* q1b = (const bf16*)a.q1 + b * a.q1s[0] + (int64_t)h * a.q1s[2];
+    const bf16* q2b = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)h * a.q2s[2];
+    const int64_t rowb = ((int64_t)b * a.heads + h) * a.seq_q;
+
+    for (int qt = qt0; qt < nqt; ++qt) {
+        const int i0 = qt * kBN;
+        const int nrows = min(kBN, a.seq_q - i0);
+        __syncthreads();   // the previous tile is no longer read
+        stage_tile<kD>(sq, q1b + (int64_t)i0 * a.q1s[1], a.q1s[1], nrows, tid, 256);
+        stage_tile<kD>(sq + kKTile, q2b + (int64_t)i0 * a.q2s[1], a.q2s[1], nrows, tid, 256);
+        stage_tile<kDV>(sq + 2 * kKTile, a.go + (rowb + i0) * kDV, kDV, nrows, tid, 256);
+        if (tid < kBN) {
+            const bool ok = tid < nrows;
+            const int64_t r = rowb + i0 + tid;
+            sv[0][tid] = ok ? a.lse[2 * r] : 0.f;
+            sv[1][tid] = ok ? a.lse[2 * r + 1] : 0.f;
+            sv[2][tid] = ok ? a.dd[2 * r] : 0.f;
+            sv[3][tid] = ok ? a.dd[2 * r + 1] : 0.f;
+        }
+        __syncthreads();
+        // skip the tile if it ends before this wave's first key (causal)
+        if (!wave_active || (a.causal && i0 + kBN - 1 + off < kw0)) continue;
+        const unsigned char* Q1s = sq;
+        const unsigned char* Q2s = sq + kKTile;
+        const unsigned char* Gs = sq + 2 * kKTile;
+        // dP = go V^T (rows = queries, lane = key n)
+        f32x16 dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Gs + rowop_v(n, kk, h2)), lds16(Vs + rowop_v(n, kk, h2)), dp);
+        // per-register query index: 8 (r / 4) + 4 h2 + r % 4
+        f32x16 pc = f32x16{};
+#pragma unroll
+        for (int map = 0; map < 2; ++map) {
+            const unsigned char* Qs = map == 0 ? Q1s : Q2s;
+            const unsigned char* Ks = map == 0 ? K1s : K2s;
+            f32x16 s = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) s = mfma32x32x16(lds16(Qs + rowop_k(n, kk, h2)), lds16(Ks + rowop_k(n, kk, h2)), s);
+            const float coef = map == 0 ? 1.f : -lam;
+            f32x16 ds;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 lse = *(const f32x4*)&sv[map][8 * g + 4 * h2];
+                const f32x4 dd = *(const f32x4*)&sv[2 + map][8 * g + 4 * h2];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * g + j;
+                    const int q = i0 + 8 * g + 4 * h2 + j;
+                    const bool vis = q < a.seq_q && key < a.seq_k && (!a.causal || key <= q + off);
+                    const float p = vis ? fast_exp2(fmaf(s[r], c, -lse[j])) : 0.f;
+                    ds[r] = coef * p * (dp[r] - dd[j]);
+                    pc[r] = fmaf(coef, p, pc[r]);
+                }
+            }
+            // dK_k^T += Q_k^T dS_k (k index = queries)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 bds = c_to_b(ds, kb);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const bf16x8 qa = tr_pair(Qs, trop_k(lane, kb, mt, 0), trop_k(lane, kb, mt, 1));
+                    if (map == 0) dk1[mt] = mfma32x32x16(qa, bds, dk1[mt]);
+                    else dk2[mt] = mfma32x32x16(qa, bds, dk2[mt]);
+                }
+            }
+        }
+        // dV^T += go^T (A1 - lambda A2)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 bp = c_to_b(pc, kb);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                dv[ct] = mfma32x32x16(tr_pair(Gs, trop_v(lane, kb, ct, 0), trop_v(lane, kb, ct, 1)), bp, dv[ct]);
+        }
+    }
+    if (key >= a.seq_k) return;
+    bf16* k1p = (bf16*)a.dk1 + b * a.dk1s[0] + (int64_t)key * a.dk1s[1] + (int64_t)h * a.dk1s[2];
+    bf16* k2p = (bf16*)a.dk2 + b * a.dk2s[0] + (int64_t)key * a.dk2s[1] + (int64_t)h * a.dk2s[2];
+    bf16* vp = (bf16*)a.dv + b * a.dvs[0] + (int64_t)key * a.dvs[1] + (int64_t)h * a.dvs[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            bf16x4 x1, x2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x1[j] = (bf16)(dk1[mt][g * 4 + j] * a.scale);
+                x2[j] = (bf16)(dk2[mt][g * 4 + j] * a.scale);
+            }
+            *(bf16x4*)(k1p + mt * 32 + g * 8 + h2 * 4) = x1;
+            *(bf16x4*)(k2p + mt * 32 + g * 8 + h2 * 4) = x2;
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            bf16x4 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = (bf16)dv[ct][g * 4 + j];
+            *(bf16x4*)(vp + ct * 32 + g * 8 + h2 * 4) = x;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init: gradients of the four vectors, one wave
+// per row.
+__global__ __launch_bounds__(64) void lambda_bwd_kernel(const float* lq1, const float* lk1, const float* lq2,
+                                                        const float* lk2, const float* dlam, int dim, float* dlq1,
+                                                        float* dlk1, float* dlq2, float* dlk2) {
+    const int r = blockIdx.x, lane = threadIdx.x;
+    const int64_t o = (int64_t)r * dim;
+    float s1 = 0.f, s2 = 0.f;
+    for (int j = lane; j < dim; j += 64) {
+        s1 = fmaf(lq1[o + j], lk1[o + j], s1);
+        s2 = fmaf(lq2[o + j], lk2[o + j], s2);
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    const float e1 = dlam[r] * expf(s1), e2 = dlam[r] * expf(s2);
+    for (int j = lane; j < dim; j += 64) {
+        dlq1[o + j] = e1 * lk1[o + j];
+        dlk1[o + j] = e1 * lq1[o + j];
+        dlq2[o + j] = -e2 * lk2[o + j];
+        dlk2[o + j] = -e2 * lq2[o + j];
+    }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int batch, int heads, int seq_q) {
+    const size_t rows = (size_t)batch * heads * seq_q;
+    const size_t n_part = (size_t)batch * heads * ((seq_q + kPreRows - 1) / kPreRows);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return up(rows * kDV * 2) + up(rows * 2 * sizeof(float)) + up(n_part * kDV * sizeof(float)) +
+           up(n_part * sizeof(float));
+}
+
+hipError_t launch_bwd(BwdArgs a, void* workspace, hipStream_t stream) {
+    const size_t rows = (size_t)a.batch * a.heads * a.seq_q;
+    const int pre_blocks = (a.seq_q + kPreRows - 1) / kPreRows;
+    a.pre_blocks = pre_blocks;
+    a.n_part = a.batch * a.heads * pre_blocks;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    unsigned char* w = (unsigned char*)workspace;
+    a.go = (bf16*)w;
+    w += up(rows * kDV * 2);
+    a.dd = (float*)w;
+    w += up(rows * 2 * sizeof(float));
+    a.wpart = (float*)w;
+    w += up((size_t)a.n_part * kDV * sizeof(float));
+    a.lampart = (float*)w;
+
+    hipLaunchKernelGGL(bwd_pre_kernel, dim3(pre_blocks, a.heads, a.batch), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((a.seq_q + 127) / 128, a.heads, a.batch), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((a.seq_k + 127) / 128, a.heads, a.batch), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int nred = a.heads + ((a.epi && a.dnorm_w) ? kDV : 0);
+    if (a.dlam || a.dnorm_w) {
+        hipLaunchKernelGGL(bwd_reduce_kernel, dim3(nred), dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_lambda_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
+                             const float* dlam, int n, int dim, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(lambda_bwd_kernel, dim3(n), dim3(64), 0, stream, lq1, lk1, lq2, lk2, dlam, dim, dlq1, dlk1,
+                       dlq2, dlk2);
+    return hipGetLastError();
+}
+
+}  // namespace diffattn

@@ -59,6 +59,69 @@ float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / st
 
 }  // namespace
 
+static diffattn_status fwd_impl(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,
+                                diffattn_tensor k2, diffattn_tensor v, int batch, int heads, int seq_q, int seq_k,
+                                int d, int dv, const float* lambda, float lambda_init, int causal,
+                                diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                                diffattn_tensor out, float* lse, float* maps, void* stream, const char* fn) {
+    if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    const diffattn_tensor* ts[6] = {&q1, &q2, &k1, &k2, &v, &out};
+    const char* names[6] = {"q1", "q2", "k1", "k2", "v", "out"};
+    for (int i = 0; i < 6; ++i)
+        if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
+    if (!lambda) return fail(DIFFATTN_ERR_ARG, "%s: lambda is null", fn);
+    if (batch < 1 || heads < 1 || seq_q < 1 || seq_k < 1 || d < 1 || dv < 1)
+        return fail(DIFFATTN_ERR_ARG, "%s: sizes must be >= 1 (batch=%d heads=%d seq_q=%d seq_k=%d d=%d dv=%d)", fn,
+                    batch, heads, seq_q, seq_k, d, dv);
+    if (heads > 65535 || batch > 65535) return fail(DIFFATTN_ERR_ARG, "%s: batch and heads must be <= 65535", fn);
+    if (causal && seq_q > seq_k)
+        return fail(DIFFATTN_ERR_ARG, "%s: causal needs seq_q (%d) <= seq_k (%d)", fn, seq_q, seq_k);
+    if (epi != DIFFATTN_EPI_NONE && epi != DIFFATTN_EPI_RMSNORM_SCALE)
+        return fail(DIFFATTN_ERR_ARG, "%s: unknown epilogue %d", fn, (int)epi);
+    if (epi == DIFFATTN_EPI_RMSNORM_SCALE && !(std::isfinite(eps) && eps >= 0.f && std::isfinite(lambda_init)))
+        return fail(DIFFATTN_ERR_ARG, "%s: eps must be finite and >= 0, lambda_init finite", fn);
+    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "%s: scale must be finite", fn);
+    if (d > 256 || dv > 512)
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "%s: d=%d dv=%d exceed the supported d <= 256, dv <= 512", fn, d, dv);
+    const float sc = resolve_scale(scale, d);
+    hipStream_t st = (hipStream_t)stream;
+
+    const bool mfma = dtype == DIFFATTN_BF16 && d == 64 && dv == 128 && vec16_ok(q1) && vec16_ok(q2) &&
+                      vec16_ok(k1) && vec16_ok(k2) && vec16_ok(v) && vec16_ok(out);
+    if (mfma) {
+        diffattn::MfmaFwdArgs a{};
+        a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.out = out.ptr;
+        copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1); copy_strides(a.k2s, k2);
+        copy_strides(a.vs, v); copy_strides(a.os, out);
+        a.lam = lambda;
+        a.lams[0] = 0; a.lams[1] = 0; a.lams[2] = 1;
+        a.norm_w = norm_w;
+        a.batch = batch; a.heads = heads; a.seq_q = seq_q; a.seq_k = seq_k;
+        a.kv_group = 1;
+        a.causal = causal ? 1 : 0;
+        a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
+        a.eps = eps; a.lambda_init = lambda_init;
+        a.scale_log2 = sc * 1.4426950408889634f;
+        a.lse = lse;
+        a.maps = maps;
+        return hip_status(diffattn::launch_v1_fwd_mfma(a, st), fn);
+    }
+    diffattn::GenericArgs a{};
+    a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.out = out.ptr;
+    copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1); copy_strides(a.k2s, k2);
+    copy_strides(a.vs, v); copy_strides(a.os, out);
+    a.q_hmul = 1; a.q1_hoff = 0; a.q2_hoff = 0; a.kv_hdiv = 1;
+    a.lam = lambda;
+    a.lams[0] = 0; a.lams[1] = 0; a.lams[2] = 1;
+    a.key_lens = nullptr;
+    a.seq_q = seq_q; a.seq_k = seq_k; a.d = d; a.dv = dv;
+    a.causal = causal ? 1 : 0;
+    a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
+    a.norm_w = norm_w; a.eps = eps; a.lambda_init = lambda_init; a.scale = sc;
+    return hip_status(diffattn::launch_generic(a, batch, heads, dtype == DIFFATTN_BF16, st), fn);
+}
+
+
 extern "C" {
 
 const char* diffattn_last_error(void) { return g_last_error.c_str(); }
@@ -85,59 +148,8 @@ diffattn_status diffattn_fwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_
                              int d, int dv, const float* lambda, float lambda_init, int causal,
                              diffattn_epilogue epi, const float* norm_w, float eps, float scale,
                              diffattn_tensor out, void* stream) {
-    if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: unknown dtype %d", (int)dtype);
-    const diffattn_tensor* ts[6] = {&q1, &q2, &k1, &k2, &v, &out};
-    const char* names[6] = {"q1", "q2", "k1", "k2", "v", "out"};
-    for (int i = 0; i < 6; ++i)
-        if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
-    if (!lambda) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: lambda is null");
-    if (batch < 1 || heads < 1 || seq_q < 1 || seq_k < 1 || d < 1 || dv < 1)
-        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: sizes must be >= 1 (batch=%d heads=%d seq_q=%d seq_k=%d d=%d dv=%d)",
-                    batch, heads, seq_q, seq_k, d, dv);
-    if (heads > 65535 || batch > 65535) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: batch and heads must be <= 65535");
-    if (causal && seq_q > seq_k)
-        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: causal needs seq_q (%d) <= seq_k (%d)", seq_q, seq_k);
-    if (epi != DIFFATTN_EPI_NONE && epi != DIFFATTN_EPI_RMSNORM_SCALE)
-        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: unknown epilogue %d", (int)epi);
-    if (epi == DIFFATTN_EPI_RMSNORM_SCALE && !(std::isfinite(eps) && eps >= 0.f && std::isfinite(lambda_init)))
-        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: eps must be finite and >= 0, lambda_init finite");
-    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd: scale must be finite");
-    if (d > 256 || dv > 512)
-        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_fwd: d=%d dv=%d exceed the supported d <= 256, dv <= 512", d, dv);
-    const float sc = resolve_scale(scale, d);
-    hipStream_t st = (hipStream_t)stream;
-
-    const bool mfma = dtype == DIFFATTN_BF16 && d == 64 && dv == 128 && vec16_ok(q1) && vec16_ok(q2) &&
-                      vec16_ok(k1) && vec16_ok(k2) && vec16_ok(v) && vec16_ok(out);
-    if (mfma) {
-        diffattn::MfmaFwdArgs a{};
-        a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.out = out.ptr;
-        copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1); copy_strides(a.k2s, k2);
-        copy_strides(a.vs, v); copy_strides(a.os, out);
-        a.lam = lambda;
-        a.lams[0] = 0; a.lams[1] = 0; a.lams[2] = 1;
-        a.norm_w = norm_w;
-        a.batch = batch; a.heads = heads; a.seq_q = seq_q; a.seq_k = seq_k;
-        a.kv_group = 1;
-        a.causal = causal ? 1 : 0;
-        a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
-        a.eps = eps; a.lambda_init = lambda_init;
-        a.scale_log2 = sc * 1.4426950408889634f;
-        return hip_status(diffattn::launch_v1_fwd_mfma(a, st), "diffattn_fwd launch");
-    }
-    diffattn::GenericArgs a{};
-    a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.out = out.ptr;
-    copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1); copy_strides(a.k2s, k2);
-    copy_strides(a.vs, v); copy_strides(a.os, out);
-    a.q_hmul = 1; a.q1_hoff = 0; a.q2_hoff = 0; a.kv_hdiv = 1;
-    a.lam = lambda;
-    a.lams[0] = 0; a.lams[1] = 0; a.lams[2] = 1;
-    a.key_lens = nullptr;
-    a.seq_q = seq_q; a.seq_k = seq_k; a.d = d; a.dv = dv;
-    a.causal = causal ? 1 : 0;
-    a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
-    a.norm_w = norm_w; a.eps = eps; a.lambda_init = lambda_init; a.scale = sc;
-    return hip_status(diffattn::launch_generic(a, batch, heads, dtype == DIFFATTN_BF16, st), "diffattn_fwd launch");
+    return fwd_impl(dtype, q1, q2, k1, k2, v, batch, heads, seq_q, seq_k, d, dv, lambda, lambda_init, causal, epi,
+                    norm_w, eps, scale, out, nullptr, nullptr, stream, "diffattn_fwd");
 }
 
 size_t diffattn_decode_workspace_size(int batch, int heads, int cache_len, int dv) {
@@ -328,6 +340,96 @@ diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diff
     a.epi = 0;
     a.norm_w = nullptr; a.eps = 0.f; a.lambda_init = 0.f; a.scale = sc;
     return hip_status(diffattn::launch_generic(a, batch, h, dtype == DIFFATTN_BF16, st), "diffattn_v2_decode launch");
+}
+
+diffattn_status diffattn_fwd_train(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,
+                                   diffattn_tensor k2, diffattn_tensor v, int batch, int heads, int seq_q, int seq_k,
+                                   int d, int dv, const float* lambda, float lambda_init, int causal,
+                                   diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                                   diffattn_tensor out, float* lse, float* maps, void* stream) {
+    if (!lse || !maps) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_train: lse and maps must be non-null");
+    if (((uintptr_t)maps) % 16 != 0 || ((uintptr_t)lse) % 8 != 0)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_train: maps must be 16-byte and lse 8-byte aligned");
+    if (!(dtype == DIFFATTN_BF16 && d == 64 && dv == 128 && vec16_ok(q1) && vec16_ok(q2) && vec16_ok(k1) &&
+          vec16_ok(k2) && vec16_ok(v) && vec16_ok(out)))
+        return fail(DIFFATTN_ERR_UNSUPPORTED,
+                    "diffattn_fwd_train: the training forward serves bf16 with d = 64, dv = 128 and aligned strides");
+    return fwd_impl(dtype, q1, q2, k1, k2, v, batch, heads, seq_q, seq_k, d, dv, lambda, lambda_init, causal, epi,
+                    norm_w, eps, scale, out, lse, maps, stream, "diffattn_fwd_train");
+}
+
+size_t diffattn_bwd_workspace_size(int batch, int heads, int seq_q) {
+    if (batch < 1 || heads < 1 || seq_q < 1) return 0;
+    return diffattn::bwd_workspace_bytes(batch, heads, seq_q);
+}
+
+diffattn_status diffattn_bwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,
+                             diffattn_tensor k2, diffattn_tensor v, diffattn_tensor dout, int batch, int heads,
+                             int seq_q, int seq_k, int d, int dv, const float* lambda, float lambda_init, int causal,
+                             diffattn_epilogue epi, const float* norm_w, float eps, float scale, const float* lse,
+                             const float* maps, diffattn_tensor dq1, diffattn_tensor dq2, diffattn_tensor dk1,
+                             diffattn_tensor dk2, diffattn_tensor dv_out, float* dlambda, float* dnorm_w,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: unknown dtype %d", (int)dtype);
+    const diffattn_tensor* ts[11] = {&q1, &q2, &k1, &k2, &v, &dout, &dq1, &dq2, &dk1, &dk2, &dv_out};
+    const char* names[11] = {"q1", "q2", "k1", "k2", "v", "dout", "dq1", "dq2", "dk1", "dk2", "dv"};
+    for (int i = 0; i < 11; ++i)
+        if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
+    if (!lambda || !lse || !maps) return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: lambda, lse and maps must be non-null");
+    if (batch < 1 || heads < 1 || seq_q < 1 || seq_k < 1 || d < 1 || dv < 1)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: sizes must be >= 1 (batch=%d heads=%d seq_q=%d seq_k=%d d=%d dv=%d)",
+                    batch, heads, seq_q, seq_k, d, dv);
+    if (heads > 65535 || batch > 65535) return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: batch and heads must be <= 65535");
+    if (causal && seq_q > seq_k)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: causal needs seq_q (%d) <= seq_k (%d)", seq_q, seq_k);
+    if (epi != DIFFATTN_EPI_NONE && epi != DIFFATTN_EPI_RMSNORM_SCALE)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: unknown epilogue %d", (int)epi);
+    if (epi == DIFFATTN_EPI_RMSNORM_SCALE && !(std::isfinite(eps) && eps >= 0.f && std::isfinite(lambda_init)))
+        return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: eps must be finite and >= 0, lambda_init finite");
+    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: scale must be finite");
+    const size_t need = diffattn_bwd_workspace_size(batch, heads, seq_q);
+    if (workspace_bytes < need)
+        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_bwd: workspace of %zu bytes < required %zu", workspace_bytes, need);
+    if (!workspace || ((uintptr_t)workspace) % 256 != 0)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: workspace must be non-null and 256-byte aligned");
+    if (!(dtype == DIFFATTN_BF16 && d == 64 && dv == 128))
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_bwd: serves bf16 with d = 64, dv = 128");
+    for (int i = 0; i < 11; ++i)
+        if (!vec16_ok(*ts[i]))
+            return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_bwd: %s needs a 16-byte aligned base and strides that are "
+                        "multiples of 8 elements", names[i]);
+    diffattn::BwdArgs a{};
+    a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.dout = dout.ptr;
+    copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1); copy_strides(a.k2s, k2);
+    copy_strides(a.vs, v); copy_strides(a.dos, dout);
+    a.dq1 = dq1.ptr; a.dq2 = dq2.ptr; a.dk1 = dk1.ptr; a.dk2 = dk2.ptr; a.dv = dv_out.ptr;
+    copy_strides(a.dq1s, dq1); copy_strides(a.dq2s, dq2); copy_strides(a.dk1s, dk1); copy_strides(a.dk2s, dk2);
+    copy_strides(a.dvs, dv_out);
+    a.lam = lambda;
+    a.norm_w = norm_w;
+    a.lse = lse;
+    a.maps = maps;
+    a.dlam = dlambda;
+    a.dnorm_w = epi == DIFFATTN_EPI_RMSNORM_SCALE ? dnorm_w : nullptr;
+    a.batch = batch; a.heads = heads; a.seq_q = seq_q; a.seq_k = seq_k;
+    a.causal = causal ? 1 : 0;
+    a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
+    a.eps = eps; a.lambda_init = lambda_init;
+    const float sc = resolve_scale(scale, d);
+    a.scale = sc;
+    a.scale_log2 = sc * 1.4426950408889634f;
+    return hip_status(diffattn::launch_bwd(a, workspace, (hipStream_t)stream), "diffattn_bwd launch");
+}
+
+diffattn_status diffattn_lambda_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
+                                    const float* dlambda, int n, int dim, float* dlq1, float* dlk1, float* dlq2,
+                                    float* dlk2, void* stream) {
+    if (!lq1 || !lk1 || !lq2 || !lk2 || !dlambda || !dlq1 || !dlk1 || !dlq2 || !dlk2)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_lambda_bwd: null pointer");
+    if (n < 1 || dim < 1) return fail(DIFFATTN_ERR_ARG, "diffattn_lambda_bwd: n=%d dim=%d must be >= 1", n, dim);
+    return hip_status(diffattn::launch_lambda_bwd(lq1, lk1, lq2, lk2, dlambda, n, dim, dlq1, dlk1, dlq2, dlk2,
+                                                  (hipStream_t)stream),
+                      "diffattn_lambda_bwd launch");
 }
 
 }  // extern "C"

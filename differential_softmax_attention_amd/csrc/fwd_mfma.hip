@@ -70,6 +70,11 @@ struct Cfg {
     static_assert(K_LOADS >= 1 && V_LOADS >= 1, "tile must cover every thread");
 };
 
+// offset of (b, token, head)'s two maps in the [batch, seq_q, heads, 2, 128] training output
+__device__ __forceinline__ int64_t row_major_maps(const MfmaFwdArgs& a, int b, int qrow, int h) {
+    return (((int64_t)b * a.seq_q + qrow) * a.heads + h) * 2 * kDV;
+}
+
 template <int D, bool V2, bool CAUSAL, bool EPI>
 __global__ __launch_bounds__(V2 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(V2 ? 1 : 2, 2)))
 void fwd_mfma_kernel(MfmaFwdArgs a) {
@@ -384,6 +389,32 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     }
     const float r1 = 1.f / l1;
     const float r2 = lam / l2;
+    if (!V2 && a.lse && qrow < a.seq_q) {
+        // training outputs for the backward pass: each map's log-sum-exp in base 2 (in the units
+        // of the scaled scores, so a weight is exp2(c s - lse)) and its normalised output A_k V
+        const int64_t row = ((int64_t)b * a.heads + hout) * a.seq_q + qrow;
+        if (h2 == 0) {
+            a.lse[2 * row] = m1 + log2f(l1);
+            a.lse[2 * row + 1] = m2 + log2f(l2);
+        }
+        const float i2 = 1.f / l2;
+        float* mp = a.maps + row_major_maps(a, b, qrow, hout);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x1, x2;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x1[j] = o1[ct][g * 4 + j] * r1;
+                    x2[j] = o2[ct][g * 4 + j] * i2;
+                }
+                const int c = ct * 32 + g * 8 + h2 * 4;
+                *(f32x4*)(mp + c) = x1;
+                *(f32x4*)(mp + kDV + c) = x2;
+            }
+        }
+    }
     float ss = 0.f;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {

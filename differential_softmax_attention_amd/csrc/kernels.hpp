@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace diffattn {
 
 // Generic kernel: one output row per wave. Head mapping for output head h:
@@ -41,6 +43,11 @@ struct MfmaFwdArgs {
     int kv_group;     // V2: query heads per KV head (2h / h_kv); V1: unused
     int causal, epi;
     float eps, lambda_init, scale_log2;  // softmax scale * log2(e)
+    // V1 training outputs, both optional (null in inference): lse [batch, heads, seq_q, 2] holds each
+    // map's log-sum-exp in base 2 of the scaled scores; maps [batch, seq_q, heads, 2, 128] holds
+    // A1 V and A2 V in fp32
+    float* lse;
+    float* maps;
 };
 
 hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
@@ -82,6 +89,35 @@ int v2_decode_num_splits(int batch, int h_kv, int cache_len);
 size_t v2_decode_workspace_bytes(int batch, int h, int h_kv, int cache_len);
 bool v2_decode_group_ok(int group);
 hipError_t launch_v2_decode(V2DecodeArgs a, hipStream_t stream);
+
+// V1 backward (bf16, d = 64, dv = 128). Inputs as the forward plus dout [batch, seq_q, heads, 128]
+// and the forward's training outputs; gradients in the inputs' layouts (bf16), dlam [heads] and
+// dnorm_w [128] in fp32 (either may be null). go, dd, wpart, lampart live in the workspace.
+struct BwdArgs {
+    const void *q1, *q2, *k1, *k2, *v, *dout;
+    int64_t q1s[3], q2s[3], k1s[3], k2s[3], vs[3], dos[3];
+    void *dq1, *dq2, *dk1, *dk2, *dv;
+    int64_t dq1s[3], dq2s[3], dk1s[3], dk2s[3], dvs[3];
+    const float* lam;
+    const float* norm_w;
+    const float* lse;
+    const float* maps;
+    float* dlam;
+    float* dnorm_w;
+    bf16* go;        // [batch, heads, seq_q, 128] dL/do
+    float* dd;       // [batch, heads, seq_q, 2] D1, D2
+    float* wpart;    // [128][n_part] partial dL/dw
+    float* lampart;  // [n_part] partial dlambda
+    int n_part, pre_blocks;
+    int batch, heads, seq_q, seq_k, causal, epi;
+    float eps, lambda_init, scale_log2, scale;
+};
+
+size_t bwd_workspace_bytes(int batch, int heads, int seq_q);
+hipError_t launch_bwd(BwdArgs a, void* workspace, hipStream_t stream);
+hipError_t launch_lambda_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
+                             const float* dlam, int n, int dim, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                             hipStream_t stream);
 
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
                          int n, int dim, float lambda_init, float* out, hipStream_t stream);

@@ -165,6 +165,63 @@ diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
                                 void* stream);
 
 /*
+ * DIFF V1 training forward: diffattn_fwd plus what the backward pass needs.
+ *  lse:  DEVICE fp32 [batch, heads, seq_q, 2], 8-byte aligned: per row and map the log-sum-exp of
+ *        the scores in base 2, in units of scale * log2(e) * q.k (a weight is exp2(that - lse)).
+ *  maps: DEVICE fp32 [batch, seq_q, heads, 2, dv], 16-byte aligned: A1 V and A2 V per row.
+ *  The output and every other argument are those of diffattn_fwd.
+ *  Serves bf16 with d = 64, dv = 128 and aligned strides (the MFMA kernel); ERR_UNSUPPORTED else.
+ */
+diffattn_status diffattn_fwd_train(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,
+                                   diffattn_tensor k1, diffattn_tensor k2, diffattn_tensor v,
+                                   int batch, int heads, int seq_q, int seq_k, int d, int dv,
+                                   const float* lambda, float lambda_init, int causal,
+                                   diffattn_epilogue epi, const float* norm_w, float eps,
+                                   float scale, diffattn_tensor out, float* lse, float* maps,
+                                   void* stream);
+
+/* Bytes of device workspace diffattn_bwd needs (0 on invalid sizes): dL/do in bf16, two fp32
+ * row statistics per row and per-block partial sums. */
+size_t diffattn_bwd_workspace_size(int batch, int heads, int seq_q);
+
+/*
+ * DIFF V1 backward: the gradients of L = sum(dout * out) for the forward of diffattn_fwd_train
+ * (same inputs and options), by the chain rule through "Noise-Canceling Attention by
+ * Subtraction", sections "The mechanism" and "Making lambda learnable and stable": the RMSNorm *
+ * (1 - lambda_init) epilogue, the difference of the two maps, the two softmaxes and the products.
+ *  dout: [batch, seq_q, heads, dv];  lse, maps: the training forward's outputs for these inputs.
+ *  dq1, dq2: [batch, seq_q, heads, d];  dk1, dk2: [batch, seq_k, heads, d];  dv: like v; all
+ *  written (bf16), fp32 accumulation inside.
+ *  dlambda: DEVICE fp32 [heads] or NULL, written with dL/dlambda_h.  dnorm_w: DEVICE fp32 [dv] or
+ *  NULL, written with dL/dw (only with the RMSNorm epilogue; summed over all heads and rows).
+ *  workspace: DEVICE buffer of at least diffattn_bwd_workspace_size(...) bytes, 256-byte aligned.
+ *  Kernels: a row pass (epilogue backward and the per-row dot products), a query-tile MFMA kernel
+ *  for dQ, a key-tile MFMA kernel for dK and dV, and a fixed-order reduction; no atomics, so the
+ *  result is bitwise reproducible. Serves bf16 with d = 64, dv = 128 and aligned strides.
+ *  Errors: ERR_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP.
+ */
+diffattn_status diffattn_bwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,
+                             diffattn_tensor k1, diffattn_tensor k2, diffattn_tensor v,
+                             diffattn_tensor dout, int batch, int heads, int seq_q, int seq_k, int d,
+                             int dv, const float* lambda, float lambda_init, int causal,
+                             diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                             const float* lse, const float* maps, diffattn_tensor dq1,
+                             diffattn_tensor dq2, diffattn_tensor dk1, diffattn_tensor dk2,
+                             diffattn_tensor dv_out, float* dlambda, float* dnorm_w,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gradients of lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init with respect to the four
+ * vectors, given dlambda per row ("Noise-Canceling Attention by Subtraction", section "Making
+ * lambda learnable and stable"). All pointers DEVICE fp32; vectors [n, dim] row-major, dlambda [n].
+ *  Errors: ERR_ARG if a pointer is NULL or n < 1 or dim < 1.
+ */
+diffattn_status diffattn_lambda_bwd(const float* lq1, const float* lk1, const float* lq2,
+                                    const float* lk2, const float* dlambda, int n, int dim,
+                                    float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                                    void* stream);
+
+/*
  * Bytes of device workspace diffattn_v2_decode needs for these sizes (0 on invalid sizes). The
  * workspace holds, per cache slice and query head, the slice's shift, weight sum and 128-wide
  * accumulator in fp32.

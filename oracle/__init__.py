@@ -305,3 +305,28 @@ def lambda_backward(lq1, lk1, lq2, lk2, dlam):
     e1 = np.exp(np.sum(lq1 * lk1, axis=1, keepdims=True))
     e2 = np.exp(np.sum(lq2 * lk2, axis=1, keepdims=True))
     return dict(dlq1=dlam * e1 * lk1, dlk1=dlam * e1 * lq1, dlq2=-dlam * e2 * lk2, dlk2=-dlam * e2 * lq2)
+
+
+def v1_train_stats(q1, q2, k1, k2, v, causal=True, scale=None):
+    """What the training forward saves for the backward pass, from the definitions:
+    lse [B, H, Nq, 2]: per row and map log2(sum_j exp(s q . k_j)) * ... expressed in base 2 of the
+    scaled scores, i.e. log2(e) * ln(sum_j exp(s q . k_j)) over the visible keys;
+    maps [B, Nq, H, 2, dv]: A1 V and A2 V (each map's attention output, lambda = 0)."""
+    q1, q2, k1, k2, v = (np.asarray(x, dtype=np.float64) for x in (q1, q2, k1, k2, v))
+    B, Nq, H, d = q1.shape
+    Nk, dv = k1.shape[1], v.shape[3]
+    s = default_scale(d) if scale is None else float(scale)
+    lse = np.empty((B, H, Nq, 2))
+    maps = np.empty((B, Nq, H, 2, dv))
+    for b in range(B):
+        for h in range(H):
+            for m, (q, k) in enumerate(((q1, k1), (q2, k2))):
+                qq, kk = _f64(q[b, :, h]), _f64(k[b, :, h])
+                maps[b, :, h, m] = _head(qq, qq, kk, kk, _f64(v[b, :, h]), np.zeros(Nq), causal, s, None)
+                z = s * (qq @ kk.T)                                     # natural-unit logits
+                for i in range(Nq):
+                    n = Nk if not causal else min(Nk, i + (Nk - Nq) + 1)
+                    zi = z[i, :n]
+                    mx = zi.max()
+                    lse[b, h, i, m] = (mx + np.log(np.sum(np.exp(zi - mx)))) / np.log(2.0)
+    return lse, maps

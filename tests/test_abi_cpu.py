@@ -163,6 +163,46 @@ def test_v2_decode_workspace_size(L):
     assert 0 < small < big < 64 << 20      # slice partials only
 
 
+def _bwd(L, B=1, H=2, N=64, d=64, dv=128, dtype=1, lse=FAKE, maps=FAKE, lam=FAKE, ws=FAKE, ws_bytes=1 << 30, epi=1,
+         causal=1, Nk=None):
+    Nk = N if Nk is None else Nk
+    ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(11)]
+    return L.diffattn_bwd(dtype, *ts[:6], B, H, N, Nk, d, dv, lam, 0.8, causal, epi, None, 1e-5, 0.0, lse, maps,
+                          *ts[6:], FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_bwd_rejects(L):
+    assert _bwd(L, lse=None) == da.DIFFATTN_ERR_ARG
+    assert _bwd(L, maps=None) == da.DIFFATTN_ERR_ARG
+    assert _bwd(L, lam=None) == da.DIFFATTN_ERR_ARG
+    assert _bwd(L, N=0) == da.DIFFATTN_ERR_ARG
+    assert _bwd(L, N=65, Nk=64) == da.DIFFATTN_ERR_ARG                   # causal with seq_q > seq_k
+    assert _bwd(L, epi=7) == da.DIFFATTN_ERR_ARG
+    need = L.diffattn_bwd_workspace_size(1, 2, 64)
+    assert need > 0
+    assert _bwd(L, ws_bytes=need - 1) == da.DIFFATTN_ERR_WORKSPACE
+    assert _bwd(L, ws=FAKE + 32) == da.DIFFATTN_ERR_ARG
+    assert _bwd(L, d=32) == da.DIFFATTN_ERR_UNSUPPORTED
+    assert _bwd(L, dtype=0) == da.DIFFATTN_ERR_UNSUPPORTED               # fp32: no backward kernel
+    assert L.diffattn_bwd_workspace_size(0, 2, 64) == 0
+
+
+def test_fwd_train_rejects(L):
+    ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(6)]
+    call = lambda lse, maps, d=64, dtype=1: L.diffattn_fwd_train(dtype, *ts[:5], 1, 2, 64, 64, d, 128, FAKE, 0.8, 1,
+                                                                 1, None, 1e-5, 0.0, ts[5], lse, maps, None)
+    assert call(None, FAKE) == da.DIFFATTN_ERR_ARG
+    assert call(FAKE, None) == da.DIFFATTN_ERR_ARG
+    assert call(FAKE, FAKE + 4) == da.DIFFATTN_ERR_ARG                   # maps not 16-byte aligned
+    assert call(FAKE, FAKE, d=32) == da.DIFFATTN_ERR_UNSUPPORTED
+    assert call(FAKE, FAKE, dtype=0) == da.DIFFATTN_ERR_UNSUPPORTED
+
+
+def test_lambda_bwd_rejects(L):
+    assert L.diffattn_lambda_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, None) == da.DIFFATTN_ERR_ARG
+    assert L.diffattn_lambda_bwd(FAKE, FAKE, FAKE, FAKE, None, 16, 64, FAKE, FAKE, FAKE, FAKE, None) == da.DIFFATTN_ERR_ARG
+
+
 def test_lambda_rejects(L):
     assert L.diffattn_lambda(FAKE, FAKE, FAKE, FAKE, 0, 64, 12, FAKE, None) == da.DIFFATTN_ERR_ARG
     assert L.diffattn_lambda(FAKE, FAKE, FAKE, FAKE, 16, 0, 12, FAKE, None) == da.DIFFATTN_ERR_ARG
