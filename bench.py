@@ -7,8 +7,9 @@ forward. Inputs are synthetic (seeded) and resident in HBM before timing starts.
 line on stdout; progress goes to stderr.
 
 Also measured in the same run (reported under "secondary"): the 32K-token prefill with a planted
-needle, the 64K-entry V1 decode and the V2 decode (GB/s against HBM) and the V2 GQA prefill; and
-the fp64 oracle on a bounded sample of the main workload, timed on the host cores ("cpu_baseline").
+needle, the 64K-entry V1 decode and the V2 decode (GB/s against HBM), the V2 GQA prefill and the
+V1 backward pass on the main workload; and the fp64 oracle on a bounded sample of the main
+workload, timed on the host cores ("cpu_baseline").
 
 Throughput counts algorithmic work only: 768 flop per visible (query, key) pair for V1 (two
 QK^T products of width 64 and two PV products of width 128), 512 per visible pair and query head
@@ -30,6 +31,9 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 FLOP_PER_PAIR_V1 = 768
 FLOP_PER_PAIR_V2 = 512
+# backward: recomputed scores (2 x 2d), dP = go V^T (2 dv), dV (2 dv), dK and dQ of both maps
+# (2 x 2d each): 1280 per visible pair at d = 64, dv = 128
+FLOP_PER_PAIR_V1_BWD = 1280
 DECODE_BYTES_PER_TOKEN = 2 * (64 + 64 + 128)
 
 
@@ -78,8 +82,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--secondary", default="32k,decode,v2,v2decode",
-                    help="comma list of extra workloads to time (32k, decode, v2, v2decode) or 'none'")
+    ap.add_argument("--secondary", default="32k,decode,v2,v2decode,bwd",
+                    help="comma list of extra workloads to time (32k, decode, v2, v2decode, bwd) or 'none'")
     ap.add_argument("--secondary-reps", type=int, default=10)
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the fp64 oracle on a sample (1) or not (0)")
     ap.add_argument("--copy-calibration", type=int, default=1,
@@ -242,6 +246,35 @@ def main():
                                       "traffic": load_traffic("v1_decode_64k", ["decode.hip", "common.hpp"])}
         log(f"[bench]   {avg:.3f} ms -> {gbs:.0f} GB/s")
         del x4, ws, o4
+    if "bwd" in which:
+        # training step of the main workload: the training forward and the backward pass
+        c7 = W.V1_PREFILL_2K
+        log(f"[bench] backward, {c7.name}")
+        x7 = W.v1_inputs(c7, device=dev)
+        lam7 = da.diffattn_lambda(*(x7[k].to(dev) for k in ("lq1", "lk1", "lq2", "lk2")), c7.layer)
+        li7 = da.lambda_init(c7.layer)
+        g7 = torch.Generator(device=dev).manual_seed(7)
+        dy7 = torch.randn((c7.B, c7.N, c7.H, c7.dv), generator=g7, device=dev).to(torch.bfloat16)
+        args7 = (x7["q1"], x7["q2"], x7["k1"], x7["k2"], x7["v"])
+        ft = lambda: da.diffattn_fwd_train(*args7, lam7, causal=True, epilogue=True, lambda_init_value=li7)
+        _, lse7, maps7 = ft()
+        ws7 = torch.empty(da.diffattn_bwd_workspace_size(c7.B, c7.H, c7.N), dtype=torch.uint8, device=dev)
+        fb = lambda: da.diffattn_bwd(*args7, dy7, lam7, lse7, maps7, causal=True, epilogue=True,
+                                     lambda_init_value=li7, workspace=ws7)
+        fb()
+        torch.cuda.synchronize()
+        avg_f, mn_f = time_launches(ft, args.secondary_reps, torch)
+        avg_b, mn_b = time_launches(fb, args.secondary_reps, torch)
+        pairs7 = c7.B * c7.H * causal_pairs(c7.N)
+        fl_b = FLOP_PER_PAIR_V1_BWD * pairs7
+        secondary["v1_backward_2k"] = {"workload": c7.name, "train_forward_avg_ms": round(avg_f, 4),
+                                       "backward_avg_ms": round(avg_b, 4), "backward_min_ms": round(mn_b, 4),
+                                       "flop": fl_b, "flop_per_visible_pair": FLOP_PER_PAIR_V1_BWD,
+                                       "TFLOP/s": round(fl_b / (avg_b * 1e-3) / 1e12, 2),
+                                       "frac_of_bf16_peak": round(fl_b / (avg_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench]   training forward {avg_f:.3f} ms, backward {avg_b:.3f} ms -> "
+            f"{fl_b / (avg_b * 1e-3) / 1e12:.1f} TFLOP/s")
+        del x7, dy7, lse7, maps7, ws7
     if "v2decode" in which:
         c6 = W.V2_DECODE_64K
         log(f"[bench] {c6.name} (generating the cache on the device)")
