@@ -22,13 +22,18 @@ ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include")]
+# Per-source additions. The dK/dV backward kernel runs one wave per SIMD with ~320 live
+# registers; left to itself the compiler gives its MFMA accumulators the AGPR form and then
+# copies them to VGPRs around every element-wise step. The VGPR form keeps them in place.
+SOURCE_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    flags = CFLAGS + SOURCE_FLAGS.get(src, [])
+    cmd = [HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -36,6 +36,11 @@ constexpr int kDV = 128;
 constexpr int kKTile = kBN * kD * 2;    // bytes of one 32-row, 64-wide tile (K-layout)
 constexpr int kVTile = kBN * kDV * 2;   // bytes of one 32-row, 128-wide tile (V-layout)
 constexpr int kPreRows = 16;            // rows per bwd_pre block (4 waves x 4 rows)
+// dK/dV query-tile stage: Q1 | Q2 (K-layout) | go (V-layout) | lse [32][2] | dd [32][2]
+constexpr int kQStats = 2 * kKTile + kVTile;
+constexpr int kQStage = kQStats + 2 * kBN * 2 * 4;
+constexpr int kQStages = 3;
+constexpr int kKStages = 3;             // dQ key-tile ring
 
 // ---- LDS operand addressing (tiles as in the forward: K-layout 64 wide, V-layout 128 wide)
 // Row operand: row `row`, 16-byte logical chunk 2kk + h2 (MFMA A rows or B columns).
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------------------
 // dQ: a block of 4 waves owns 128 queries of one head, 32 per wave, and walks the key tiles.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
-    __shared__ __align__(16) unsigned char smem[1][2 * kKTile + kVTile];
+    __shared__ __align__(16) unsigned char smem[kKStages][2 * kKTile + kVTile];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, h2 = lane >> 5;
     const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -227,16 +232,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) { dq1[mt] = f32x16{}; dq2[mt] = f32x16{}; }
 
-    auto stage = [&](int kt, int st) {
-        const int nrows = min(kBN, a.seq_k - kt * kBN);
-        stage_tile<kD>(smem[st], k1b + (int64_t)kt * kBN * a.k1s[1], a.k1s[1], nrows, tid, 256);
-        stage_tile<kD>(smem[st] + kKTile, k2b + (int64_t)kt * kBN * a.k2s[1], a.k2s[1], nrows, tid, 256);
-        stage_tile<kDV>(smem[st] + 2 * kKTile, vb + (int64_t)kt * kBN * a.vs[1], a.vs[1], nrows, tid, 256);
+    // key-tile DMA (as the forward): thread tid fills K1 and K2 slot tid and V slots tid, tid + 256;
+    // rows past the last key are fetched from the last one (their weights are masked to zero)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8_t*)&smem[0][0];
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int k_row = tid >> 3, k_col = (tid & 7) ^ k_swz<kD>(k_row);
+    const int v_row0 = tid >> 4, v_row1 = v_row0 + 16;
+    const int v_col0 = v_logical(v_row0, tid & 15), v_col1 = v_logical(v_row1, tid & 15);
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+        const int last = min(kBN, a.seq_k - kt * kBN) - 1;
+        const uint32_t st = lds0 + (kt % kKStages) * (2 * kKTile + kVTile) + wave_u * 1024;
+        const int kr = min(k_row, last);
+        dma16(k1b + (int64_t)kt * kBN * a.k1s[1], (uint32_t)(kr * a.k1s[1] + k_col * 8) * 2u, st);
+        dma16(k2b + (int64_t)kt * kBN * a.k2s[1], (uint32_t)(kr * a.k2s[1] + k_col * 8) * 2u, st + kKTile);
+        const bf16* vt = vb + (int64_t)kt * kBN * a.vs[1];
+        dma16(vt, (uint32_t)(min(v_row0, last) * a.vs[1] + v_col0 * 8) * 2u, st + 2 * kKTile);
+        dma16(vt, (uint32_t)(min(v_row1, last) * a.vs[1] + v_col1 * 8) * 2u, st + 2 * kKTile + 4096);
     };
+    for (int kt = 0; kt < nkt && kt < kKStages - 1; ++kt) issue(kt);
     for (int kt = 0; kt < nkt; ++kt) {
-        const int st = 0;   // one stage: the block syncs before and after each tile
-        stage(kt, st);
-        __syncthreads();
+        const int st = kt % kKStages;
+        if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(kVmcnt[4]);   // tile kt+1's loads may stay in flight
+        else __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+        __syncthreads();   // tile kt landed for every thread; the stage of tile kt-1 is free
+        if (kt + kKStages - 1 < nkt) issue(kt + kKStages - 1);
         const int k0 = kt * kBN;
         if (wave_active && (!a.causal || k0 <= wave_qlast + off)) {
             const unsigned char* K1s = smem[st];
@@ -273,7 +292,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             }
         }
-        __syncthreads();
     }
     if (!qok) return;
     // dQ_k = s dS_k K_k; lane (n, h2) holds d = 32 mt + (r / 4) * 8 + 4 h2 + r % 4 of query n
@@ -299,11 +317,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // dK, dV: a block of 4 waves owns 128 keys of one head, 32 per wave, and walks the query tiles.
 // (82 KB of LDS allow one block per CU, so the waves may use the whole register file)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs a) {
-    // the wave's own K1 | K2 | V (read as B operands every step) and the shared query tile
+    // the wave's own K1 | K2 | V (read as B operands every step) and a ring of query tiles
     __shared__ __align__(16) unsigned char skv[4][2 * kKTile + kVTile];
-    __shared__ __align__(16) unsigned char sq[2 * kKTile + kVTile];
-    __shared__ __align__(16) float sv[4][kBN];   // lse1, lse2, D1, D2 of the query tile
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    __shared__ __align__(16) unsigned char sq[kQStages][kQStage];
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = tid & 63;
     const int n = lane & 31, h2 = lane >> 5;
     const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int k0 = kt * 128, kw0 = k0 + wave * 32, key = kw0 + n;
@@ -313,13 +330,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     {
         const int nrows = max(0, min(kBN, a.seq_k - kw0));
-        const int64_t t = tid & 63;
         stage_tile<kD>(skv[wave], (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)h * a.k1s[2] + (int64_t)kw0 * a.k1s[1],
-                       a.k1s[1], nrows, (int)t, 64);
+                       a.k1s[1], nrows, lane, 64);
         stage_tile<kD>(skv[wave] + kKTile, (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)h * a.k2s[2] + (int64_t)kw0 * a.k2s[1],
-                       a.k2s[1], nrows, (int)t, 64);
+                       a.k2s[1], nrows, lane, 64);
         stage_tile<kDV>(skv[wave] + 2 * kKTile, (const bf16*)a.v + b * a.vs[0] + (int64_t)h * a.vs[2] + (int64_t)kw0 * a.vs[1],
-                        a.vs[1], nrows, (int)t, 64);
+                        a.vs[1], nrows, lane, 64);
     }
     const unsigned char* K1s = skv[wave];
     const unsigned char* K2s = skv[wave] + kKTile;
@@ -340,27 +356,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16* q2b = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)h * a.q2s[2];
     const int64_t rowb = ((int64_t)b * a.heads + h) * a.seq_q;
 
+    // query-tile DMA: thread tid fills Q1 and Q2 slot tid and go slots tid, tid + 256; wave 0 also
+    // fetches the rows' log-sum-exp and D values (64 floats each). Rows past the last query are
+    // fetched from the last one (their weights are masked to zero).
+    const uint32_t lds_sq = (uint32_t)(uintptr_t)(lds_u8_t*)&sq[0][0];
+    const int q_row = tid >> 3, q_col = (tid & 7) ^ k_swz<kD>(q_row);
+    const int g_row0 = tid >> 4, g_row1 = g_row0 + 16;
+    const int g_col0 = v_logical(g_row0, tid & 15), g_col1 = v_logical(g_row1, tid & 15);
+    auto issue_q = [&](int qt) __attribute__((always_inline)) {
+        const int i0 = qt * kBN;
+        const int last = min(kBN, a.seq_q - i0) - 1;
+        const uint32_t st = lds_sq + (qt % kQStages) * kQStage + wave * 1024;
+        const int qr = min(q_row, last);
+        dma16(q1b + (int64_t)i0 * a.q1s[1], (uint32_t)(qr * a.q1s[1] + q_col * 8) * 2u, st);
+        dma16(q2b + (int64_t)i0 * a.q2s[1], (uint32_t)(qr * a.q2s[1] + q_col * 8) * 2u, st + kKTile);
+        const bf16* gb = a.go + (rowb + i0) * kDV;
+        dma16(gb, (uint32_t)(min(g_row0, last) * kDV + g_col0 * 8) * 2u, st + 2 * kKTile);
+        dma16(gb, (uint32_t)(min(g_row1, last) * kDV + g_col1 * 8) * 2u, st + 2 * kKTile + 4096);
+        if (wave == 0) {
+            // lane i fetches float i of the tile's 32 rows x 2 (clamped to the last row)
+            const uint32_t sst = lds_sq + (qt % kQStages) * kQStage + kQStats;
+            const uint32_t fo = (uint32_t)min(lane, 2 * last + 1) * 4u;
+            dma4(a.lse + 2 * (rowb + i0), fo, sst);
+            dma4(a.dd + 2 * (rowb + i0), fo, sst + 256);
+        }
+    };
+
+    for (int qt = qt0; qt < nqt && qt < qt0 + kQStages - 1; ++qt) issue_q(qt);
     for (int qt = qt0; qt < nqt; ++qt) {
         const int i0 = qt * kBN;
-        const int nrows = min(kBN, a.seq_q - i0);
-        __syncthreads();   // the previous tile is no longer read
-        stage_tile<kD>(sq, q1b + (int64_t)i0 * a.q1s[1], a.q1s[1], nrows, tid, 256);
-        stage_tile<kD>(sq + kKTile, q2b + (int64_t)i0 * a.q2s[1], a.q2s[1], nrows, tid, 256);
-        stage_tile<kDV>(sq + 2 * kKTile, a.go + (rowb + i0) * kDV, kDV, nrows, tid, 256);
-        if (tid < kBN) {
-            const bool ok = tid < nrows;
-            const int64_t r = rowb + i0 + tid;
-            sv[0][tid] = ok ? a.lse[2 * r] : 0.f;
-            sv[1][tid] = ok ? a.lse[2 * r + 1] : 0.f;
-            sv[2][tid] = ok ? a.dd[2 * r] : 0.f;
-            sv[3][tid] = ok ? a.dd[2 * r + 1] : 0.f;
+        // this thread's DMA of tile qt has landed (the next tile's loads may be in flight)
+        if (qt + 1 < nqt) {
+            if (wave == 0) __builtin_amdgcn_s_waitcnt(kVmcnt[6]);
+            else __builtin_amdgcn_s_waitcnt(kVmcnt[4]);
+        } else {
+            __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
         }
-        __syncthreads();
+        __syncthreads();   // every thread's loads of tile qt landed; the stage of tile qt-1 is free
+        if (qt + kQStages - 1 < nqt) issue_q(qt + kQStages - 1);
+        const unsigned char* stq = &sq[qt % kQStages][0];
+        const float* svl = (const float*)(stq + kQStats);          // lse [32][2]
+        const float* svd = (const float*)(stq + kQStats + 256);    // dd [32][2]
         // skip the tile if it ends before this wave's first key (causal)
         if (!wave_active || (a.causal && i0 + kBN - 1 + off < kw0)) continue;
-        const unsigned char* Q1s = sq;
-        const unsigned char* Q2s = sq + kKTile;
-        const unsigned char* Gs = sq + 2 * kKTile;
+        const unsigned char* Q1s = stq;
+        const unsigned char* Q2s = stq + kKTile;
+        const unsigned char* Gs = stq + 2 * kKTile;
         // dP = go V^T (rows = queries, lane = key n)
         f32x16 dp = f32x16{};
 #pragma unroll
@@ -378,12 +419,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             f32x16 ds;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 lse = *(const f32x4*)&sv[map][8 * g + 4 * h2];
-                const f32x4 dd = *(const f32x4*)&sv[2 + map][8 * g + 4 * h2];
+                // rows 8g + 4h2 .. +3: their (map 1, map 2) pairs are 8 consecutive floats
+                const int q4 = 8 * g + 4 * h2;
+                const f32x4 l01 = *(const f32x4*)(svl + 2 * q4), l23 = *(const f32x4*)(svl + 2 * q4 + 4);
+                const f32x4 d01 = *(const f32x4*)(svd + 2 * q4), d23 = *(const f32x4*)(svd + 2 * q4 + 4);
+                const float lse[4] = {l01[map], l01[2 + map], l23[map], l23[2 + map]};
+                const float dd[4] = {d01[map], d01[2 + map], d23[map], d23[2 + map]};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * g + j;
-                    const int q = i0 + 8 * g + 4 * h2 + j;
+                    const int q = i0 + q4 + j;
                     const bool vis = q < a.seq_q && key < a.seq_k && (!a.causal || key <= q + off);
                     const float p = vis ? fast_exp2(fmaf(s[r], c, -lse[j])) : 0.f;
                     ds[r] = coef * p * (dp[r] - dd[j]);

@@ -43,6 +43,15 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                  : : "v"(voff), "s"((const void*)(uintptr_t)u), "{m0}"(lds_wave_base) : "memory");
 }
 
+// 4-byte variant: lane i reads sbase + voff and the word lands at lds_wave_base + 4 i
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+    const uint64_t p = (uint64_t)(uintptr_t)sbase;
+    const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    asm volatile("global_load_lds_dword %0, %1"
+                 : : "v"(voff), "s"((const void*)(uintptr_t)u), "{m0}"(lds_wave_base) : "memory");
+}
+
 // maximum that ignores NaN-quieting (v_maximum3 / v_max without canonicalisation)
 __device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
