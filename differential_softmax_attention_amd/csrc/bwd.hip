@@ -18,9 +18,11 @@
 //  - bwd_dq: query-tile parallel like the forward (S^T = K Q^T, lane = query): K1, K2, V tiles of
 //    32 keys staged through LDS; dP^T = V go^T; dQ_k^T += K_k^T dS_k^T with K^T read by the
 //    transposing LDS read.
-//  - bwd_dkdv: key-tile parallel (S = Q K^T, lane = key): each wave keeps its 32 keys' K1, K2, V in
-//    LDS and walks the query tiles; dV^T += go^T (A1 - lambda A2) and dK_k^T += Q_k^T dS_k with the
-//    transposed operands again read by ds_read_b64_tr_b16.
+//  - bwd_dkdv: key-tile parallel (S = Q K^T, lane = key): each lane keeps its key's K1, K2, V rows
+//    in registers and the block walks the query tiles (Q1, Q2, go staged through LDS);
+//    dV^T += go^T (A1 - lambda A2) and dK_k^T += Q_k^T dS_k with the transposed operands again
+//    read by ds_read_b64_tr_b16.
+// Tiles that hold no masked (query, key) pair skip the per-element visibility test.
 //  - bwd_reduce: dlambda per head and dL/dw per channel from the partials.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -40,20 +42,28 @@ constexpr int kPreRows = 16;            // rows per bwd_pre block (4 waves x 4 r
 constexpr int kQStats = 2 * kKTile + kVTile;
 constexpr int kQStage = kQStats + 2 * kBN * 2 * 4;
 constexpr int kQStages = 3;
-constexpr int kKStages = 3;             // dQ key-tile ring
+constexpr int kKStage = 2 * kKTile + kVTile;   // dQ key-tile stage: K1 | K2 (64 wide) | V
+constexpr int kKStages = 3;
 
-// ---- LDS operand addressing (tiles as in the forward: K-layout 64 wide, V-layout 128 wide)
+// ---- LDS operand addressing
+// V-layout (128 wide) tiles use the forward's layout. The 64-wide tiles of the backward (Q tiles in
+// dK/dV, K tiles in dQ) are read both by rows (16-byte reads) and transposed (8-byte reads), so
+// their chunk swizzle differs from the forward's K-layout: 16-byte chunk c of row r sits at
+//   c ^ (4 ((r >> 1) & 1) | ((r >> 2) & 3)),
+// which puts 16 consecutive rows of one chunk, and 4 consecutive rows of 4 chunks, on distinct
+// banks.
+__device__ __forceinline__ int bswz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 // Row operand: row `row`, 16-byte logical chunk 2kk + h2 (MFMA A rows or B columns).
-__device__ __forceinline__ int rowop_k(int row, int kk, int h2) { return row * (kD * 2) + (((2 * kk + h2) ^ k_swz<kD>(row)) * 16); }
+__device__ __forceinline__ int rowop_b(int row, int kk, int h2) { return row * (kD * 2) + (((2 * kk + h2) ^ bswz(row)) * 16); }
 __device__ __forceinline__ int rowop_v(int row, int kk, int h2) { return row * (kDV * 2) + v_phys(row, 2 * kk + h2) * 16; }
 // Transposing read (A operand X^T of a row-major tile X whose rows are the MFMA k index): 16-lane
 // group G covers columns 32 mt + 16 (G & 1) .. +15 and rows 16 kb + 4 (G >> 1) + 0..3 (lo) and
 // +8 (hi); lane L supplies row + L/4 and columns + 4 (L % 4) .. +3.
-__device__ __forceinline__ int trop_k(int lane, int kb, int mt, int hi) {
+__device__ __forceinline__ int trop_b(int lane, int kb, int mt, int hi) {
     const int G = lane >> 4, L = lane & 15;
     const int row = 16 * kb + 4 * (G >> 1) + (L >> 2) + 8 * hi;
     const int c = mt * 4 + (G & 1) * 2 + ((L >> 1) & 1);
-    return row * (kD * 2) + ((c ^ k_swz<kD>(row)) * 16) + (L & 1) * 8;
+    return row * (kD * 2) + ((c ^ bswz(row)) * 16) + (L & 1) * 8;
 }
 __device__ __forceinline__ int trop_v(int lane, int kb, int ct, int hi) {
     const int G = lane >> 4, L = lane & 15;
@@ -75,19 +85,21 @@ __device__ __forceinline__ bf16x8 c_to_b(const f32x16& x, int kb) {
     return r;
 }
 
-// Copy a 32-row tile from global (row stride rs elements) into LDS in the K- (W = 64) or
-// V-layout (W = 128), rows past `nrows` zeroed. All nt threads of the block take part.
-template <int W>
-__device__ __forceinline__ void stage_tile(unsigned char* dst, const bf16* src, int64_t rs, int nrows, int tid, int nt) {
-    constexpr int CPR = W / 8;   // chunks per row
-    for (int s = tid; s < kBN * CPR; s += nt) {
-        const int row = s / CPR, c = s % CPR;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row < nrows) x = *(const u32x4*)(src + (int64_t)row * rs + c * 8);
-        const int phys = W == kD ? (c ^ k_swz<kD>(row)) : v_phys(row, c);
-        *(u32x4*)(dst + row * (W * 2) + phys * 16) = x;
-    }
+// acc += a b with the accumulator held in AGPRs. The gradient accumulators stay live across the
+// whole tile loop while each tile's products are worked on by VALU code in VGPRs; issuing these
+// accumulations by hand pins the accumulators to the AGPR file, where the compiler would otherwise
+// copy them back and forth. The compiler does not look into the asm, so it also carries the two
+// wait states that a VALU write of an operand needs before an MFMA reads it.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// Wait states between the last such MFMA and VALU reads of its accumulator (more than the 18 the
+// longest MFMA needs).
+__device__ __forceinline__ void agpr_drain(f32x16& x0, f32x16& x1, f32x16& x2, f32x16& x3) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3));
+}
+
+template <int V> struct IC { static constexpr int value = V; };
 
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
@@ -189,10 +201,11 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------------------
 // dQ: a block of 4 waves owns 128 queries of one head, 32 per wave, and walks the key tiles.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
-    __shared__ __align__(16) unsigned char smem[kKStages][2 * kKTile + kVTile];
+    __shared__ __align__(16) unsigned char smem[kKStages * kKStage];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, h2 = lane >> 5;
-    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // the last query tiles see the most keys under causal masking: they go first
+    const int qt = gridDim.y - 1 - blockIdx.y, h = blockIdx.x % a.heads, b = blockIdx.x / a.heads;
     const int q0 = qt * 128, qw0 = q0 + wave * 32, qrow = qw0 + n;
     const int off = a.seq_k - a.seq_q;
     const bool qok = qrow < a.seq_q;
@@ -223,6 +236,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (a.causal) nkt = min(nkt, (min(q0 + 127, a.seq_q - 1) + off) / kBN + 1);
     const bool wave_active = qw0 < a.seq_q;
     const int wave_qlast = min(qw0 + 31, a.seq_q - 1);
+    // last key each lane's query sees
+    const int qlim = a.causal ? min(qrow + off, a.seq_k - 1) : a.seq_k - 1;
 
     const bf16* k1b = (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)h * a.k1s[2];
     const bf16* k2b = (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)h * a.k2s[2];
@@ -232,16 +247,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) { dq1[mt] = f32x16{}; dq2[mt] = f32x16{}; }
 
-    // key-tile DMA (as the forward): thread tid fills K1 and K2 slot tid and V slots tid, tid + 256;
-    // rows past the last key are fetched from the last one (their weights are masked to zero)
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8_t*)&smem[0][0];
+    // key-tile DMA: thread tid fills K1 and K2 slot tid and V slots tid, tid + 256; rows past the
+    // last key are fetched from the last one (their weights are masked to zero)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int k_row = tid >> 3, k_col = (tid & 7) ^ k_swz<kD>(k_row);
+    const int k_row = tid >> 3, k_col = (tid & 7) ^ bswz(k_row);
     const int v_row0 = tid >> 4, v_row1 = v_row0 + 16;
     const int v_col0 = v_logical(v_row0, tid & 15), v_col1 = v_logical(v_row1, tid & 15);
-    auto issue = [&](int kt) __attribute__((always_inline)) {
+    auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         const int last = min(kBN, a.seq_k - kt * kBN) - 1;
-        const uint32_t st = lds0 + (kt % kKStages) * (2 * kKTile + kVTile) + wave_u * 1024;
+        const uint32_t st = lds0 + stage * kKStage + wave_u * 1024;
         const int kr = min(k_row, last);
         dma16(k1b + (int64_t)kt * kBN * a.k1s[1], (uint32_t)(kr * a.k1s[1] + k_col * 8) * 2u, st);
         dma16(k2b + (int64_t)kt * kBN * a.k2s[1], (uint32_t)(kr * a.k2s[1] + k_col * 8) * 2u, st + kKTile);
@@ -249,49 +264,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dma16(vt, (uint32_t)(min(v_row0, last) * a.vs[1] + v_col0 * 8) * 2u, st + 2 * kKTile);
         dma16(vt, (uint32_t)(min(v_row1, last) * a.vs[1] + v_col1 * 8) * 2u, st + 2 * kKTile + 4096);
     };
-    for (int kt = 0; kt < nkt && kt < kKStages - 1; ++kt) issue(kt);
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int st = kt % kKStages;
-        if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(kVmcnt[4]);   // tile kt+1's loads may stay in flight
-        else __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
-        __syncthreads();   // tile kt landed for every thread; the stage of tile kt-1 is free
-        if (kt + kKStages - 1 < nkt) issue(kt + kKStages - 1);
-        const int k0 = kt * kBN;
-        if (wave_active && (!a.causal || k0 <= wave_qlast + off)) {
-            const unsigned char* K1s = smem[st];
-            const unsigned char* K2s = smem[st] + kKTile;
-            const unsigned char* Vs = smem[st] + 2 * kKTile;
-            // S^T = K Q^T (lane = query n, 16 keys), dP^T = V go^T
-            f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
+
+    // one key tile; !full: some (query, key) pair of the wave's 32 x 32 block is not visible
+    auto compute = [&](auto ST, bool full, int k0) __attribute__((always_inline)) {
+        const unsigned char* K1s = smem + decltype(ST)::value * kKStage;
+        const unsigned char* K2s = K1s + kKTile;
+        const unsigned char* Vs = K1s + 2 * kKTile;
+        // S^T = K Q^T (lane = query n, 16 keys), dP^T = V go^T
+        f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                s1 = mfma32x32x16(lds16(K1s + rowop_k(n, kk, h2)), bq1[kk], s1);
-                s2 = mfma32x32x16(lds16(K2s + rowop_k(n, kk, h2)), bq2[kk], s2);
-            }
+        for (int kk = 0; kk < 4; ++kk) {
+            s1 = mfma32x32x16(lds16(K1s + rowop_b(n, kk, h2)), bq1[kk], s1);
+            s2 = mfma32x32x16(lds16(K2s + rowop_b(n, kk, h2)), bq2[kk], s2);
+        }
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Vs + rowop_v(n, kk, h2)), bg[kk], dp);
-            const int qlim = a.causal ? min(qrow + off, a.seq_k - 1) : a.seq_k - 1;
-            f32x16 ds1, ds2;
+        for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Vs + rowop_v(n, kk, h2)), bg[kk], dp);
+        f32x16 p1, p2, ds1, ds2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p1[r] = fast_exp2(fmaf(s1[r], c, -lse1));
+            p2[r] = fast_exp2(fmaf(s2[r], c, -lse2));
+        }
+        if (!full) {
+            asm volatile("");   // keeps this a branch: full tiles skip the test
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = k0 + (r >> 2) * 8 + h2 * 4 + (r & 3);
                 const bool vis = qok && key <= qlim;
-                const float p1 = vis ? fast_exp2(fmaf(s1[r], c, -lse1)) : 0.f;
-                const float p2 = vis ? fast_exp2(fmaf(s2[r], c, -lse2)) : 0.f;
-                ds1[r] = p1 * (dp[r] - D1);
-                ds2[r] = -lam * p2 * (dp[r] - D2);
-            }
-            // dQ_k^T += K_k^T dS_k^T (k index = keys)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 b1 = c_to_b(ds1, kb), b2 = c_to_b(ds2, kb);
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    dq1[mt] = mfma32x32x16(tr_pair(K1s, trop_k(lane, kb, mt, 0), trop_k(lane, kb, mt, 1)), b1, dq1[mt]);
-                    dq2[mt] = mfma32x32x16(tr_pair(K2s, trop_k(lane, kb, mt, 0), trop_k(lane, kb, mt, 1)), b2, dq2[mt]);
-                }
+                p1[r] = vis ? p1[r] : 0.f;
+                p2[r] = vis ? p2[r] : 0.f;
             }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            ds1[r] = p1[r] * (dp[r] - D1);
+            ds2[r] = -lam * p2[r] * (dp[r] - D2);
+        }
+        // dQ_k^T += K_k^T dS_k^T (k index = keys)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 b1 = c_to_b(ds1, kb), b2 = c_to_b(ds2, kb);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                dq1[mt] = mfma32x32x16(tr_pair(K1s, trop_b(lane, kb, mt, 0), trop_b(lane, kb, mt, 1)), b1, dq1[mt]);
+                dq2[mt] = mfma32x32x16(tr_pair(K2s, trop_b(lane, kb, mt, 0), trop_b(lane, kb, mt, 1)), b2, dq2[mt]);
+            }
+        }
+    };
+    auto tile = [&](auto ST, int kt) __attribute__((always_inline)) {
+        constexpr int st = decltype(ST)::value;
+        if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(kVmcnt[4]);   // tile kt+1's loads may stay in flight
+        else __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+        __syncthreads();   // tile kt landed for every thread; the stage of tile kt-1 is free
+        if (kt + kKStages - 1 < nkt) issue(kt + kKStages - 1, (st + kKStages - 1) % kKStages);
+        const int k0 = kt * kBN;
+        if (!wave_active || (a.causal && k0 > wave_qlast + off)) return;
+        compute(ST, qw0 + kBN <= a.seq_q && k0 + kBN <= a.seq_k && (!a.causal || k0 + kBN - 1 <= qw0 + off), k0);
+    };
+    // the ring position of a tile is its index modulo 3, and the loop is unrolled by 3 so that
+    // every LDS address is a register plus a constant
+    for (int kt = 0; kt < nkt && kt < kKStages - 1; ++kt) issue(kt, kt);
+    // the query operands and the first tiles have landed: from here on the compiler sees no
+    // outstanding loads of its own and adds no waits on the key-tile DMA
+    __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+    for (int kt = 0; kt < nkt; kt += kKStages) {
+        tile(IC<0>{}, kt);
+        if (kt + 1 < nkt) tile(IC<1>{}, kt + 1);
+        if (kt + 2 < nkt) tile(IC<2>{}, kt + 2);
     }
     if (!qok) return;
     // dQ_k = s dS_k K_k; lane (n, h2) holds d = 32 mt + (r / 4) * 8 + 4 h2 + r % 4 of query n
@@ -315,31 +354,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ------------------------------------------------------------------------------------------------
 // dK, dV: a block of 4 waves owns 128 keys of one head, 32 per wave, and walks the query tiles.
-// (82 KB of LDS allow one block per CU, so the waves may use the whole register file)
+// Each lane holds its key's K1, K2 and V rows as MFMA B operands; the gradient accumulators
+// (dK1^T, dK2^T, dV^T of the wave's 32 keys, 128 registers) sit in AGPRs. One wave per SIMD.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(BwdArgs a) {
-    // the wave's own K1 | K2 | V (read as B operands every step) and a ring of query tiles
-    __shared__ __align__(16) unsigned char skv[4][2 * kKTile + kVTile];
-    __shared__ __align__(16) unsigned char sq[kQStages][kQStage];
+    __shared__ __align__(16) unsigned char sq[kQStages * kQStage];
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = tid & 63;
     const int n = lane & 31, h2 = lane >> 5;
-    const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // the first key tiles see the most queries under causal masking: they go first
+    const int kt = blockIdx.y, h = blockIdx.x % a.heads, b = blockIdx.x / a.heads;
     const int k0 = kt * 128, kw0 = k0 + wave * 32, key = kw0 + n;
     const int off = a.seq_k - a.seq_q;
     const float lam = a.lam[h];
     const float c = a.scale_log2;
+    const bool wave_active = kw0 < a.seq_k;
 
+    // B operands of this lane's key (lane n = key, 16-byte chunk 2 kk + h2); keys past the end
+    // read the last key (their weights are masked to zero)
+    bf16x8 kr1[4], kr2[4], vr[8];
     {
-        const int nrows = max(0, min(kBN, a.seq_k - kw0));
-        stage_tile<kD>(skv[wave], (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)h * a.k1s[2] + (int64_t)kw0 * a.k1s[1],
-                       a.k1s[1], nrows, lane, 64);
-        stage_tile<kD>(skv[wave] + kKTile, (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)h * a.k2s[2] + (int64_t)kw0 * a.k2s[1],
-                       a.k2s[1], nrows, lane, 64);
-        stage_tile<kDV>(skv[wave] + 2 * kKTile, (const bf16*)a.v + b * a.vs[0] + (int64_t)h * a.vs[2] + (int64_t)kw0 * a.vs[1],
-                        a.vs[1], nrows, lane, 64);
+        const int kr = min(key, a.seq_k - 1);
+        const bf16* k1p = (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)kr * a.k1s[1] + (int64_t)h * a.k1s[2] + 8 * h2;
+        const bf16* k2p = (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)kr * a.k2s[1] + (int64_t)h * a.k2s[2] + 8 * h2;
+        const bf16* vp = (const bf16*)a.v + b * a.vs[0] + (int64_t)kr * a.vs[1] + (int64_t)h * a.vs[2] + 8 * h2;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            kr1[kk] = ld_global_bf16x8(k1p + 16 * kk);
+            kr2[kk] = ld_global_bf16x8(k2p + 16 * kk);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) vr[kk] = ld_global_bf16x8(vp + 16 * kk);
     }
-    const unsigned char* K1s = skv[wave];
-    const unsigned char* K2s = skv[wave] + kKTile;
-    const unsigned char* Vs = skv[wave] + 2 * kKTile;
 
     f32x16 dk1[2], dk2[2], dv[4];
 #pragma unroll
@@ -349,9 +393,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // query tiles that see any of the block's keys
     const int nqt = (a.seq_q + kBN - 1) / kBN;
-    int qt0 = 0;
-    if (a.causal) qt0 = max(0, (k0 - off) / kBN);
-    const bool wave_active = kw0 < a.seq_k;
+    const int qt0 = a.causal ? max(0, (k0 - off) / kBN) : 0;
     const bf16* q1b = (const bf16*)a.q1 + b * a.q1s[0] + (int64_t)h * a.q1s[2];
     const bf16* q2b = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)h * a.q2s[2];
     const int64_t rowb = ((int64_t)b * a.heads + h) * a.seq_q;
@@ -359,14 +401,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // query-tile DMA: thread tid fills Q1 and Q2 slot tid and go slots tid, tid + 256; wave 0 also
     // fetches the rows' log-sum-exp and D values (64 floats each). Rows past the last query are
     // fetched from the last one (their weights are masked to zero).
-    const uint32_t lds_sq = (uint32_t)(uintptr_t)(lds_u8_t*)&sq[0][0];
-    const int q_row = tid >> 3, q_col = (tid & 7) ^ k_swz<kD>(q_row);
+    const uint32_t lds_sq = (uint32_t)(uintptr_t)(lds_u8_t*)sq;
+    const int q_row = tid >> 3, q_col = (tid & 7) ^ bswz(q_row);
     const int g_row0 = tid >> 4, g_row1 = g_row0 + 16;
     const int g_col0 = v_logical(g_row0, tid & 15), g_col1 = v_logical(g_row1, tid & 15);
-    auto issue_q = [&](int qt) __attribute__((always_inline)) {
+    auto issue_q = [&](int qt, int stage) __attribute__((always_inline)) {
         const int i0 = qt * kBN;
         const int last = min(kBN, a.seq_q - i0) - 1;
-        const uint32_t st = lds_sq + (qt % kQStages) * kQStage + wave * 1024;
+        const uint32_t st = lds_sq + stage * kQStage + wave * 1024;
         const int qr = min(q_row, last);
         dma16(q1b + (int64_t)i0 * a.q1s[1], (uint32_t)(qr * a.q1s[1] + q_col * 8) * 2u, st);
         dma16(q2b + (int64_t)i0 * a.q2s[1], (uint32_t)(qr * a.q2s[1] + q_col * 8) * 2u, st + kKTile);
@@ -375,16 +417,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dma16(gb, (uint32_t)(min(g_row1, last) * kDV + g_col1 * 8) * 2u, st + 2 * kKTile + 4096);
         if (wave == 0) {
             // lane i fetches float i of the tile's 32 rows x 2 (clamped to the last row)
-            const uint32_t sst = lds_sq + (qt % kQStages) * kQStage + kQStats;
+            const uint32_t sst = lds_sq + stage * kQStage + kQStats;
             const uint32_t fo = (uint32_t)min(lane, 2 * last + 1) * 4u;
             dma4(a.lse + 2 * (rowb + i0), fo, sst);
             dma4(a.dd + 2 * (rowb + i0), fo, sst + 256);
         }
     };
 
-    for (int qt = qt0; qt < nqt && qt < qt0 + kQStages - 1; ++qt) issue_q(qt);
-    for (int qt = qt0; qt < nqt; ++qt) {
-        const int i0 = qt * kBN;
+    // one query tile; !full: some (query, key) pair of the wave's 32 x 32 block is not visible
+    auto compute = [&](auto ST, bool full, int i0) __attribute__((always_inline)) {
+        const unsigned char* Q1s = sq + decltype(ST)::value * kQStage;
+        const unsigned char* Q2s = Q1s + kKTile;
+        const unsigned char* Gs = Q1s + 2 * kKTile;
+        const float* svl = (const float*)(Q1s + kQStats);   // lse [32][2]
+        const float* svd = svl + 64;                          // dd [32][2]
+        // dP = go V^T, S_k = Q_k K_k^T (rows = queries, lane = key)
+        f32x16 dp = f32x16{}, s1 = f32x16{}, s2 = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Gs + rowop_v(n, kk, h2)), vr[kk], dp);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            s1 = mfma32x32x16(lds16(Q1s + rowop_b(n, kk, h2)), kr1[kk], s1);
+            s2 = mfma32x32x16(lds16(Q2s + rowop_b(n, kk, h2)), kr2[kk], s2);
+        }
+        // register r holds query row 8 (r / 4) + 4 h2 + r % 4
+        f32x16 p1, p2, dm1, dm2, ds1, ds2, pc;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            // rows 8g + 4h2 .. +3: their (map 1, map 2) pairs are 8 consecutive floats
+            const int q4 = 8 * g + 4 * h2;
+            const f32x4 l01 = *(const f32x4*)(svl + 2 * q4), l23 = *(const f32x4*)(svl + 2 * q4 + 4);
+            const f32x4 d01 = *(const f32x4*)(svd + 2 * q4), d23 = *(const f32x4*)(svd + 2 * q4 + 4);
+            const float lse1[4] = {l01[0], l01[2], l23[0], l23[2]}, lse2[4] = {l01[1], l01[3], l23[1], l23[3]};
+            const float dd1[4] = {d01[0], d01[2], d23[0], d23[2]}, dd2[4] = {d01[1], d01[3], d23[1], d23[3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g + j;
+                p1[r] = fast_exp2(fmaf(s1[r], c, -lse1[j]));
+                p2[r] = fast_exp2(fmaf(s2[r], c, -lse2[j]));
+                dm1[r] = dp[r] - dd1[j];
+                dm2[r] = dp[r] - dd2[j];
+            }
+        }
+        if (!full) {
+            asm volatile("");   // keeps this a branch: full tiles skip the test
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int q = i0 + (r >> 2) * 8 + 4 * h2 + (r & 3);
+                const bool vis = q < a.seq_q && key < a.seq_k && (!a.causal || key <= q + off);
+                p1[r] = vis ? p1[r] : 0.f;
+                p2[r] = vis ? p2[r] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            ds1[r] = p1[r] * dm1[r];
+            ds2[r] = -lam * p2[r] * dm2[r];
+            pc[r] = fmaf(-lam, p2[r], p1[r]);
+        }
+        // dK_k^T += Q_k^T dS_k and dV^T += go^T (A1 - lambda A2) (k index = queries)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 b1 = c_to_b(ds1, kb), b2 = c_to_b(ds2, kb), bp = c_to_b(pc, kb);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                mfma_agpr(dk1[mt], tr_pair(Q1s, trop_b(lane, kb, mt, 0), trop_b(lane, kb, mt, 1)), b1);
+                mfma_agpr(dk2[mt], tr_pair(Q2s, trop_b(lane, kb, mt, 0), trop_b(lane, kb, mt, 1)), b2);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                mfma_agpr(dv[ct], tr_pair(Gs, trop_v(lane, kb, ct, 0), trop_v(lane, kb, ct, 1)), bp);
+        }
+    };
+    auto tile = [&](auto ST, int qt) __attribute__((always_inline)) {
+        constexpr int st = decltype(ST)::value;
         // this thread's DMA of tile qt has landed (the next tile's loads may be in flight)
         if (qt + 1 < nqt) {
             if (wave == 0) __builtin_amdgcn_s_waitcnt(kVmcnt[6]);
@@ -393,69 +499,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
         }
         __syncthreads();   // every thread's loads of tile qt landed; the stage of tile qt-1 is free
-        if (qt + kQStages - 1 < nqt) issue_q(qt + kQStages - 1);
-        const unsigned char* stq = &sq[qt % kQStages][0];
-        const float* svl = (const float*)(stq + kQStats);          // lse [32][2]
-        const float* svd = (const float*)(stq + kQStats + 256);    // dd [32][2]
+        if (qt + kQStages - 1 < nqt) issue_q(qt + kQStages - 1, (st + kQStages - 1) % kQStages);
+        const int i0 = qt * kBN;
         // skip the tile if it ends before this wave's first key (causal)
-        if (!wave_active || (a.causal && i0 + kBN - 1 + off < kw0)) continue;
-        const unsigned char* Q1s = stq;
-        const unsigned char* Q2s = stq + kKTile;
-        const unsigned char* Gs = stq + 2 * kKTile;
-        // dP = go V^T (rows = queries, lane = key n)
-        f32x16 dp = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Gs + rowop_v(n, kk, h2)), lds16(Vs + rowop_v(n, kk, h2)), dp);
-        // per-register query index: 8 (r / 4) + 4 h2 + r % 4
-        f32x16 pc = f32x16{};
-#pragma unroll
-        for (int map = 0; map < 2; ++map) {
-            const unsigned char* Qs = map == 0 ? Q1s : Q2s;
-            const unsigned char* Ks = map == 0 ? K1s : K2s;
-            f32x16 s = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) s = mfma32x32x16(lds16(Qs + rowop_k(n, kk, h2)), lds16(Ks + rowop_k(n, kk, h2)), s);
-            const float coef = map == 0 ? 1.f : -lam;
-            f32x16 ds;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // rows 8g + 4h2 .. +3: their (map 1, map 2) pairs are 8 consecutive floats
-                const int q4 = 8 * g + 4 * h2;
-                const f32x4 l01 = *(const f32x4*)(svl + 2 * q4), l23 = *(const f32x4*)(svl + 2 * q4 + 4);
-                const f32x4 d01 = *(const f32x4*)(svd + 2 * q4), d23 = *(const f32x4*)(svd + 2 * q4 + 4);
-                const float lse[4] = {l01[map], l01[2 + map], l23[map], l23[2 + map]};
-                const float dd[4] = {d01[map], d01[2 + map], d23[map], d23[2 + map]};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * g + j;
-                    const int q = i0 + q4 + j;
-                    const bool vis = q < a.seq_q && key < a.seq_k && (!a.causal || key <= q + off);
-                    const float p = vis ? fast_exp2(fmaf(s[r], c, -lse[j])) : 0.f;
-                    ds[r] = coef * p * (dp[r] - dd[j]);
-                    pc[r] = fmaf(coef, p, pc[r]);
-                }
-            }
-            // dK_k^T += Q_k^T dS_k (k index = queries)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 bds = c_to_b(ds, kb);
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const bf16x8 qa = tr_pair(Qs, trop_k(lane, kb, mt, 0), trop_k(lane, kb, mt, 1));
-                    if (map == 0) dk1[mt] = mfma32x32x16(qa, bds, dk1[mt]);
-                    else dk2[mt] = mfma32x32x16(qa, bds, dk2[mt]);
-                }
-            }
-        }
-        // dV^T += go^T (A1 - lambda A2)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 bp = c_to_b(pc, kb);
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                dv[ct] = mfma32x32x16(tr_pair(Gs, trop_v(lane, kb, ct, 0), trop_v(lane, kb, ct, 1)), bp, dv[ct]);
-        }
+        if (!wave_active || (a.causal && i0 + kBN - 1 + off < kw0)) return;
+        compute(ST, i0 + kBN <= a.seq_q && kw0 + kBN <= a.seq_k && (!a.causal || kw0 + kBN - 1 <= i0 + off), i0);
+    };
+    // ring position = (tile - first tile) modulo 3; the loop is unrolled by 3 so that every LDS
+    // address is a register plus a constant
+    for (int qt = qt0; qt < nqt && qt < qt0 + kQStages - 1; ++qt) issue_q(qt, qt - qt0);
+    // the key operands and the first tiles have landed: from here on the compiler sees no
+    // outstanding loads of its own and adds no waits on the query-tile DMA
+    __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+    for (int qt = qt0; qt < nqt; qt += kQStages) {
+        tile(IC<0>{}, qt);
+        if (qt + 1 < nqt) tile(IC<1>{}, qt + 1);
+        if (qt + 2 < nqt) tile(IC<2>{}, qt + 2);
     }
+    agpr_drain(dk1[0], dk1[1], dk2[0], dk2[1]);
+    agpr_drain(dv[0], dv[1], dv[2], dv[3]);
     if (key >= a.seq_k) return;
     bf16* k1p = (bf16*)a.dk1 + b * a.dk1s[0] + (int64_t)key * a.dk1s[1] + (int64_t)h * a.dk1s[2];
     bf16* k2p = (bf16*)a.dk2 + b * a.dk2s[0] + (int64_t)key * a.dk2s[1] + (int64_t)h * a.dk2s[2];
@@ -535,9 +597,9 @@ hipError_t launch_bwd(BwdArgs a, void* workspace, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_pre_kernel, dim3(pre_blocks, a.heads, a.batch), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((a.seq_q + 127) / 128, a.heads, a.batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(a.heads * a.batch, (a.seq_q + 127) / 128), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((a.seq_k + 127) / 128, a.heads, a.batch), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.heads * a.batch, (a.seq_k + 127) / 128), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int nred = a.heads + ((a.epi && a.dnorm_w) ? kDV : 0);
     if (a.dlam || a.dnorm_w) {
