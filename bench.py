@@ -34,6 +34,7 @@ FLOP_PER_PAIR_V2 = 512
 # backward: recomputed scores (2 x 2d), dP = go V^T (2 dv), dV (2 dv), dK and dQ of both maps
 # (2 x 2d each): 1280 per visible pair at d = 64, dv = 128
 FLOP_PER_PAIR_V1_BWD = 1280
+PAGE_SIZE = 256                # tokens per page of the paged decode legs
 DECODE_BYTES_PER_TOKEN = 2 * (64 + 64 + 128)
 
 
@@ -245,7 +246,21 @@ def main():
                                       "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                                       "traffic": load_traffic("v1_decode_64k", ["decode.hip", "common.hpp"])}
         log(f"[bench]   {avg:.3f} ms -> {gbs:.0f} GB/s")
-        del x4, ws, o4
+        # the same cache in 256-token pages of a shared pool, in a random page order
+        (p1, p2, pv), table = W.scatter_to_pages((x4["k1"], x4["k2"], x4["v"]), PAGE_SIZE, seed=c4.seed + 50)
+        del x4["k1"], x4["k2"], x4["v"]
+        fp = lambda: da.diffattn_decode_paged(x4["q1"], x4["q2"], p1, p2, pv, table, lam4, max_len=c4.L,
+                                              epilogue=True, lambda_init_value=c4.lambda_init, workspace=ws, out=o4)
+        fp()
+        torch.cuda.synchronize()
+        avg, mn = time_launches(fp, args.secondary_reps, torch)
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        secondary["v1_decode_64k_paged"] = {"workload": c4.name + f", {PAGE_SIZE}-token pages",
+                                            "split_plus_reduce_avg_ms": round(avg, 4), "min_ms": round(mn, 4),
+                                            "bytes": nbytes, "GB/s": round(gbs, 1),
+                                            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench]   paged: {avg:.3f} ms -> {gbs:.0f} GB/s")
+        del x4, ws, o4, p1, p2, pv, table
     if "bwd" in which:
         # training step of the main workload: the training forward and the backward pass
         c7 = W.V1_PREFILL_2K
@@ -295,7 +310,20 @@ def main():
                                       "traffic": load_traffic("v2_decode_64k", ["decode_v2.hip", "mfma_tile.hpp",
                                                                                 "common.hpp"])}
         log(f"[bench]   {avg:.3f} ms -> {gbs:.0f} GB/s")
-        del x6, ws6, o6
+        (pk6, pv6), table6 = W.scatter_to_pages((x6["k"], x6["v"]), PAGE_SIZE, seed=c6.seed + 50)
+        del x6["k"], x6["v"]
+        fp6 = lambda: da.diffattn_v2_decode_paged(x6["q"], pk6, pv6, table6, lam6, max_len=c6.L, workspace=ws6,
+                                                  out=o6)
+        fp6()
+        torch.cuda.synchronize()
+        avg, mn = time_launches(fp6, args.secondary_reps, torch)
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        secondary["v2_decode_64k_paged"] = {"workload": c6.name + f", {PAGE_SIZE}-token pages",
+                                            "split_plus_reduce_avg_ms": round(avg, 4), "min_ms": round(mn, 4),
+                                            "bytes": nbytes, "GB/s": round(gbs, 1),
+                                            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench]   paged: {avg:.3f} ms -> {gbs:.0f} GB/s")
+        del x6, ws6, o6, pk6, pv6, table6
     if secondary:
         result["secondary"] = secondary
 

@@ -36,7 +36,8 @@ EPI_RMSNORM_SCALE = 1
 EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "diffattn_lambda",
             "diffattn_fwd", "diffattn_decode_workspace_size", "diffattn_decode", "diffattn_v2_fwd",
             "diffattn_v2_decode_workspace_size", "diffattn_v2_decode", "diffattn_fwd_train",
-            "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd")
+            "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd", "diffattn_decode_paged",
+            "diffattn_v2_decode_paged")
 
 
 class DiffAttnError(RuntimeError):
@@ -92,6 +93,12 @@ def lib():
         L.diffattn_v2_decode_workspace_size.argtypes = [i, i, i, i]
         L.diffattn_v2_decode.restype = i
         L.diffattn_v2_decode.argtypes = [i, T, T, T, vp, vp, i, i, i, i, i, f, T, vp, sz, vp]
+        i64 = ctypes.c_int64
+        L.diffattn_decode_paged.restype = i
+        L.diffattn_decode_paged.argtypes = [i, T, T, T, T, T, vp, i64, i, i, vp, i, i, i, i, i, vp, f, i, vp, f,
+                                            f, T, vp, sz, vp]
+        L.diffattn_v2_decode_paged.restype = i
+        L.diffattn_v2_decode_paged.argtypes = [i, T, T, T, vp, i64, i, i, vp, vp, i, i, i, i, i, f, T, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -298,6 +305,76 @@ def diffattn_v2_decode(q, kc, vc, lam: torch.Tensor, cache_lens: torch.Tensor | 
     _check(lib().diffattn_v2_decode(_dtype_code(q), _t4(q), _t4(kc), _t4(vc), _ptr(cache_lens), lam.data_ptr(),
                                     B, h, hkv, L, d, float(scale), _t4(out), workspace.data_ptr(),
                                     workspace.numel(), _stream(q.device)))
+    return out.squeeze(1)
+
+
+def _check_table(block_table: torch.Tensor, cache_lens):
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be an int32 [batch, pages_per_seq] tensor with unit column stride")
+    if cache_lens is not None and cache_lens.dtype != torch.int32:
+        raise ValueError("cache_lens must be int32")
+
+
+def diffattn_decode_paged(q1, q2, k1_pages, k2_pages, v_pages, block_table: torch.Tensor, lam: torch.Tensor,
+                          cache_lens: torch.Tensor | None = None, max_len: int | None = None,
+                          epilogue: bool = True, lambda_init_value: float = 0.8,
+                          norm_w: torch.Tensor | None = None, eps: float = 1e-5, scale: float = 0.0,
+                          workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """DIFF V1 decode against a paged cache. q1, q2: [B, H, d] (or [B, 1, H, d]); page pools
+    k1_pages, k2_pages: [P, page_size, H, d], v_pages: [P, page_size, H, dv]; block_table: int32
+    [B, pages_per_seq] on the device; cache_lens: int32 [B] on the device or None (every length
+    max_len). max_len defaults to pages_per_seq * page_size. Returns [B, H, dv]."""
+    if q1.dim() == 3:
+        q1, q2 = q1.unsqueeze(1), q2.unsqueeze(1)
+    _check_table(block_table, cache_lens)
+    B, _, H, d = q1.shape
+    P, page, dv = k1_pages.shape[0], k1_pages.shape[1], v_pages.shape[3]
+    L = int(max_len) if max_len is not None else block_table.shape[1] * page
+    if out is None:
+        out = torch.empty((B, 1, H, dv), dtype=q1.dtype, device=q1.device)
+    elif out.dim() == 3:
+        out = out.unsqueeze(1)
+    need = diffattn_decode_workspace_size(B, H, L, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q1.device)
+    _check(lib().diffattn_decode_paged(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1_pages), _t4(k2_pages),
+                                       _t4(v_pages), block_table.data_ptr(), block_table.stride(0), P, page,
+                                       _ptr(cache_lens), B, H, L, d, dv, lam.data_ptr(), float(lambda_init_value),
+                                       EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
+                                       float(scale), _t4(out), workspace.data_ptr(), workspace.numel(),
+                                       _stream(q1.device)))
+    return out.squeeze(1)
+
+
+def diffattn_v2_decode_paged(q, k_pages, v_pages, block_table: torch.Tensor, lam: torch.Tensor,
+                             cache_lens: torch.Tensor | None = None, max_len: int | None = None,
+                             scale: float = 0.0, workspace: torch.Tensor | None = None,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """DIFF V2 decode against a paged cache. q: [B, 2h, d] (or [B, 1, 2h, d]); page pools
+    k_pages, v_pages: [P, page_size, h_kv, d]; block_table, cache_lens, max_len as in
+    diffattn_decode_paged; lam: fp32 [B, h] contiguous. Returns [B, h, d]."""
+    if q.dim() == 3:
+        q = q.unsqueeze(1)
+    _check_table(block_table, cache_lens)
+    B, _, H2, d = q.shape
+    P, page, hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    h = H2 // 2
+    if H2 % 2:
+        raise ValueError("q must hold an even number of heads (2h)")
+    if not (lam.is_contiguous() and lam.dtype == torch.float32 and tuple(lam.shape) == (B, h)):
+        raise ValueError("lam must be a contiguous float32 [B, h] tensor")
+    L = int(max_len) if max_len is not None else block_table.shape[1] * page
+    if out is None:
+        out = torch.empty((B, 1, h, d), dtype=q.dtype, device=q.device)
+    elif out.dim() == 3:
+        out = out.unsqueeze(1)
+    need = diffattn_v2_decode_workspace_size(B, h, hkv, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().diffattn_v2_decode_paged(_dtype_code(q), _t4(q), _t4(k_pages), _t4(v_pages),
+                                          block_table.data_ptr(), block_table.stride(0), P, page,
+                                          _ptr(cache_lens), lam.data_ptr(), B, h, hkv, L, d, float(scale), _t4(out),
+                                          workspace.data_ptr(), workspace.numel(), _stream(q.device)))
     return out.squeeze(1)
 
 

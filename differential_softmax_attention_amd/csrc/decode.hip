@@ -57,9 +57,12 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
             q2[2 * j + 1] = bf_hi(w2[j]) * a.scale_log2;
         }
     }
-    const bf16* k1b = (const bf16*)a.k1 + b * a.k1s[0] + (int64_t)h * a.k1s[2] + 8 * g;
-    const bf16* k2b = (const bf16*)a.k2 + b * a.k2s[0] + (int64_t)h * a.k2s[2] + 8 * g;
-    const bf16* vb = (const bf16*)a.v + b * a.vs[0] + (int64_t)h * a.vs[2] + 16 * g;
+    // contiguous cache: batch b's rows; paged: the pool (the batch stride is the page stride)
+    const bool paged = a.pc.block_table != nullptr;
+    const int64_t bsel = paged ? 0 : b;
+    const bf16* k1b = (const bf16*)a.k1 + bsel * a.k1s[0] + (int64_t)h * a.k1s[2] + 8 * g;
+    const bf16* k2b = (const bf16*)a.k2 + bsel * a.k2s[0] + (int64_t)h * a.k2s[2] + 8 * g;
+    const bf16* vb = (const bf16*)a.v + bsel * a.vs[0] + (int64_t)h * a.vs[2] + 16 * g;
 
     const int x1 = (lane ^ 1) << 2, x2 = (lane ^ 2) << 2, x4 = (lane ^ 4) << 2;
 
@@ -72,14 +75,29 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(DecodeArgs 
     for (int t0 = ks; t0 < ke; t0 += kStep) {
         u32x4 rk1[kUnroll], rk2[kUnroll], rv0[kUnroll], rv1[kUnroll];
         bool valid[kUnroll];
+        // this wave's 32 tokens start at tw (a multiple of 32, so they share one page); tokens
+        // past the slice end load row tb instead (a valid row of the same page) and are dropped
+        const int tw = t0 + wave * 8 * kUnroll;
+        const int tb = tw < ke ? tw : ks;
+        const bf16 *k1w, *k2w, *vw;   // row of token tb
+        if (paged) {
+            const int64_t pg = a.pc.page(b, tb), in = tb % a.pc.page_size;
+            k1w = k1b + pg * a.k1s[0] + in * a.k1s[1];
+            k2w = k2b + pg * a.k2s[0] + in * a.k2s[1];
+            vw = vb + pg * a.vs[0] + in * a.vs[1];
+        } else {
+            k1w = k1b + (int64_t)tb * a.k1s[1];
+            k2w = k2b + (int64_t)tb * a.k2s[1];
+            vw = vb + (int64_t)tb * a.vs[1];
+        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int t = t0 + wave * 8 * kUnroll + u * 8 + kg;
+            const int t = tw + u * 8 + kg;
             valid[u] = t < ke;
-            const int tt = valid[u] ? t : ks;   // clamp: load a valid row, discard it below
-            rk1[u] = *(const u32x4*)(k1b + (int64_t)tt * a.k1s[1]);
-            rk2[u] = *(const u32x4*)(k2b + (int64_t)tt * a.k2s[1]);
-            const bf16* vr = vb + (int64_t)tt * a.vs[1];
+            const int64_t dt = valid[u] ? t - tb : 0;
+            rk1[u] = *(const u32x4*)(k1w + dt * a.k1s[1]);
+            rk2[u] = *(const u32x4*)(k2w + dt * a.k2s[1]);
+            const bf16* vr = vw + dt * a.vs[1];
             rv0[u] = *(const u32x4*)(vr);
             rv1[u] = *(const u32x4*)(vr + 8);
         }

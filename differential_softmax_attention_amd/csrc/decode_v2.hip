@@ -66,14 +66,44 @@ __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
     }
 
     // ---- tile DMA: lane i fills K slots i + 64j and V slots i + 64j (j < 8) of a stage
-    const bf16* kbase = (const bf16*)a.k + b * a.kcs[0] + (int64_t)g * a.kcs[2] + (int64_t)ks * a.kcs[1];
-    const bf16* vbase = (const bf16*)a.v + b * a.vcs[0] + (int64_t)g * a.vcs[2] + (int64_t)ks * a.vcs[1];
+    // contiguous cache: batch b's rows; paged: the pool (the batch stride is the page stride), a
+    // tile of 32 keys starting at a multiple of 32 lying in one page
+    const bool paged = a.pc.block_table != nullptr;
+    const bf16* kbase = (const bf16*)a.k + (int64_t)g * a.kcs[2];
+    const bf16* vbase = (const bf16*)a.v + (int64_t)g * a.vcs[2];
+    if (!paged) {
+        kbase += b * a.kcs[0] + (int64_t)ks * a.kcs[1];
+        vbase += b * a.vcs[0] + (int64_t)ks * a.vcs[1];
+    }
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
+    // paged: the slice's page indices, 64 at a time, one per lane (lane i holds page slot
+    // 64 w + i of the slice), so that a tile's lookup is a lane read rather than a memory load
+    // with its latency in front of the tile's DMA
+    const int first_slot = paged ? ks / a.pc.page_size : 0;
+    int win = -1, pvec = 0;
+    auto page_of = [&](int t0) __attribute__((always_inline)) -> int64_t {
+        const int slot = t0 / a.pc.page_size - first_slot;
+        if ((slot >> 6) != win) {
+            win = slot >> 6;
+            const int sl = first_slot + win * 64 + lane;
+            const int p = sl <= (ke - 1) / a.pc.page_size ? a.pc.block_table[(int64_t)b * a.pc.bt_stride + sl] : 0;
+            pvec = min(max(p, 0), a.pc.num_pages - 1);
+        }
+        return (int64_t)__builtin_amdgcn_readlane(pvec, slot & 63);
+    };
     auto issue_tile = [&](int t) __attribute__((always_inline)) {
         const uint32_t st = lds0 + (t % kStages) * kStageBytes;
         const int last = min(kBN, ke - ks - t * kBN) - 1;   // last valid row of this tile
-        const bf16* kb = kbase + (int64_t)t * kBN * a.kcs[1];
-        const bf16* vb = vbase + (int64_t)t * kBN * a.vcs[1];
+        const bf16 *kb, *vb;
+        if (paged) {
+            const int t0 = ks + t * kBN;
+            const int64_t pg = page_of(t0), in = t0 % a.pc.page_size;
+            kb = kbase + pg * a.kcs[0] + in * a.kcs[1];
+            vb = vbase + pg * a.vcs[0] + in * a.vcs[1];
+        } else {
+            kb = kbase + (int64_t)t * kBN * a.kcs[1];
+            vb = vbase + (int64_t)t * kBN * a.vcs[1];
+        }
 #pragma unroll
         for (int j = 0; j < kLoadsK; ++j) {
             const int s = lane + 64 * j;

@@ -157,11 +157,27 @@ size_t diffattn_decode_workspace_size(int batch, int heads, int cache_len, int d
     return diffattn::decode_workspace_bytes(batch, heads, cache_len, dv);
 }
 
-diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1c,
-                                diffattn_tensor k2c, diffattn_tensor vc, const int32_t* cache_lens, int batch,
-                                int heads, int cache_len, int d, int dv, const float* lambda, float lambda_init,
-                                diffattn_epilogue epi, const float* norm_w, float eps, float scale,
-                                diffattn_tensor out, void* workspace, size_t workspace_bytes, void* stream) {
+// Page-table arguments: non-null table, page size a positive multiple of 32, a table row long
+// enough for cache_len tokens.
+static diffattn_status check_pages(const int32_t* block_table, int64_t bt_stride, int num_pages, int page_size,
+                                   int cache_len, const char* fn) {
+    if (!block_table) return fail(DIFFATTN_ERR_ARG, "%s: block_table is null", fn);
+    if (page_size < 32 || page_size % 32 != 0)
+        return fail(DIFFATTN_ERR_ARG, "%s: page_size=%d must be a positive multiple of 32", fn, page_size);
+    if (num_pages < 1) return fail(DIFFATTN_ERR_ARG, "%s: num_pages=%d must be >= 1", fn, num_pages);
+    if (cache_len >= 1 && bt_stride < (cache_len + page_size - 1) / page_size)
+        return fail(DIFFATTN_ERR_ARG, "%s: bt_stride=%lld holds fewer than the %d pages of max_len=%d tokens", fn,
+                    (long long)bt_stride, (cache_len + page_size - 1) / page_size, cache_len);
+    return DIFFATTN_OK;
+}
+
+static diffattn_status decode_impl(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1c,
+                                   diffattn_tensor k2c, diffattn_tensor vc, const int32_t* cache_lens, int batch,
+                                   int heads, int cache_len, int d, int dv, const float* lambda, float lambda_init,
+                                   diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                                   diffattn_tensor out, void* workspace, size_t workspace_bytes, void* stream,
+                                   const diffattn::PagedCache& pc) {
+    const char* fn_name = pc.block_table ? "diffattn_decode_paged" : "diffattn_decode";
     if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_decode: unknown dtype %d", (int)dtype);
     const diffattn_tensor* ts[6] = {&q1, &q2, &k1c, &k2c, &vc, &out};
     const char* names[6] = {"q1", "q2", "k1c", "k2c", "vc", "out"};
@@ -189,12 +205,16 @@ diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffat
 
     const bool split = dtype == DIFFATTN_BF16 && d == 64 && dv == 128 && vec16_ok(q1) && vec16_ok(q2) &&
                        vec16_ok(k1c) && vec16_ok(k2c) && vec16_ok(vc);
+    if (pc.block_table && !split)
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "%s: a paged cache needs bf16, d=64, dv=128 and 16-byte aligned tensors",
+                    fn_name);
     if (split) {
         diffattn::DecodeArgs a{};
         a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1c.ptr; a.k2 = k2c.ptr; a.v = vc.ptr; a.out = out.ptr;
         copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1c); copy_strides(a.k2s, k2c);
         copy_strides(a.vs, vc); copy_strides(a.os, out);
         a.cache_lens = cache_lens;
+        a.pc = pc;
         a.lam = lambda;
         a.norm_w = norm_w;
         a.ws = (float*)workspace;
@@ -217,6 +237,29 @@ diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffat
     a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
     a.norm_w = norm_w; a.eps = eps; a.lambda_init = lambda_init; a.scale = sc;
     return hip_status(diffattn::launch_generic(a, batch, heads, dtype == DIFFATTN_BF16, st), "diffattn_decode launch");
+}
+
+diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1c,
+                                diffattn_tensor k2c, diffattn_tensor vc, const int32_t* cache_lens, int batch,
+                                int heads, int cache_len, int d, int dv, const float* lambda, float lambda_init,
+                                diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                                diffattn_tensor out, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(dtype, q1, q2, k1c, k2c, vc, cache_lens, batch, heads, cache_len, d, dv, lambda, lambda_init,
+                       epi, norm_w, eps, scale, out, workspace, workspace_bytes, stream, diffattn::PagedCache{});
+}
+
+diffattn_status diffattn_decode_paged(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,
+                                      diffattn_tensor k1_pages, diffattn_tensor k2_pages, diffattn_tensor v_pages,
+                                      const int32_t* block_table, int64_t bt_stride, int num_pages, int page_size,
+                                      const int32_t* cache_lens, int batch, int heads, int max_len, int d, int dv,
+                                      const float* lambda, float lambda_init, diffattn_epilogue epi,
+                                      const float* norm_w, float eps, float scale, diffattn_tensor out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (diffattn_status s = check_pages(block_table, bt_stride, num_pages, page_size, max_len, "diffattn_decode_paged"))
+        return s;
+    diffattn::PagedCache pc{block_table, bt_stride, page_size, num_pages};
+    return decode_impl(dtype, q1, q2, k1_pages, k2_pages, v_pages, cache_lens, batch, heads, max_len, d, dv, lambda,
+                       lambda_init, epi, norm_w, eps, scale, out, workspace, workspace_bytes, stream, pc);
 }
 
 diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k, diffattn_tensor v,
@@ -282,10 +325,10 @@ size_t diffattn_v2_decode_workspace_size(int batch, int h, int h_kv, int cache_l
     return diffattn::v2_decode_workspace_bytes(batch, h, h_kv, cache_len);
 }
 
-diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor kc, diffattn_tensor vc,
-                                   const int32_t* cache_lens, const float* lam, int batch, int h, int h_kv,
-                                   int cache_len, int d, float scale, diffattn_tensor out, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+static diffattn_status v2_decode_impl(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor kc, diffattn_tensor vc,
+                                      const int32_t* cache_lens, const float* lam, int batch, int h, int h_kv,
+                                      int cache_len, int d, float scale, diffattn_tensor out, void* workspace,
+                                      size_t workspace_bytes, void* stream, const diffattn::PagedCache& pc) {
     if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: unknown dtype %d", (int)dtype);
     const diffattn_tensor* ts[4] = {&q, &kc, &vc, &out};
     const char* names[4] = {"q", "kc", "vc", "out"};
@@ -315,11 +358,16 @@ diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diff
 
     const bool split = dtype == DIFFATTN_BF16 && d == 128 && diffattn::v2_decode_group_ok(group) && vec16_ok(q) &&
                        vec16_ok(kc) && vec16_ok(vc);
+    if (pc.block_table && !split)
+        return fail(DIFFATTN_ERR_UNSUPPORTED,
+                    "diffattn_v2_decode_paged: a paged cache needs bf16, d=128, a group of 2..32 query heads and "
+                    "16-byte aligned tensors");
     if (split) {
         diffattn::V2DecodeArgs a{};
         a.q = q.ptr; a.k = kc.ptr; a.v = vc.ptr; a.out = out.ptr;
         copy_strides(a.qs, q); copy_strides(a.kcs, kc); copy_strides(a.vcs, vc); copy_strides(a.os, out);
         a.cache_lens = cache_lens;
+        a.pc = pc;
         a.lam = lam;
         a.lam_bs = h;
         a.ws = (float*)workspace;
@@ -340,6 +388,27 @@ diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diff
     a.epi = 0;
     a.norm_w = nullptr; a.eps = 0.f; a.lambda_init = 0.f; a.scale = sc;
     return hip_status(diffattn::launch_generic(a, batch, h, dtype == DIFFATTN_BF16, st), "diffattn_v2_decode launch");
+}
+
+diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor kc, diffattn_tensor vc,
+                                   const int32_t* cache_lens, const float* lam, int batch, int h, int h_kv,
+                                   int cache_len, int d, float scale, diffattn_tensor out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    return v2_decode_impl(dtype, q, kc, vc, cache_lens, lam, batch, h, h_kv, cache_len, d, scale, out, workspace,
+                          workspace_bytes, stream, diffattn::PagedCache{});
+}
+
+diffattn_status diffattn_v2_decode_paged(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k_pages,
+                                         diffattn_tensor v_pages, const int32_t* block_table, int64_t bt_stride,
+                                         int num_pages, int page_size, const int32_t* cache_lens, const float* lam,
+                                         int batch, int h, int h_kv, int max_len, int d, float scale,
+                                         diffattn_tensor out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (diffattn_status s =
+            check_pages(block_table, bt_stride, num_pages, page_size, max_len, "diffattn_v2_decode_paged"))
+        return s;
+    diffattn::PagedCache pc{block_table, bt_stride, page_size, num_pages};
+    return v2_decode_impl(dtype, q, k_pages, v_pages, cache_lens, lam, batch, h, h_kv, max_len, d, scale, out,
+                          workspace, workspace_bytes, stream, pc);
 }
 
 diffattn_status diffattn_fwd_train(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,

@@ -54,6 +54,21 @@ hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
 
 // Split-K decode (bf16, d = 64, dv = 128).
+// Paged KV cache (block_table non-null): each cache tensor is a pool of pages whose batch stride
+// is the page stride; token t of sequence b is row t % page_size of page
+// block_table[b * bt_stride + t / page_size] (clamped into 0..num_pages-1). page_size is a
+// multiple of 32, so a 32-token run that starts at a multiple of 32 lies in one page.
+struct PagedCache {
+    const int32_t* block_table;
+    int64_t bt_stride;
+    int page_size, num_pages;
+    // page of token t of sequence b
+    __device__ __forceinline__ int64_t page(int b, int t) const {
+        const int p = block_table[(int64_t)b * bt_stride + t / page_size];
+        return (int64_t)min(max(p, 0), num_pages - 1);
+    }
+};
+
 struct DecodeArgs {
     const void *q1, *q2, *k1, *k2, *v;
     void* out;
@@ -62,6 +77,7 @@ struct DecodeArgs {
     const float* lam;
     const float* norm_w;
     float* ws;  // workspace: partials
+    PagedCache pc;
     int batch, heads, cache_len, n_splits, split_len;
     int epi;
     float eps, lambda_init, scale_log2;
@@ -81,6 +97,7 @@ struct V2DecodeArgs {
     const float* lam;
     int64_t lam_bs;
     float* ws;  // workspace: per-slice partials
+    PagedCache pc;
     int batch, h, h_kv, group, cache_len, n_splits, split_len;
     float scale_log2;
 };

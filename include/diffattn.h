@@ -146,6 +146,37 @@ diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffat
                                 void* stream);
 
 /*
+ * DIFF V1 decode against a paged KV cache: the same operation as diffattn_decode, with the cache
+ * of each sequence held in fixed-size pages of shared pools, listed by a block table.
+ *  k1_pages, k2_pages: [num_pages, page_size, heads, d];  v_pages: [num_pages, page_size, heads, dv]
+ *     as strided views whose s_batch is the page stride (s_seq: token stride within a page).
+ *  block_table: DEVICE int32 [batch, bt_stride]; token t of sequence b is row t % page_size of page
+ *     block_table[b * bt_stride + t / page_size]. Entries for the pages of tokens 0..len_b-1 must be
+ *     page indices below num_pages (an entry outside 0..num_pages-1 is clamped into it on the
+ *     device); entries past them are not read.
+ *  page_size: tokens per page, a positive multiple of 32 (a 32-token run of the kernels' tiles
+ *     never straddles two pages).
+ *  cache_lens: DEVICE int32 [batch] (each clamped into 1..max_len on the device), or NULL (every
+ *     len = max_len).  max_len: the largest length; it sizes the split-K slices and the workspace
+ *     (diffattn_decode_workspace_size(batch, heads, max_len, dv)), and bt_stride must hold
+ *     ceil(max_len / page_size) entries.
+ *  Other arguments as in diffattn_decode. Read traffic is the same as the contiguous decode's: each
+ *  cached row once, plus one table entry per 32 tokens.
+ *  Kernels: the split-K kernel of diffattn_decode, with a page lookup per 32-token run; bf16,
+ *  d = 64, dv = 128 and 16-byte aligned views only.
+ *  Errors: ERR_ARG (as diffattn_decode, and a null table, page_size not a multiple of 32, num_pages
+ *  < 1, bt_stride too short), ERR_WORKSPACE, ERR_UNSUPPORTED (other dtypes, shapes or alignments),
+ *  ERR_HIP.
+ */
+diffattn_status diffattn_decode_paged(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,
+                                      diffattn_tensor k1_pages, diffattn_tensor k2_pages, diffattn_tensor v_pages,
+                                      const int32_t* block_table, int64_t bt_stride, int num_pages, int page_size,
+                                      const int32_t* cache_lens, int batch, int heads, int max_len, int d, int dv,
+                                      const float* lambda, float lambda_init, diffattn_epilogue epi,
+                                      const float* norm_w, float eps, float scale, diffattn_tensor out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * DIFF V2 forward: out[b, i, p] = O_{2p} - lam[b, i, p] * O_{2p+1}, where O_j is ordinary softmax
  * attention of query head j over KV head j / (2h / h_kv) (the heads of one GQA group are
  * contiguous, and a differenced pair sits in one group). No norm, no rescale.
@@ -252,6 +283,24 @@ diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diff
                                    int batch, int h, int h_kv, int cache_len, int d, float scale,
                                    diffattn_tensor out, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * DIFF V2 decode against a paged KV cache: the same operation as diffattn_v2_decode, with the
+ * cache of each sequence held in fixed-size pages of shared pools, listed by a block table.
+ *  k_pages, v_pages: [num_pages, page_size, h_kv, d] as strided views whose s_batch is the page
+ *     stride.  block_table, bt_stride, num_pages, page_size, cache_lens, max_len: as in
+ *     diffattn_decode_paged (workspace: diffattn_v2_decode_workspace_size(batch, h, h_kv, max_len)).
+ *  Other arguments as in diffattn_v2_decode.
+ *  Kernels: the split-K MFMA kernel of diffattn_v2_decode, one table lookup per 32-key tile; bf16,
+ *  d = 128, a group of 2..32 query heads and 16-byte aligned views only.
+ *  Errors: ERR_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED (other dtypes, shapes or alignments), ERR_HIP.
+ */
+diffattn_status diffattn_v2_decode_paged(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k_pages,
+                                         diffattn_tensor v_pages, const int32_t* block_table, int64_t bt_stride,
+                                         int num_pages, int page_size, const int32_t* cache_lens, const float* lam,
+                                         int batch, int h, int h_kv, int max_len, int d, float scale,
+                                         diffattn_tensor out, void* workspace, size_t workspace_bytes,
+                                         void* stream);
 
 #ifdef __cplusplus
 }

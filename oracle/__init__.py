@@ -17,6 +17,10 @@ What it computes, with the pages it follows:
   - ``v2_forward``: "softmax can't say zero, so it subtracts", section
     "DIFF V2: what the authors changed", and the "Differential Transformer V2"
     write-up (paired heads of one GQA group, contiguous group heads).
+  - ``gather_pages``: the storage convention of the paged decodes (a cache
+    held in fixed-size pages listed by a block table) read back as a
+    contiguous cache; the paged decodes compute ``decode`` / ``v2_decode`` of
+    that cache.
 """
 import ctypes
 import os
@@ -242,6 +246,19 @@ def v2_decode(q, kc, vc, lam_pairs, cache_lens=None, scale=None, pairs=None):
         out[n] = _head(q[b, 2 * p][None], q[b, 2 * p + 1][None], kc[b, :n_b, g], kc[b, :n_b, g],
                        vc[b, :n_b, g], np.array([lam_pairs[b, p]]), False, s, None)[0]
     return out.reshape(B, H2 // 2, -1) if full else out
+
+
+def gather_pages(pool, block_table, length: int, page_size: int):
+    """A paged cache read back as a contiguous one: token t of sequence b is row t % page_size of
+    pool page block_table[b, t // page_size] (the storage convention of the paged decodes).
+    pool: [P, page_size, H, D]; block_table: [B, >= ceil(length / page_size)]. Returns [B, length, H, D]."""
+    pool, table = np.asarray(pool), np.asarray(block_table, dtype=np.int64)
+    B = table.shape[0]
+    out = np.empty((B, length) + pool.shape[2:], dtype=pool.dtype)
+    for b in range(B):
+        for t in range(length):
+            out[b, t] = pool[table[b, t // page_size], t % page_size]
+    return out
 
 
 def v1_backward(q1, q2, k1, k2, v, lam_heads, dy, causal=True, epilogue=True, lambda_init_value=0.8,

@@ -198,6 +198,33 @@ def test_fwd_train_rejects(L):
     assert call(FAKE, FAKE, dtype=0) == da.DIFFATTN_ERR_UNSUPPORTED
 
 
+def _paged(L, v2=False, table=FAKE, bt_stride=4, num_pages=16, page=64, max_len=256, d=None, dtype=1, ws_bytes=1 << 30,
+           ws=FAKE):
+    if v2:
+        d = 128 if d is None else d
+        ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(4)]
+        return L.diffattn_v2_decode_paged(dtype, ts[0], ts[1], ts[2], table, bt_stride, num_pages, page, None, FAKE,
+                                          2, 8, 2, max_len, d, 0.0, ts[3], ws, ws_bytes, None)
+    d = 64 if d is None else d
+    ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(6)]
+    return L.diffattn_decode_paged(dtype, *ts[:5], table, bt_stride, num_pages, page, None, 2, 4, max_len, d, 128,
+                                   FAKE, 0.8, 1, None, 1e-5, 0.0, ts[5], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("v2", [False, True])
+def test_paged_decode_rejects(L, v2):
+    assert _paged(L, v2, table=None) == da.DIFFATTN_ERR_ARG
+    assert _paged(L, v2, page=48) == da.DIFFATTN_ERR_ARG                 # not a multiple of 32
+    assert _paged(L, v2, page=0) == da.DIFFATTN_ERR_ARG
+    assert _paged(L, v2, num_pages=0) == da.DIFFATTN_ERR_ARG
+    assert _paged(L, v2, bt_stride=3) == da.DIFFATTN_ERR_ARG             # 256 tokens need 4 pages of 64
+    assert _paged(L, v2, max_len=0) == da.DIFFATTN_ERR_ARG
+    assert _paged(L, v2, ws_bytes=16) == da.DIFFATTN_ERR_WORKSPACE
+    assert _paged(L, v2, ws=FAKE + 32) == da.DIFFATTN_ERR_ARG
+    assert _paged(L, v2, d=32) == da.DIFFATTN_ERR_UNSUPPORTED            # no paged generic kernel
+    assert _paged(L, v2, dtype=0) == da.DIFFATTN_ERR_UNSUPPORTED
+
+
 def test_lambda_bwd_rejects(L):
     assert L.diffattn_lambda_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, None) == da.DIFFATTN_ERR_ARG
     assert L.diffattn_lambda_bwd(FAKE, FAKE, FAKE, FAKE, None, 16, 64, FAKE, FAKE, FAKE, FAKE, None) == da.DIFFATTN_ERR_ARG

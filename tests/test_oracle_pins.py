@@ -410,3 +410,33 @@ def test_v2_decode_is_last_causal_row():
     fwd = oracle.v2_forward(q, k, v, lam, causal=True)
     dec = oracle.v2_decode(q[:, -1], k, v, lam[:, -1])
     assert np.array_equal(dec, fwd[:, -1])
+
+
+# ------------------------------------------------------------------------------------------------
+# Paged caches: the gather that reads a page pool through a block table
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L,page", [(100, 32), (96, 32), (300, 64), (5, 256)])
+def test_gather_pages_round_trip(L, page):
+    # the seeded scatter (an input generator, written separately) followed by the gather gives the
+    # contiguous cache back exactly, for ragged last pages too
+    import workloads as W
+    c = torch.randn(3, L, 2, 8, generator=torch.Generator().manual_seed(L + page))
+    pool, table = W.scatter_to_pages(c, page, seed=L * page)
+    assert table.shape == (3, (L + page - 1) // page)
+    assert len(set(table.flatten().tolist())) == table.numel()          # no page shared
+    back = oracle.gather_pages(pool.numpy(), table.numpy(), L, page)
+    assert np.array_equal(back, c.numpy())
+
+
+def test_gather_pages_identity_table():
+    # sequence b's pages stored consecutively: the pool is the contiguous cache cut into pages
+    B, L, page = 2, 128, 32
+    c = np.arange(B * L * 3 * 4, dtype=np.float64).reshape(B, L, 3, 4)
+    pool = c.reshape(B * L // page, page, 3, 4)
+    table = np.arange(B * L // page).reshape(B, L // page)
+    assert np.array_equal(oracle.gather_pages(pool, table, L, page), c)
+    # a shorter length reads a prefix, and entries past it are never used
+    table2 = table.copy()
+    table2[:, -1] = 10 ** 6
+    assert np.array_equal(oracle.gather_pages(pool, table2, L - page, page), c[:, :L - page])

@@ -211,3 +211,41 @@ def v2_decode_inputs(cfg: V2DecodeConfig, device="cpu", B=None, L=None) -> dict:
     gl = _gen(cfg.seed + 1000, "cpu")
     lam = torch.rand((B, cfg.hq // 2), generator=gl, dtype=torch.float32)
     return dict(q=q, k=k, v=v, lam=lam)
+
+
+def scatter_to_pages(caches, page_size: int, seed: int, spare_pages: int = 3):
+    """Lay contiguous caches [B, L, H, D] out as a shared page pool and a block table.
+
+    Every sequence's pages take distinct pool slots in a seeded random order, plus a few spare
+    slots that no table entry names, the layout a serving system's allocator leaves behind. Pool
+    rows that hold no token (spare pages, the tail of a sequence's last page) are filled with
+    seeded noise. ``caches`` is one tensor or a tuple of tensors that share the table; pools are
+    built on the caches' device.
+    Returns (pools [P, page_size, H, D] in the order given, block_table int32 [B, ceil(L / page_size)]).
+    """
+    single = isinstance(caches, torch.Tensor)
+    caches = (caches,) if single else tuple(caches)
+    B, L = caches[0].shape[:2]
+    dev = caches[0].device
+    per_seq = (L + page_size - 1) // page_size
+    P = B * per_seq + spare_pages
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(P, generator=g)[:B * per_seq].to(torch.int32)
+    gd = _gen(seed + 1, dev)
+    pools = []
+    for c in caches:
+        tail = per_seq * page_size - L
+        if tail:
+            pad = torch.randn((B, tail) + tuple(c.shape[2:]), generator=gd, device=dev).to(c.dtype)
+            c = torch.cat([c, pad], dim=1)
+        pool = torch.empty((P, page_size) + tuple(c.shape[2:]), dtype=c.dtype, device=dev)
+        pool.index_copy_(0, perm.to(dev).long(), c.reshape((B * per_seq, page_size) + tuple(c.shape[2:])))
+        if spare_pages:
+            used = torch.zeros(P, dtype=torch.bool)
+            used[perm.long()] = True
+            spare = torch.nonzero(~used).flatten().to(dev)
+            pool[spare] = torch.randn((spare.numel(), page_size) + tuple(c.shape[2:]), generator=gd,
+                                      device=dev).to(c.dtype)
+        pools.append(pool)
+    table = perm.reshape(B, per_seq).to(dev)
+    return (pools[0] if single else tuple(pools)), table
