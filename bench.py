@@ -226,7 +226,17 @@ def main():
                                   "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                                   "traffic": load_traffic("v2_gqa_8k", ["fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"])}
         log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s")
-        del x5, o5
+        # lambda from its logits inside the kernel (sigmoid per query row)
+        z5 = W.lambda_logits((c5.B, c5.N, c5.hq // 2), seed=c5.seed + 2000, device=dev)
+        fz = lambda: da.diffattn_v2_fwd(x5["q"], x5["k"], x5["v"], z5, causal=True, out=o5, lam_logits=True)
+        fz()
+        torch.cuda.synchronize()
+        avg, mn = time_launches(fz, args.secondary_reps, torch)
+        tf = fl5 / (avg * 1e-3) / 1e12
+        secondary["v2_gqa_8k"]["lam_logits_kernel_avg_ms"] = round(avg, 4)
+        secondary["v2_gqa_8k"]["lam_logits_TFLOP/s"] = round(tf, 2)
+        log(f"[bench]   lambda logits: {avg:.3f} ms -> {tf:.1f} TFLOP/s")
+        del x5, o5, z5
     if "decode" in which:
         c4 = W.V1_DECODE_64K
         log(f"[bench] {c4.name} (generating the cache on the device)")

@@ -79,7 +79,7 @@ def lib():
         L.diffattn_decode.argtypes = [i, T, T, T, T, T, vp, i, i, i, i, i, vp, f, i, vp, f, f, T, vp,
                                       sz, vp]
         L.diffattn_v2_fwd.restype = i
-        L.diffattn_v2_fwd.argtypes = [i, T, T, T, vp, i, i, i, i, i, i, f, T, vp]
+        L.diffattn_v2_fwd.argtypes = [i, T, T, T, vp, i, i, i, i, i, i, i, f, T, vp]
         L.diffattn_fwd_train.restype = i
         L.diffattn_fwd_train.argtypes = [i, T, T, T, T, T, i, i, i, i, i, i, vp, f, i, i, vp, f, f, T, vp, vp, vp]
         L.diffattn_bwd_workspace_size.restype = sz
@@ -92,13 +92,14 @@ def lib():
         L.diffattn_v2_decode_workspace_size.restype = sz
         L.diffattn_v2_decode_workspace_size.argtypes = [i, i, i, i]
         L.diffattn_v2_decode.restype = i
-        L.diffattn_v2_decode.argtypes = [i, T, T, T, vp, vp, i, i, i, i, i, f, T, vp, sz, vp]
+        L.diffattn_v2_decode.argtypes = [i, T, T, T, vp, vp, i, i, i, i, i, i, f, T, vp, sz, vp]
         i64 = ctypes.c_int64
         L.diffattn_decode_paged.restype = i
         L.diffattn_decode_paged.argtypes = [i, T, T, T, T, T, vp, i64, i, i, vp, i, i, i, i, i, vp, f, i, vp, f,
                                             f, T, vp, sz, vp]
         L.diffattn_v2_decode_paged.restype = i
-        L.diffattn_v2_decode_paged.argtypes = [i, T, T, T, vp, i64, i, i, vp, vp, i, i, i, i, i, f, T, vp, sz, vp]
+        L.diffattn_v2_decode_paged.argtypes = [i, T, T, T, vp, i64, i, i, vp, vp, i, i, i, i, i, i, f, T, vp, sz,
+                                               vp]
         _lib = L
     return _lib
 
@@ -201,8 +202,9 @@ def diffattn_decode(q1, q2, k1c, k2c, vc, lam: torch.Tensor, cache_lens: torch.T
 
 
 def diffattn_v2_fwd(q, k, v, lam: torch.Tensor, causal: bool = True, scale: float = 0.0,
-                    out: torch.Tensor | None = None) -> torch.Tensor:
-    """DIFF V2 forward. q: [B, N, 2h, d]; k, v: [B, N, h_kv, d]; lam: fp32 [B, N, h] contiguous.
+                    out: torch.Tensor | None = None, lam_logits: bool = False) -> torch.Tensor:
+    """DIFF V2 forward. q: [B, N, 2h, d]; k, v: [B, N, h_kv, d]; lam: fp32 [B, N, h] contiguous,
+    lambda itself or (lam_logits=True) the projected logits whose sigmoid the kernel takes.
     Returns [B, N, h, d]."""
     B, N, H2, d = q.shape
     hkv = k.shape[2]
@@ -213,7 +215,8 @@ def diffattn_v2_fwd(q, k, v, lam: torch.Tensor, causal: bool = True, scale: floa
         raise ValueError("lam must be a contiguous float32 [B, N, h] tensor")
     if out is None:
         out = torch.empty((B, N, h, d), dtype=q.dtype, device=q.device)
-    _check(lib().diffattn_v2_fwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), lam.data_ptr(), B, N, h, hkv,
+    _check(lib().diffattn_v2_fwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), lam.data_ptr(), int(bool(lam_logits)), B, N,
+                                 h, hkv,
                                  d, int(bool(causal)), float(scale), _t4(out), _stream(q.device)))
     return out
 
@@ -281,9 +284,10 @@ def diffattn_v2_decode_workspace_size(batch: int, h: int, h_kv: int, cache_len: 
 
 def diffattn_v2_decode(q, kc, vc, lam: torch.Tensor, cache_lens: torch.Tensor | None = None,
                        scale: float = 0.0, workspace: torch.Tensor | None = None,
-                       out: torch.Tensor | None = None) -> torch.Tensor:
+                       out: torch.Tensor | None = None, lam_logits: bool = False) -> torch.Tensor:
     """DIFF V2 decode. q: [B, 2h, d] (or [B, 1, 2h, d]); caches kc, vc: [B, L, h_kv, d];
-    lam: fp32 [B, h] contiguous; cache_lens: int32 [B] on the device or None. Returns [B, h, d]."""
+    lam: fp32 [B, h] contiguous (lambda, or its logits with lam_logits=True); cache_lens: int32 [B]
+    on the device or None. Returns [B, h, d]."""
     if q.dim() == 3:
         q = q.unsqueeze(1)
     B, _, H2, d = q.shape
@@ -303,7 +307,7 @@ def diffattn_v2_decode(q, kc, vc, lam: torch.Tensor, cache_lens: torch.Tensor | 
     if cache_lens is not None and cache_lens.dtype != torch.int32:
         raise ValueError("cache_lens must be int32")
     _check(lib().diffattn_v2_decode(_dtype_code(q), _t4(q), _t4(kc), _t4(vc), _ptr(cache_lens), lam.data_ptr(),
-                                    B, h, hkv, L, d, float(scale), _t4(out), workspace.data_ptr(),
+                                    int(bool(lam_logits)), B, h, hkv, L, d, float(scale), _t4(out), workspace.data_ptr(),
                                     workspace.numel(), _stream(q.device)))
     return out.squeeze(1)
 
@@ -349,7 +353,7 @@ def diffattn_decode_paged(q1, q2, k1_pages, k2_pages, v_pages, block_table: torc
 def diffattn_v2_decode_paged(q, k_pages, v_pages, block_table: torch.Tensor, lam: torch.Tensor,
                              cache_lens: torch.Tensor | None = None, max_len: int | None = None,
                              scale: float = 0.0, workspace: torch.Tensor | None = None,
-                             out: torch.Tensor | None = None) -> torch.Tensor:
+                             out: torch.Tensor | None = None, lam_logits: bool = False) -> torch.Tensor:
     """DIFF V2 decode against a paged cache. q: [B, 2h, d] (or [B, 1, 2h, d]); page pools
     k_pages, v_pages: [P, page_size, h_kv, d]; block_table, cache_lens, max_len as in
     diffattn_decode_paged; lam: fp32 [B, h] contiguous. Returns [B, h, d]."""
@@ -373,7 +377,8 @@ def diffattn_v2_decode_paged(q, k_pages, v_pages, block_table: torch.Tensor, lam
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().diffattn_v2_decode_paged(_dtype_code(q), _t4(q), _t4(k_pages), _t4(v_pages),
                                           block_table.data_ptr(), block_table.stride(0), P, page,
-                                          _ptr(cache_lens), lam.data_ptr(), B, h, hkv, L, d, float(scale), _t4(out),
+                                          _ptr(cache_lens), lam.data_ptr(), int(bool(lam_logits)), B, h, hkv, L, d,
+                                          float(scale), _t4(out),
                                           workspace.data_ptr(), workspace.numel(), _stream(q.device)))
     return out.squeeze(1)
 

@@ -43,6 +43,10 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// 1 / (1 + e^-z): DIFF V2's per-token lambda from its projected logit. Saturates to 0 and 1 for
+// large |z| (e^-z overflowing to +inf gives 0).
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.f / (1.f + __expf(-z)); }
+
 // 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -262,7 +262,7 @@ __global__ __launch_bounds__(128) void v2_decode_reduce_kernel(V2DecodeArgs a) {
         }
         res[k] = O / L;
     }
-    const float lam = a.lam[(int64_t)b * a.lam_bs + p];
+    const float lam = a.lam_sigmoid ? sigmoid_f32(a.lam[(int64_t)b * a.lam_bs + p]) : a.lam[(int64_t)b * a.lam_bs + p];
     float x;
     {
 #pragma clang fp contract(off)

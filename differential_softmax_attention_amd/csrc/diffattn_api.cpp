@@ -262,15 +262,18 @@ diffattn_status diffattn_decode_paged(diffattn_dtype dtype, diffattn_tensor q1, 
                        lambda_init, epi, norm_w, eps, scale, out, workspace, workspace_bytes, stream, pc);
 }
 
+static bool valid_lam_mode(diffattn_lambda_mode m) { return m == DIFFATTN_LAMBDA_VALUE || m == DIFFATTN_LAMBDA_SIGMOID; }
+
 diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k, diffattn_tensor v,
-                                const float* lam, int batch, int seq, int h, int h_kv, int d, int causal, float scale,
-                                diffattn_tensor out, void* stream) {
+                                const float* lam, diffattn_lambda_mode lam_mode, int batch, int seq, int h, int h_kv,
+                                int d, int causal, float scale, diffattn_tensor out, void* stream) {
     if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: unknown dtype %d", (int)dtype);
     const diffattn_tensor* ts[4] = {&q, &k, &v, &out};
     const char* names[4] = {"q", "k", "v", "out"};
     for (int i = 0; i < 4; ++i)
         if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
     if (!lam) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: lam is null");
+    if (!valid_lam_mode(lam_mode)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: unknown lam_mode %d", (int)lam_mode);
     if (batch < 1 || seq < 1 || h < 1 || h_kv < 1 || d < 1)
         return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: sizes must be >= 1 (batch=%d seq=%d h=%d h_kv=%d d=%d)", batch,
                     seq, h, h_kv, d);
@@ -295,6 +298,7 @@ diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
         copy_strides(a.vs, v); copy_strides(a.os, out);
         a.lam = lam;
         a.lams[0] = (int64_t)seq * h; a.lams[1] = h; a.lams[2] = 1;
+        a.lam_sigmoid = lam_mode == DIFFATTN_LAMBDA_SIGMOID;
         a.norm_w = nullptr;
         a.batch = batch; a.heads = h; a.seq_q = seq; a.seq_k = seq;
         a.kv_group = group;
@@ -311,6 +315,7 @@ diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
     a.q_hmul = 2; a.q1_hoff = 0; a.q2_hoff = 1; a.kv_hdiv = group;
     a.lam = lam;
     a.lams[0] = (int64_t)seq * h; a.lams[1] = h; a.lams[2] = 1;
+    a.lam_sigmoid = lam_mode == DIFFATTN_LAMBDA_SIGMOID;
     a.key_lens = nullptr;
     a.seq_q = seq; a.seq_k = seq; a.d = d; a.dv = d;
     a.causal = causal ? 1 : 0;
@@ -326,7 +331,8 @@ size_t diffattn_v2_decode_workspace_size(int batch, int h, int h_kv, int cache_l
 }
 
 static diffattn_status v2_decode_impl(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor kc, diffattn_tensor vc,
-                                      const int32_t* cache_lens, const float* lam, int batch, int h, int h_kv,
+                                      const int32_t* cache_lens, const float* lam, diffattn_lambda_mode lam_mode,
+                                      int batch, int h, int h_kv,
                                       int cache_len, int d, float scale, diffattn_tensor out, void* workspace,
                                       size_t workspace_bytes, void* stream, const diffattn::PagedCache& pc) {
     if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: unknown dtype %d", (int)dtype);
@@ -335,6 +341,8 @@ static diffattn_status v2_decode_impl(diffattn_dtype dtype, diffattn_tensor q, d
     for (int i = 0; i < 4; ++i)
         if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
     if (!lam) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: lam is null");
+    if (!valid_lam_mode(lam_mode))
+        return fail(DIFFATTN_ERR_ARG, "diffattn_v2_decode: unknown lam_mode %d", (int)lam_mode);
     if (batch < 1 || h < 1 || h_kv < 1 || cache_len < 1 || d < 1)
         return fail(DIFFATTN_ERR_ARG,
                     "diffattn_v2_decode: sizes must be >= 1 (batch=%d h=%d h_kv=%d cache_len=%d d=%d)", batch, h,
@@ -370,6 +378,7 @@ static diffattn_status v2_decode_impl(diffattn_dtype dtype, diffattn_tensor q, d
         a.pc = pc;
         a.lam = lam;
         a.lam_bs = h;
+        a.lam_sigmoid = lam_mode == DIFFATTN_LAMBDA_SIGMOID;
         a.ws = (float*)workspace;
         a.batch = batch; a.h = h; a.h_kv = h_kv; a.group = group; a.cache_len = cache_len;
         a.scale_log2 = sc * 1.4426950408889634f;
@@ -382,6 +391,7 @@ static diffattn_status v2_decode_impl(diffattn_dtype dtype, diffattn_tensor q, d
     a.q_hmul = 2; a.q1_hoff = 0; a.q2_hoff = 1; a.kv_hdiv = group;
     a.lam = lam;
     a.lams[0] = h; a.lams[1] = 0; a.lams[2] = 1;
+    a.lam_sigmoid = lam_mode == DIFFATTN_LAMBDA_SIGMOID;
     a.key_lens = cache_lens;
     a.seq_q = 1; a.seq_k = cache_len; a.d = d; a.dv = d;
     a.causal = 0;
@@ -391,24 +401,25 @@ static diffattn_status v2_decode_impl(diffattn_dtype dtype, diffattn_tensor q, d
 }
 
 diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor kc, diffattn_tensor vc,
-                                   const int32_t* cache_lens, const float* lam, int batch, int h, int h_kv,
-                                   int cache_len, int d, float scale, diffattn_tensor out, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
-    return v2_decode_impl(dtype, q, kc, vc, cache_lens, lam, batch, h, h_kv, cache_len, d, scale, out, workspace,
-                          workspace_bytes, stream, diffattn::PagedCache{});
+                                   const int32_t* cache_lens, const float* lam, diffattn_lambda_mode lam_mode,
+                                   int batch, int h, int h_kv, int cache_len, int d, float scale, diffattn_tensor out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    return v2_decode_impl(dtype, q, kc, vc, cache_lens, lam, lam_mode, batch, h, h_kv, cache_len, d, scale, out,
+                          workspace, workspace_bytes, stream, diffattn::PagedCache{});
 }
 
 diffattn_status diffattn_v2_decode_paged(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k_pages,
                                          diffattn_tensor v_pages, const int32_t* block_table, int64_t bt_stride,
                                          int num_pages, int page_size, const int32_t* cache_lens, const float* lam,
-                                         int batch, int h, int h_kv, int max_len, int d, float scale,
-                                         diffattn_tensor out, void* workspace, size_t workspace_bytes, void* stream) {
+                                         diffattn_lambda_mode lam_mode, int batch, int h, int h_kv, int max_len, int d,
+                                         float scale, diffattn_tensor out, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
     if (diffattn_status s =
             check_pages(block_table, bt_stride, num_pages, page_size, max_len, "diffattn_v2_decode_paged"))
         return s;
     diffattn::PagedCache pc{block_table, bt_stride, page_size, num_pages};
-    return v2_decode_impl(dtype, q, k_pages, v_pages, cache_lens, lam, batch, h, h_kv, max_len, d, scale, out,
-                          workspace, workspace_bytes, stream, pc);
+    return v2_decode_impl(dtype, q, k_pages, v_pages, cache_lens, lam, lam_mode, batch, h, h_kv, max_len, d, scale,
+                          out, workspace, workspace_bytes, stream, pc);
 }
 
 diffattn_status diffattn_fwd_train(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,

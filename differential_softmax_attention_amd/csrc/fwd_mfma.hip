@@ -384,6 +384,7 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     float lam;
     if (V2) {
         lam = (qrow < a.seq_q) ? a.lam[b * a.lams[0] + (int64_t)qrow * a.lams[1] + (int64_t)hout * a.lams[2]] : 0.f;
+        if (a.lam_sigmoid) lam = sigmoid_f32(lam);
     } else {
         lam = a.lam[hout];
     }

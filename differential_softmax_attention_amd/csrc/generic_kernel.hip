@@ -103,7 +103,8 @@ __global__ __launch_bounds__(64) void generic_diffattn_kernel(GenericArgs a) {
         __syncthreads();
     }
 
-    const float lam = a.lam[b * a.lams[0] + (int64_t)i * a.lams[1] + (int64_t)h * a.lams[2]];
+    const float lam_raw = a.lam[b * a.lams[0] + (int64_t)i * a.lams[1] + (int64_t)h * a.lams[2]];
+    const float lam = a.lam_sigmoid ? sigmoid_f32(lam_raw) : lam_raw;
     const float r1 = 1.f / l1, r2 = 1.f / l2;
     float o[kMaxDvPerLane];
     float ss = 0.f;

@@ -20,6 +20,7 @@ struct GenericArgs {
     int q_hmul, q1_hoff, q2_hoff, kv_hdiv;
     const float* lam;
     int64_t lams[3];
+    int lam_sigmoid;          // lam holds logits: lambda = sigmoid(lam)
     const int32_t* key_lens;  // per-batch key count (decode) or null
     int seq_q, seq_k, d, dv, causal, epi;
     const float* norm_w;
@@ -38,6 +39,7 @@ struct MfmaFwdArgs {
     int64_t q1s[3], q2s[3], k1s[3], k2s[3], vs[3], os[3];
     const float* lam;
     int64_t lams[3];
+    int lam_sigmoid;  // V2: lam holds logits, lambda = sigmoid(lam)
     const float* norm_w;
     int batch, heads, seq_q, seq_k;
     int kv_group;     // V2: query heads per KV head (2h / h_kv); V1: unused
@@ -96,6 +98,7 @@ struct V2DecodeArgs {
     const int32_t* cache_lens;
     const float* lam;
     int64_t lam_bs;
+    int lam_sigmoid;  // lam holds logits: lambda = sigmoid(lam)
     float* ws;  // workspace: per-slice partials
     PagedCache pc;
     int batch, h, h_kv, group, cache_len, n_splits, split_len;

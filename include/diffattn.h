@@ -57,6 +57,16 @@ typedef enum {
     DIFFATTN_EPI_RMSNORM_SCALE = 1  /* O <- O / sqrt(mean_c O_c^2 + eps) * w_c * (1 - lambda_init) */
 } diffattn_epilogue;
 
+/*
+ * How a DIFF V2 entry point reads its lambda buffer. DIFF V2 learns lambda per token and per head
+ * pair as the sigmoid of a linear projection of the token ("softmax can't say zero, so it
+ * subtracts", section "DIFF V2: what the authors changed"; "Differential Transformer V2").
+ */
+typedef enum {
+    DIFFATTN_LAMBDA_VALUE = 0,   /* lam holds lambda itself, used as given */
+    DIFFATTN_LAMBDA_SIGMOID = 1  /* lam holds the projected logits z; the kernels use 1 / (1 + e^-z) */
+} diffattn_lambda_mode;
+
 /* A strided [batch, tokens, heads, dim] view; strides in elements, dim stride 1. */
 typedef struct {
     void* ptr;
@@ -181,8 +191,9 @@ diffattn_status diffattn_decode_paged(diffattn_dtype dtype, diffattn_tensor q1, 
  * attention of query head j over KV head j / (2h / h_kv) (the heads of one GQA group are
  * contiguous, and a differenced pair sits in one group). No norm, no rescale.
  *  q: [batch, seq, 2h, d];  k, v: [batch, seq, h_kv, d];  out: [batch, seq, h, d]
- *  lam: DEVICE fp32 [batch, seq, h] contiguous, used as given (a caller that learns it as
- *       sigmoid(W x) applies the sigmoid before the call).
+ *  lam: DEVICE fp32 [batch, seq, h] contiguous: lambda itself (lam_mode DIFFATTN_LAMBDA_VALUE) or
+ *       the projected logits W_lambda x, whose sigmoid the kernel takes per row
+ *       (DIFFATTN_LAMBDA_SIGMOID), so no separate pass over the logits is needed.
  *  causal: as in diffattn_fwd with seq_q = seq_k = seq.
  *  Requires 2h divisible by h_kv with an even group size (so no pair straddles two groups).
  *  Kernels: bf16 with d = 128 and aligned strides runs the MFMA kernel, in which one block owns a
@@ -191,9 +202,9 @@ diffattn_status diffattn_decode_paged(diffattn_dtype dtype, diffattn_tensor q1, 
  *  Errors: ERR_ARG, ERR_UNSUPPORTED (d > 256), ERR_HIP.
  */
 diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k,
-                                diffattn_tensor v, const float* lam, int batch, int seq, int h,
-                                int h_kv, int d, int causal, float scale, diffattn_tensor out,
-                                void* stream);
+                                diffattn_tensor v, const float* lam, diffattn_lambda_mode lam_mode,
+                                int batch, int seq, int h, int h_kv, int d, int causal, float scale,
+                                diffattn_tensor out, void* stream);
 
 /*
  * DIFF V1 training forward: diffattn_fwd plus what the backward pass needs.
@@ -268,7 +279,8 @@ size_t diffattn_v2_decode_workspace_size(int batch, int h, int h_kv, int cache_l
  *  q: [batch, 1, 2h, d] (the token stride is unused);  kc, vc: [batch, cache_len, h_kv, d]
  *  cache_lens: DEVICE int32 [batch] with 1 <= len <= cache_len, or NULL (every len = cache_len);
  *              an entry outside that range is clamped into it on the device.
- *  lam: DEVICE fp32 [batch, h] contiguous, used as given.   out: [batch, 1, h, d].
+ *  lam: DEVICE fp32 [batch, h] contiguous, lambda or its logits as lam_mode says (see
+ *       diffattn_v2_fwd).   out: [batch, 1, h, d].
  *  scale: softmax scale; <= 0 selects 1/sqrt(d).
  *  workspace: DEVICE buffer of at least diffattn_v2_decode_workspace_size(...) bytes, 256-byte
  *  aligned; its contents on entry do not matter.
@@ -280,9 +292,9 @@ size_t diffattn_v2_decode_workspace_size(int batch, int h, int h_kv, int cache_l
  */
 diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor kc,
                                    diffattn_tensor vc, const int32_t* cache_lens, const float* lam,
-                                   int batch, int h, int h_kv, int cache_len, int d, float scale,
-                                   diffattn_tensor out, void* workspace, size_t workspace_bytes,
-                                   void* stream);
+                                   diffattn_lambda_mode lam_mode, int batch, int h, int h_kv,
+                                   int cache_len, int d, float scale, diffattn_tensor out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * DIFF V2 decode against a paged KV cache: the same operation as diffattn_v2_decode, with the
@@ -298,9 +310,9 @@ diffattn_status diffattn_v2_decode(diffattn_dtype dtype, diffattn_tensor q, diff
 diffattn_status diffattn_v2_decode_paged(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k_pages,
                                          diffattn_tensor v_pages, const int32_t* block_table, int64_t bt_stride,
                                          int num_pages, int page_size, const int32_t* cache_lens, const float* lam,
-                                         int batch, int h, int h_kv, int max_len, int d, float scale,
-                                         diffattn_tensor out, void* workspace, size_t workspace_bytes,
-                                         void* stream);
+                                         diffattn_lambda_mode lam_mode, int batch, int h, int h_kv, int max_len,
+                                         int d, float scale, diffattn_tensor out, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

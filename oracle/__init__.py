@@ -189,15 +189,26 @@ def decode(q1, q2, k1c, k2c, vc, lam_heads, cache_lens=None, epilogue=True, lamb
     return out.reshape(B, H, dv) if full else out
 
 
-def v2_forward(q, k, v, lam_tok, causal=True, scale=None, rows=None):
+def sigmoid(z):
+    """1 / (1 + e^-z) in fp64: DIFF V2's lambda from its projected logit ("softmax can't say
+    zero", section "DIFF V2: what the authors changed")."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def v2_forward(q, k, v, lam_tok, causal=True, scale=None, rows=None, lam_logits=False):
     """DIFF V2 forward (no per-head norm).
 
-    q: [B, N, 2h, d]; k, v: [B, N, h_kv, d]; lam_tok: [B, N, h] (used as given).
+    q: [B, N, 2h, d]; k, v: [B, N, h_kv, d]; lam_tok: [B, N, h], lambda itself or, with
+    lam_logits, the projected logits (lambda = sigmoid of them).
     Pair p takes query heads 2p (map 1) and 2p+1 (map 2); both read KV head
     2p // (2h / h_kv), since the heads of one GQA group are contiguous.
     rows: None, or an int array [n, 3] of (b, p, i). Returns [B, N, h, d] or [n, d].
     """
     q, k, v, lam_tok = (np.asarray(x) for x in (q, k, v, lam_tok))
+    if lam_logits:
+        lam_tok = sigmoid(lam_tok)
     B, N, H2, d = q.shape
     h = H2 // 2
     hkv = k.shape[2]
@@ -221,15 +232,18 @@ def v2_forward(q, k, v, lam_tok, causal=True, scale=None, rows=None):
                              v[b, :, g], lam_tok[b, :, p], causal, s, rows[sel, 2])
     return out
 
-def v2_decode(q, kc, vc, lam_pairs, cache_lens=None, scale=None, pairs=None):
+def v2_decode(q, kc, vc, lam_pairs, cache_lens=None, scale=None, pairs=None, lam_logits=False):
     """DIFF V2 decode: the new token's query heads against the first cache_lens[b] cached keys.
 
     Each pair p subtracts query head 2p+1's attention from head 2p's with the token's lambda, both
     over the KV head of their GQA group ("softmax can't say zero", section "DIFF V2: what the
-    authors changed"); no norm. q: [B, 2h, d]; kc, vc: [B, L, h_kv, d]; lam_pairs: [B, h].
+    authors changed"); no norm. q: [B, 2h, d]; kc, vc: [B, L, h_kv, d]; lam_pairs: [B, h]
+    (logits whose sigmoid is lambda, with lam_logits).
     pairs: None for every (b, p), else an int array [n, 2] of (b, p); returns [B, h, d] or [n, d].
     """
     q, kc, vc, lam_pairs = (np.asarray(x) for x in (q, kc, vc, lam_pairs))
+    if lam_logits:
+        lam_pairs = sigmoid(lam_pairs)
     B, H2, d = q.shape
     L, hkv = kc.shape[1], kc.shape[2]
     group = H2 // hkv

@@ -119,9 +119,9 @@ def test_decode_workspace_size(L):
     assert 0 < small < big < 64 << 20      # partials only: a few MB even for a 17 GB cache
 
 
-def _v2(L, B=1, N=8, h=4, hkv=2, d=128, lam=FAKE, causal=1, dtype=1, scale=0.0):
+def _v2(L, B=1, N=8, h=4, hkv=2, d=128, lam=FAKE, causal=1, dtype=1, scale=0.0, mode=0):
     ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(4)]
-    return L.diffattn_v2_fwd(dtype, ts[0], ts[1], ts[2], lam, B, N, h, hkv, d, causal, scale, ts[3], None)
+    return L.diffattn_v2_fwd(dtype, ts[0], ts[1], ts[2], lam, mode, B, N, h, hkv, d, causal, scale, ts[3], None)
 
 
 def test_v2_rejects(L):
@@ -131,11 +131,13 @@ def test_v2_rejects(L):
     assert _v2(L, N=0) == da.DIFFATTN_ERR_ARG
     assert _v2(L, d=512) == da.DIFFATTN_ERR_UNSUPPORTED
     assert _v2(L, dtype=9) == da.DIFFATTN_ERR_ARG
+    assert _v2(L, mode=2) == da.DIFFATTN_ERR_ARG         # unknown lambda mode
+    assert _v2(L, mode=-1) == da.DIFFATTN_ERR_ARG
 
 
-def _v2dec(L, B=2, h=8, hkv=2, Lc=300, d=128, lam=FAKE, ws=FAKE, ws_bytes=1 << 30, dtype=1, lens=None):
+def _v2dec(L, B=2, h=8, hkv=2, Lc=300, d=128, lam=FAKE, ws=FAKE, ws_bytes=1 << 30, dtype=1, lens=None, mode=1):
     ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(4)]
-    return L.diffattn_v2_decode(dtype, ts[0], ts[1], ts[2], lens, lam, B, h, hkv, Lc, d, 0.0, ts[3], ws,
+    return L.diffattn_v2_decode(dtype, ts[0], ts[1], ts[2], lens, lam, mode, B, h, hkv, Lc, d, 0.0, ts[3], ws,
                                 ws_bytes, None)
 
 
@@ -152,6 +154,7 @@ def test_v2_decode_rejects(L):
     assert _v2dec(L, ws=None) == da.DIFFATTN_ERR_ARG
     assert _v2dec(L, ws=FAKE + 64) == da.DIFFATTN_ERR_ARG      # not 256-byte aligned
     assert _v2dec(L, d=512) == da.DIFFATTN_ERR_UNSUPPORTED
+    assert _v2dec(L, mode=5) == da.DIFFATTN_ERR_ARG
 
 
 def test_v2_decode_workspace_size(L):
@@ -203,7 +206,7 @@ def _paged(L, v2=False, table=FAKE, bt_stride=4, num_pages=16, page=64, max_len=
     if v2:
         d = 128 if d is None else d
         ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(4)]
-        return L.diffattn_v2_decode_paged(dtype, ts[0], ts[1], ts[2], table, bt_stride, num_pages, page, None, FAKE,
+        return L.diffattn_v2_decode_paged(dtype, ts[0], ts[1], ts[2], table, bt_stride, num_pages, page, None, FAKE, 0,
                                           2, 8, 2, max_len, d, 0.0, ts[3], ws, ws_bytes, None)
     d = 64 if d is None else d
     ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(6)]

@@ -440,3 +440,46 @@ def test_gather_pages_identity_table():
     table2 = table.copy()
     table2[:, -1] = 10 ** 6
     assert np.array_equal(oracle.gather_pages(pool, table2, L - page, page), c[:, :L - page])
+
+
+# ------------------------------------------------------------------------------------------------
+# DIFF V2 lambda from logits: lambda = sigmoid(W x) ("softmax can't say zero", section "DIFF V2:
+# what the authors changed"), pinned at points where the sigmoid has a closed form
+# ------------------------------------------------------------------------------------------------
+
+def _v2_small(seed):
+    rng = np.random.default_rng(seed)
+    B, N, H2, hkv, d = 2, 9, 4, 2, 8
+    return rng.standard_normal((B, N, H2, d)), rng.standard_normal((B, N, hkv, d)), rng.standard_normal((B, N, hkv, d))
+
+
+@pytest.mark.parametrize("z,lam_value", [(0.0, 0.5), (math.log(3.0), 0.75), (-math.log(3.0), 0.25),
+                                         (math.log(0.25), 0.2)])
+def test_v2_logits_closed_form_points(z, lam_value):
+    q, k, v = _v2_small(11)
+    B, N = q.shape[:2]
+    out_z = oracle.v2_forward(q, k, v, np.full((B, N, 2), z), causal=True, lam_logits=True)
+    out_v = oracle.v2_forward(q, k, v, np.full((B, N, 2), lam_value), causal=True)
+    assert np.max(np.abs(out_z - out_v)) < 1e-14
+
+
+def test_v2_logits_saturate():
+    # a large positive logit gives lambda = 1 (the full difference), a large negative one gives
+    # lambda = 0: the pair's first head alone, i.e. plain GQA attention of head 2p
+    q, k, v = _v2_small(12)
+    B, N = q.shape[:2]
+    hi = oracle.v2_forward(q, k, v, np.full((B, N, 2), 60.0), causal=True, lam_logits=True)
+    one = oracle.v2_forward(q, k, v, np.ones((B, N, 2)), causal=True)
+    assert np.max(np.abs(hi - one)) < 1e-12
+    lo = oracle.v2_forward(q, k, v, np.full((B, N, 2), -800.0), causal=True, lam_logits=True)
+    zero = oracle.v2_forward(q, k, v, np.zeros((B, N, 2)), causal=True)
+    assert np.array_equal(lo, zero)
+
+
+def test_v2_decode_logits_match_forward_last_row():
+    q, k, v = _v2_small(13)
+    B, N = q.shape[:2]
+    z = np.random.default_rng(14).standard_normal((B, N, 2)) * 3
+    fwd = oracle.v2_forward(q, k, v, z, causal=True, lam_logits=True)
+    dec = oracle.v2_decode(q[:, -1], k, v, z[:, -1], lam_logits=True)
+    assert np.max(np.abs(fwd[:, -1] - dec)) < 1e-13

@@ -249,3 +249,9 @@ def scatter_to_pages(caches, page_size: int, seed: int, spare_pages: int = 3):
         pools.append(pool)
     table = perm.reshape(B, per_seq).to(dev)
     return (pools[0] if single else tuple(pools)), table
+
+
+def lambda_logits(shape, seed: int, device="cpu", std: float = 2.0) -> torch.Tensor:
+    """DIFF V2 lambda logits (the projection W_lambda x before its sigmoid), fp32 ~ N(0, std^2):
+    wide enough that some sigmoids saturate near 0 and 1."""
+    return torch.randn(shape, generator=_gen(seed, "cpu"), dtype=torch.float32).mul_(std).to(device)
