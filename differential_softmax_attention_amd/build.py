@@ -14,7 +14,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
 SOURCES = ["diffattn_api.cpp", "generic_kernel.hip", "fwd_mfma.hip", "decode.hip", "decode_v2.hip", "bwd.hip", "lambda_kernel.hip"]
-HEADERS = ["common.hpp", "kernels.hpp", "mfma_tile.hpp"]
+HEADERS = ["common.hpp", "kernels.hpp", "mfma_tile.hpp", "bwd_tile.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

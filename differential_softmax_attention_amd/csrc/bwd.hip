@@ -27,79 +27,30 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
+#include "bwd_tile.hpp"
 
 namespace diffattn {
 
 namespace {
 
-constexpr int kBN = 32;
+using namespace bwdt;
+
 constexpr int kD = 64;
 constexpr int kDV = 128;
-constexpr int kKTile = kBN * kD * 2;    // bytes of one 32-row, 64-wide tile (K-layout)
-constexpr int kVTile = kBN * kDV * 2;   // bytes of one 32-row, 128-wide tile (V-layout)
+constexpr int kKTile = kBN * kD * 2;    // bytes of one 32-row, 64-wide tile
+constexpr int kVTile = kBN * kDV * 2;   // bytes of one 32-row, 128-wide tile
 constexpr int kPreRows = 16;            // rows per bwd_pre block (4 waves x 4 rows)
-// dK/dV query-tile stage: Q1 | Q2 (K-layout) | go (V-layout) | lse [32][2] | dd [32][2]
+// dK/dV query-tile stage: Q1 | Q2 (64 wide) | go (128 wide) | lse [32][2] | dd [32][2]
 constexpr int kQStats = 2 * kKTile + kVTile;
 constexpr int kQStage = kQStats + 2 * kBN * 2 * 4;
 constexpr int kQStages = 3;
 constexpr int kKStage = 2 * kKTile + kVTile;   // dQ key-tile stage: K1 | K2 (64 wide) | V
 constexpr int kKStages = 3;
 
-// ---- LDS operand addressing
-// V-layout (128 wide) tiles use the forward's layout. The 64-wide tiles of the backward (Q tiles in
-// dK/dV, K tiles in dQ) are read both by rows (16-byte reads) and transposed (8-byte reads), so
-// their chunk swizzle differs from the forward's K-layout: 16-byte chunk c of row r sits at
-//   c ^ (4 ((r >> 1) & 1) | ((r >> 2) & 3)),
-// which puts 16 consecutive rows of one chunk, and 4 consecutive rows of 4 chunks, on distinct
-// banks.
-__device__ __forceinline__ int bswz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
-// Row operand: row `row`, 16-byte logical chunk 2kk + h2 (MFMA A rows or B columns).
-__device__ __forceinline__ int rowop_b(int row, int kk, int h2) { return row * (kD * 2) + (((2 * kk + h2) ^ bswz(row)) * 16); }
-__device__ __forceinline__ int rowop_v(int row, int kk, int h2) { return row * (kDV * 2) + v_phys(row, 2 * kk + h2) * 16; }
-// Transposing read (A operand X^T of a row-major tile X whose rows are the MFMA k index): 16-lane
-// group G covers columns 32 mt + 16 (G & 1) .. +15 and rows 16 kb + 4 (G >> 1) + 0..3 (lo) and
-// +8 (hi); lane L supplies row + L/4 and columns + 4 (L % 4) .. +3.
-__device__ __forceinline__ int trop_b(int lane, int kb, int mt, int hi) {
-    const int G = lane >> 4, L = lane & 15;
-    const int row = 16 * kb + 4 * (G >> 1) + (L >> 2) + 8 * hi;
-    const int c = mt * 4 + (G & 1) * 2 + ((L >> 1) & 1);
-    return row * (kD * 2) + ((c ^ bswz(row)) * 16) + (L & 1) * 8;
-}
-__device__ __forceinline__ int trop_v(int lane, int kb, int ct, int hi) {
-    const int G = lane >> 4, L = lane & 15;
-    const int row = 16 * kb + 4 * (G >> 1) + (L >> 2) + 8 * hi;
-    const int c = ct * 4 + (G & 1) * 2 + ((L >> 1) & 1);
-    return row * (kDV * 2) + v_phys(row, c) * 16 + (L & 1) * 8;
-}
-__device__ __forceinline__ bf16x8 tr_pair(const unsigned char* base, int lo, int hi) {
-    const i16x4 a = lds_read_tr16((const bf16*)(base + lo));
-    const i16x4 b = lds_read_tr16((const bf16*)(base + hi));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-// C registers kb*8 .. kb*8+7 of a 32x32 tile as the bf16 B operand of the next MFMA whose k index
-// is the tile's row index (the k order matches the transposing read)
-__device__ __forceinline__ bf16x8 c_to_b(const f32x16& x, int kb) {
-    bf16x8 r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (bf16)x[kb * 8 + j];
-    return r;
-}
-
-// acc += a b with the accumulator held in AGPRs. The gradient accumulators stay live across the
-// whole tile loop while each tile's products are worked on by VALU code in VGPRs; issuing these
-// accumulations by hand pins the accumulators to the AGPR file, where the compiler would otherwise
-// copy them back and forth. The compiler does not look into the asm, so it also carries the two
-// wait states that a VALU write of an operand needs before an MFMA reads it.
-__device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// Wait states between the last such MFMA and VALU reads of its accumulator (more than the 18 the
-// longest MFMA needs).
-__device__ __forceinline__ void agpr_drain(f32x16& x0, f32x16& x1, f32x16& x2, f32x16& x3) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3));
-}
-
-template <int V> struct IC { static constexpr int value = V; };
+__device__ __forceinline__ int rowop_b(int row, int kk, int h2) { return rowop<kD>(row, kk, h2); }
+__device__ __forceinline__ int trop_b(int lane, int kb, int mt, int hi) { return trop<kD>(lane, kb, mt, hi); }
+__device__ __forceinline__ int rowop_v(int row, int kk, int h2) { return rowop<kDV>(row, kk, h2); }
+__device__ __forceinline__ int trop_v(int lane, int kb, int ct, int hi) { return trop<kDV>(lane, kb, ct, hi); }
 
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
@@ -251,9 +202,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // last key are fetched from the last one (their weights are masked to zero)
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int k_row = tid >> 3, k_col = (tid & 7) ^ bswz(k_row);
-    const int v_row0 = tid >> 4, v_row1 = v_row0 + 16;
-    const int v_col0 = v_logical(v_row0, tid & 15), v_col1 = v_logical(v_row1, tid & 15);
+    const int k_row = slot_row<kD>(tid), k_col = slot_chunk<kD>(tid);
+    const int v_row0 = slot_row<kDV>(tid), v_row1 = v_row0 + 16;
+    const int v_col0 = slot_chunk<kDV>(tid), v_col1 = slot_chunk<kDV>(tid + 256);
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         const int last = min(kBN, a.seq_k - kt * kBN) - 1;
         const uint32_t st = lds0 + stage * kKStage + wave_u * 1024;
@@ -402,9 +353,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // fetches the rows' log-sum-exp and D values (64 floats each). Rows past the last query are
     // fetched from the last one (their weights are masked to zero).
     const uint32_t lds_sq = (uint32_t)(uintptr_t)(lds_u8_t*)sq;
-    const int q_row = tid >> 3, q_col = (tid & 7) ^ bswz(q_row);
-    const int g_row0 = tid >> 4, g_row1 = g_row0 + 16;
-    const int g_col0 = v_logical(g_row0, tid & 15), g_col1 = v_logical(g_row1, tid & 15);
+    const int q_row = slot_row<kD>(tid), q_col = slot_chunk<kD>(tid);
+    const int g_row0 = slot_row<kDV>(tid), g_row1 = g_row0 + 16;
+    const int g_col0 = slot_chunk<kDV>(tid), g_col1 = slot_chunk<kDV>(tid + 256);
     auto issue_q = [&](int qt, int stage) __attribute__((always_inline)) {
         const int i0 = qt * kBN;
         const int last = min(kBN, a.seq_q - i0) - 1;
