@@ -37,7 +37,7 @@ EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "
             "diffattn_fwd", "diffattn_decode_workspace_size", "diffattn_decode", "diffattn_v2_fwd",
             "diffattn_v2_decode_workspace_size", "diffattn_v2_decode", "diffattn_fwd_train",
             "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd", "diffattn_decode_paged",
-            "diffattn_v2_decode_paged")
+            "diffattn_v2_decode_paged", "diffattn_v2_fwd_train", "diffattn_v2_bwd_workspace_size", "diffattn_v2_bwd")
 
 
 class DiffAttnError(RuntimeError):
@@ -97,6 +97,12 @@ def lib():
         L.diffattn_decode_paged.restype = i
         L.diffattn_decode_paged.argtypes = [i, T, T, T, T, T, vp, i64, i, i, vp, i, i, i, i, i, vp, f, i, vp, f,
                                             f, T, vp, sz, vp]
+        L.diffattn_v2_fwd_train.restype = i
+        L.diffattn_v2_fwd_train.argtypes = [i, T, T, T, vp, i, i, i, i, i, i, i, f, T, vp, vp, vp]
+        L.diffattn_v2_bwd_workspace_size.restype = sz
+        L.diffattn_v2_bwd_workspace_size.argtypes = [i, i, i]
+        L.diffattn_v2_bwd.restype = i
+        L.diffattn_v2_bwd.argtypes = [i, T, T, T, T, vp, i, i, i, i, i, i, i, f, vp, vp, T, T, T, vp, vp, sz, vp]
         L.diffattn_v2_decode_paged.restype = i
         L.diffattn_v2_decode_paged.argtypes = [i, T, T, T, vp, i64, i, i, vp, vp, i, i, i, i, i, i, f, T, vp, sz,
                                                vp]
@@ -236,6 +242,51 @@ def diffattn_fwd_train(q1, q2, k1, k2, v, lam: torch.Tensor, causal: bool = True
                                     EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
                                     float(scale), _t4(out), lse.data_ptr(), maps.data_ptr(), _stream(q1.device)))
     return out, lse, maps
+
+
+def diffattn_v2_fwd_train(q, k, v, lam: torch.Tensor, causal: bool = True, scale: float = 0.0,
+                          out: torch.Tensor | None = None, lam_logits: bool = False):
+    """DIFF V2 training forward. Returns (out [B, N, h, d], lse [B, h, N, 2] fp32,
+    maps [B, N, h, 2, d] fp32)."""
+    B, N, H2, d = q.shape
+    hkv = k.shape[2]
+    h = H2 // 2
+    if H2 % 2:
+        raise ValueError("q must hold an even number of heads (2h)")
+    if not (lam.is_contiguous() and lam.dtype == torch.float32 and tuple(lam.shape) == (B, N, h)):
+        raise ValueError("lam must be a contiguous float32 [B, N, h] tensor")
+    if out is None:
+        out = torch.empty((B, N, h, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, h, N, 2), dtype=torch.float32, device=q.device)
+    maps = torch.empty((B, N, h, 2, d), dtype=torch.float32, device=q.device)
+    _check(lib().diffattn_v2_fwd_train(_dtype_code(q), _t4(q), _t4(k), _t4(v), lam.data_ptr(), int(bool(lam_logits)),
+                                       B, N, h, hkv, d, int(bool(causal)), float(scale), _t4(out), lse.data_ptr(),
+                                       maps.data_ptr(), _stream(q.device)))
+    return out, lse, maps
+
+
+def diffattn_v2_bwd_workspace_size(batch: int, h: int, seq: int) -> int:
+    return int(lib().diffattn_v2_bwd_workspace_size(batch, h, seq))
+
+
+def diffattn_v2_bwd(q, k, v, dout, lam: torch.Tensor, lse: torch.Tensor, maps: torch.Tensor, causal: bool = True,
+                    scale: float = 0.0, lam_logits: bool = False, workspace: torch.Tensor | None = None) -> dict:
+    """DIFF V2 backward for L = sum(dout * out). Returns dq, dk, dv (like the inputs) and dlam
+    (fp32 [B, N, h]: the gradient with respect to what lam holds, lambda or its logits)."""
+    B, N, H2, d = q.shape
+    hkv = k.shape[2]
+    h = H2 // 2
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v)}
+    dlam = torch.empty((B, N, h), dtype=torch.float32, device=q.device)
+    need = diffattn_v2_bwd_workspace_size(B, h, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().diffattn_v2_bwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), _t4(dout), lam.data_ptr(),
+                                 int(bool(lam_logits)), B, N, h, hkv, d, int(bool(causal)), float(scale),
+                                 lse.data_ptr(), maps.data_ptr(), _t4(g["dq"]), _t4(g["dk"]), _t4(g["dv"]),
+                                 dlam.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+    g["dlam"] = dlam
+    return g
 
 
 def diffattn_bwd_workspace_size(batch: int, heads: int, seq_q: int) -> int:

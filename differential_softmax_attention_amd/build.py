@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
-SOURCES = ["diffattn_api.cpp", "generic_kernel.hip", "fwd_mfma.hip", "decode.hip", "decode_v2.hip", "bwd.hip", "lambda_kernel.hip"]
+SOURCES = ["diffattn_api.cpp", "generic_kernel.hip", "fwd_mfma.hip", "decode.hip", "decode_v2.hip", "bwd.hip", "bwd_v2.hip", "lambda_kernel.hip"]
 HEADERS = ["common.hpp", "kernels.hpp", "mfma_tile.hpp", "bwd_tile.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,7 +25,7 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 # Per-source additions. The dK/dV backward kernel runs one wave per SIMD with ~320 live
 # registers; left to itself the compiler gives its MFMA accumulators the AGPR form and then
 # copies them to VGPRs around every element-wise step. The VGPR form keeps them in place.
-SOURCE_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+SOURCE_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "bwd_v2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

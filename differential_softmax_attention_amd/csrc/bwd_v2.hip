@@ -1,0 +1,436 @@
+// DIFF V2 backward on bf16 MFMA (gfx950): d = 128, query heads 2p and 2p+1 of one GQA group form
+// pair p and read their group's K and V; lambda per (token, pair), given or as the sigmoid of its
+// logit; no norm ("softmax can't say zero, so it subtracts", section "DIFF V2: what the authors
+// changed"; "Differential Transformer V2").
+//
+// Gradients of out_p = A_{2p} V - lambda A_{2p+1} V for L = sum(dout * out), by the chain rule:
+//   go = dout_p,  dP = go V^T (shared by both heads),  D_k = go . (A_k V) per row,
+//   dS_{2p} = A_{2p} (dP - D_1),  dS_{2p+1} = -lambda A_{2p+1} (dP - D_2),
+//   dQ_j = s dS_j K,  dK = s sum over the group's heads of dS_j^T Q_j,
+//   dV = sum over the group's pairs of (A_{2p} - lambda A_{2p+1})^T go_p,
+//   dlambda = -go . (A_{2p+1} V) per row (times sigmoid'(z) = lambda (1 - lambda) for logits).
+// The training forward supplies each head's log-sum-exp and A_k V.
+//
+// Kernels (no atomics; every sum in a fixed order):
+//  - bwd_v2_pre: one wave per (row, pair): go (a copy of dout, head-major for the DMA), D_1, D_2,
+//    lambda after the sigmoid, and dlambda.
+//  - bwd_v2_dq: 32 queries of one pair per wave, walking key tiles (K and V of the group through
+//    a three-stage LDS ring); each K row fragment feeds both heads' scores and each transposed K
+//    fragment both heads' dQ.
+//  - bwd_v2_dkdv: 32 keys of one KV head per wave (K and V rows in registers), walking the query
+//    tiles of every pair of the group; dK gathers both heads of every pair, dV every pair.
+// The dQ and dK/dV accumulators sit in AGPRs (inline-asm MFMAs); tiles are 128 wide in the
+// backward layout of bwd_tile.hpp.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_tile.hpp"
+#include "bwd_tile.hpp"
+
+namespace diffattn {
+
+namespace {
+
+using namespace bwdt;
+
+constexpr int kD = 128;
+constexpr int kTile = kBN * kD * 2;          // bytes of one 32-row, 128-wide tile
+constexpr int kPreRows = 16;                 // rows per pre block (4 waves x 4 rows)
+// dQ key-tile stage: K | V
+constexpr int kKStage = 2 * kTile;
+// dK/dV query-tile stage: Q_{2p} | Q_{2p+1} | go_p | lse [32][2] | dd [32][2] | lambda [32] (+pad)
+constexpr int kQStats = 3 * kTile;
+constexpr int kQStage = kQStats + 3 * 256;
+constexpr int kStages = 3;
+
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_v2_pre_kernel(V2BwdArgs a) {
+    const int blk = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int k = 0; k < kPreRows / 4; ++k) {
+        const int i = blk * kPreRows + wave * (kPreRows / 4) + k;
+        if (i >= a.seq) break;
+        const int64_t row = ((int64_t)b * a.h + p) * a.seq + i;      // head-major row
+        const int64_t tok = ((int64_t)b * a.seq + i) * a.h + p;      // token-major (lam, maps)
+        const float* mp = a.maps + tok * 2 * kD;
+        const float a1x = mp[lane], a1y = mp[lane + 64];
+        const float a2x = mp[kD + lane], a2y = mp[kD + lane + 64];
+        const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)i * a.dos[1] + (int64_t)p * a.dos[2];
+        const bf16 g0 = dyp[lane], g1 = dyp[lane + 64];
+        const float y0 = (float)g0, y1 = (float)g1;
+        const float D1 = wave_sum(y0 * a1x + y1 * a1y);
+        const float D2 = wave_sum(y0 * a2x + y1 * a2y);
+        bf16* gp = a.go + row * kD;
+        gp[lane] = g0;
+        gp[lane + 64] = g1;
+        if (lane == 0) {
+            const float z = a.lam[tok];
+            const float lam = a.lam_sigmoid ? sigmoid_f32(z) : z;
+            const float dl = -D2;
+            a.dlam[tok] = a.lam_sigmoid ? dl * lam * (1.f - lam) : dl;
+            a.lamr[row] = lam;
+            a.dd[2 * row] = D1;
+            a.dd[2 * row + 1] = D2;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dQ: a block of 4 waves owns 128 queries of one pair, 32 per wave, and walks the key tiles.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_v2_dq_kernel(V2BwdArgs a) {
+    __shared__ __align__(16) unsigned char smem[kStages * kKStage];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, h2 = lane >> 5;
+    // the last query tiles see the most keys under causal masking: they go first
+    const int qt = gridDim.y - 1 - blockIdx.y, p = blockIdx.x % a.h, b = blockIdx.x / a.h;
+    const int g = (2 * p) / a.group;
+    const int q0 = qt * 128, qw0 = q0 + wave * 32, qrow = qw0 + n;
+    const bool qok = qrow < a.seq;
+    const int qr = qok ? qrow : 0;
+    const int64_t row = ((int64_t)b * a.h + p) * a.seq + qr;
+
+    // per-lane query operands (B operands, lane = query n): both heads' Q (for S^T) and go (for dP^T)
+    bf16x8 bq1[8], bq2[8], bg[8];
+    {
+        const bf16* q1p = (const bf16*)a.q + b * a.qs[0] + (int64_t)qr * a.qs[1] + (int64_t)(2 * p) * a.qs[2] + 8 * h2;
+        const bf16* q2p = q1p + a.qs[2];
+        const bf16* gp = a.go + row * kD + 8 * h2;
+        const bf16x8 z = {};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            bq1[kk] = qok ? ld_global_bf16x8(q1p + 16 * kk) : z;
+            bq2[kk] = qok ? ld_global_bf16x8(q2p + 16 * kk) : z;
+            bg[kk] = qok ? ld_global_bf16x8(gp + 16 * kk) : z;
+        }
+    }
+    const float lse1 = qok ? a.lse[2 * row] : 0.f, lse2 = qok ? a.lse[2 * row + 1] : 0.f;
+    const float D1 = qok ? a.dd[2 * row] : 0.f, D2 = qok ? a.dd[2 * row + 1] : 0.f;
+    const float nlam = qok ? -a.lamr[row] : 0.f;
+    const float c = a.scale_log2;
+
+    int nkt = (a.seq + kBN - 1) / kBN;
+    if (a.causal) nkt = min(nkt, min(q0 + 127, a.seq - 1) / kBN + 1);
+    const bool wave_active = qw0 < a.seq;
+    const int wave_qlast = min(qw0 + 31, a.seq - 1);
+    const int qlim = a.causal ? qrow : a.seq - 1;   // last key this lane's query sees
+
+    const bf16* kb0 = (const bf16*)a.k + b * a.ks[0] + (int64_t)g * a.ks[2];
+    const bf16* vb0 = (const bf16*)a.v + b * a.vs[0] + (int64_t)g * a.vs[2];
+
+    f32x16 dq1[4], dq2[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) { dq1[mt] = f32x16{}; dq2[mt] = f32x16{}; }
+
+    // key-tile DMA: thread tid fills K and V slots tid and tid + 256; rows past the last key are
+    // fetched from the last one (their weights are masked to zero)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8_t*)smem;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int r0 = slot_row<kD>(tid), r1 = r0 + 16;
+    const int c0 = slot_chunk<kD>(tid), c1 = slot_chunk<kD>(tid + 256);
+    auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+        const int last = min(kBN, a.seq - kt * kBN) - 1;
+        const uint32_t st = lds0 + stage * kKStage + wave_u * 1024;
+        const bf16* kt_p = kb0 + (int64_t)kt * kBN * a.ks[1];
+        const bf16* vt_p = vb0 + (int64_t)kt * kBN * a.vs[1];
+        dma16(kt_p, (uint32_t)(min(r0, last) * a.ks[1] + c0 * 8) * 2u, st);
+        dma16(kt_p, (uint32_t)(min(r1, last) * a.ks[1] + c1 * 8) * 2u, st + 4096);
+        dma16(vt_p, (uint32_t)(min(r0, last) * a.vs[1] + c0 * 8) * 2u, st + kTile);
+        dma16(vt_p, (uint32_t)(min(r1, last) * a.vs[1] + c1 * 8) * 2u, st + kTile + 4096);
+    };
+
+    auto compute = [&](auto ST, bool full, int k0) __attribute__((always_inline)) {
+        const unsigned char* Ks = smem + decltype(ST)::value * kKStage;
+        const unsigned char* Vs = Ks + kTile;
+        // S_j^T = K Q_j^T (lane = query n, 16 keys), dP^T = V go^T
+        f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const bf16x8 kf = lds16(Ks + rowop<kD>(n, kk, h2));
+            s1 = mfma32x32x16(kf, bq1[kk], s1);
+            s2 = mfma32x32x16(kf, bq2[kk], s2);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Vs + rowop<kD>(n, kk, h2)), bg[kk], dp);
+        f32x16 p1, p2, ds1, ds2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p1[r] = fast_exp2(fmaf(s1[r], c, -lse1));
+            p2[r] = fast_exp2(fmaf(s2[r], c, -lse2));
+        }
+        if (!full) {
+            asm volatile("");   // keeps this a branch: full tiles skip the test
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + (r >> 2) * 8 + h2 * 4 + (r & 3);
+                const bool vis = qok && key <= qlim;
+                p1[r] = vis ? p1[r] : 0.f;
+                p2[r] = vis ? p2[r] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            ds1[r] = p1[r] * (dp[r] - D1);
+            ds2[r] = nlam * p2[r] * (dp[r] - D2);
+        }
+        // dQ_j^T += K^T dS_j^T (k index = keys); one transposed K fragment serves both heads
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 b1 = c_to_b(ds1, kb), b2 = c_to_b(ds2, kb);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 kt_f = tr_pair(Ks, trop<kD>(lane, kb, mt, 0), trop<kD>(lane, kb, mt, 1));
+                mfma_agpr(dq1[mt], kt_f, b1);
+                mfma_agpr(dq2[mt], kt_f, b2);
+            }
+        }
+    };
+    auto tile = [&](auto ST, int kt) __attribute__((always_inline)) {
+        constexpr int st = decltype(ST)::value;
+        if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(kVmcnt[4]);   // tile kt+1's loads may stay in flight
+        else __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+        __syncthreads();   // tile kt landed for every thread; the stage of tile kt-1 is free
+        if (kt + kStages - 1 < nkt) issue(kt + kStages - 1, (st + kStages - 1) % kStages);
+        const int k0 = kt * kBN;
+        if (!wave_active || (a.causal && k0 > wave_qlast)) return;
+        compute(ST, qw0 + kBN <= a.seq && k0 + kBN <= a.seq && (!a.causal || k0 + kBN - 1 <= qw0), k0);
+    };
+    for (int kt = 0; kt < nkt && kt < kStages - 1; ++kt) issue(kt, kt);
+    // the query operands and the first tiles have landed: from here on the compiler sees no
+    // outstanding loads of its own and adds no waits on the key-tile DMA
+    __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+    for (int kt = 0; kt < nkt; kt += kStages) {
+        tile(IC<0>{}, kt);
+        if (kt + 1 < nkt) tile(IC<1>{}, kt + 1);
+        if (kt + 2 < nkt) tile(IC<2>{}, kt + 2);
+    }
+    agpr_drain(dq1[0], dq1[1], dq1[2], dq1[3]);
+    agpr_drain(dq2[0], dq2[1], dq2[2], dq2[3]);
+    if (!qok) return;
+    // dQ_j = s dS_j K; lane (n, h2) holds d = 32 mt + (r / 4) * 8 + 4 h2 + r % 4 of query n
+    bf16* o1p = (bf16*)a.dq + b * a.dqs[0] + (int64_t)qrow * a.dqs[1] + (int64_t)(2 * p) * a.dqs[2];
+    bf16* o2p = o1p + a.dqs[2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            bf16x4 x1, x2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x1[j] = (bf16)(dq1[mt][gq * 4 + j] * a.scale);
+                x2[j] = (bf16)(dq2[mt][gq * 4 + j] * a.scale);
+            }
+            *(bf16x4*)(o1p + mt * 32 + gq * 8 + h2 * 4) = x1;
+            *(bf16x4*)(o2p + mt * 32 + gq * 8 + h2 * 4) = x2;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dK, dV: a block of 4 waves owns 128 keys of one KV head, 32 per wave, and walks the query tiles
+// of every pair of the group. Each lane holds its key's K and V rows as MFMA B operands; dK^T and
+// dV^T of the wave's 32 keys (128 registers) sit in AGPRs. One wave per SIMD.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_v2_dkdv_kernel(V2BwdArgs a) {
+    __shared__ __align__(16) unsigned char sq[kStages * kQStage];
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = tid & 63;
+    const int n = lane & 31, h2 = lane >> 5;
+    // the first key tiles see the most queries under causal masking: they go first
+    const int kt = blockIdx.y, g = blockIdx.x % a.h_kv, b = blockIdx.x / a.h_kv;
+    const int k0 = kt * 128, kw0 = k0 + wave * 32, key = kw0 + n;
+    const int npair = a.group / 2;        // pairs of this KV group: g * npair .. + npair - 1
+    const float c = a.scale_log2;
+    const bool wave_active = kw0 < a.seq;
+
+    // B operands of this lane's key (lane n = key, 16-byte chunk 2 kk + h2); keys past the end
+    // read the last key (their weights are masked to zero)
+    bf16x8 kr[8], vr[8];
+    {
+        const int kr_ = min(key, a.seq - 1);
+        const bf16* kp = (const bf16*)a.k + b * a.ks[0] + (int64_t)kr_ * a.ks[1] + (int64_t)g * a.ks[2] + 8 * h2;
+        const bf16* vp = (const bf16*)a.v + b * a.vs[0] + (int64_t)kr_ * a.vs[1] + (int64_t)g * a.vs[2] + 8 * h2;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            kr[kk] = ld_global_bf16x8(kp + 16 * kk);
+            vr[kk] = ld_global_bf16x8(vp + 16 * kk);
+        }
+    }
+
+    f32x16 dk[4], dv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) { dk[t] = f32x16{}; dv[t] = f32x16{}; }
+
+    // work items: (query tile, pair of the group), query tile outermost
+    const int nqt = (a.seq + kBN - 1) / kBN;
+    const int qt0 = a.causal ? k0 / kBN : 0;
+    const int nit = (nqt - qt0) * npair;
+
+    // stage DMA: thread tid fills Q_{2p}, Q_{2p+1} and go_p slots tid and tid + 256; wave 0 also
+    // fetches the rows' log-sum-exp and D (64 floats each) and lambda (32 floats). Rows past the
+    // last query are fetched from the last one (their weights are masked to zero).
+    const uint32_t lds_sq = (uint32_t)(uintptr_t)(lds_u8_t*)sq;
+    const int r0 = slot_row<kD>(tid), r1 = r0 + 16;
+    const int c0 = slot_chunk<kD>(tid), c1 = slot_chunk<kD>(tid + 256);
+    auto issue = [&](int it, int stage) __attribute__((always_inline)) {
+        const int qt = qt0 + it / npair, p = g * npair + it % npair;
+        const int i0 = qt * kBN;
+        const int last = min(kBN, a.seq - i0) - 1;
+        const uint32_t st = lds_sq + stage * kQStage + wave * 1024;
+        const bf16* q1b = (const bf16*)a.q + b * a.qs[0] + (int64_t)i0 * a.qs[1] + (int64_t)(2 * p) * a.qs[2];
+        const bf16* q2b = q1b + a.qs[2];
+        const int64_t rowb = ((int64_t)b * a.h + p) * a.seq + i0;
+        const bf16* gb = a.go + rowb * kD;
+        const int ra = min(r0, last), rb = min(r1, last);
+        dma16(q1b, (uint32_t)(ra * a.qs[1] + c0 * 8) * 2u, st);
+        dma16(q1b, (uint32_t)(rb * a.qs[1] + c1 * 8) * 2u, st + 4096);
+        dma16(q2b, (uint32_t)(ra * a.qs[1] + c0 * 8) * 2u, st + kTile);
+        dma16(q2b, (uint32_t)(rb * a.qs[1] + c1 * 8) * 2u, st + kTile + 4096);
+        dma16(gb, (uint32_t)(ra * kD + c0 * 8) * 2u, st + 2 * kTile);
+        dma16(gb, (uint32_t)(rb * kD + c1 * 8) * 2u, st + 2 * kTile + 4096);
+        if (wave == 0) {
+            const uint32_t sst = lds_sq + stage * kQStage + kQStats;
+            const uint32_t fo = (uint32_t)min(lane, 2 * last + 1) * 4u;
+            dma4(a.lse + 2 * rowb, fo, sst);
+            dma4(a.dd + 2 * rowb, fo, sst + 256);
+            dma4(a.lamr + rowb, (uint32_t)min(lane, last) * 4u, sst + 512);
+        }
+    };
+
+    auto compute = [&](auto ST, bool full, int i0) __attribute__((always_inline)) {
+        const unsigned char* Q1s = sq + decltype(ST)::value * kQStage;
+        const unsigned char* Q2s = Q1s + kTile;
+        const unsigned char* Gs = Q1s + 2 * kTile;
+        const float* svl = (const float*)(Q1s + kQStats);   // lse [32][2]
+        const float* svd = svl + 64;                          // dd [32][2]
+        const float* svm = svl + 128;                         // lambda [32]
+        // dP = go V^T, S_j = Q_j K^T (rows = queries, lane = key)
+        f32x16 dp = f32x16{}, s1 = f32x16{}, s2 = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Gs + rowop<kD>(n, kk, h2)), vr[kk], dp);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            s1 = mfma32x32x16(lds16(Q1s + rowop<kD>(n, kk, h2)), kr[kk], s1);
+            s2 = mfma32x32x16(lds16(Q2s + rowop<kD>(n, kk, h2)), kr[kk], s2);
+        }
+        // register r holds query row 8 (r / 4) + 4 h2 + r % 4
+        f32x16 p1, p2, dm1, dm2, nl, ds1, ds2, pc;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int q4 = 8 * gq + 4 * h2;
+            const f32x4 l01 = *(const f32x4*)(svl + 2 * q4), l23 = *(const f32x4*)(svl + 2 * q4 + 4);
+            const f32x4 d01 = *(const f32x4*)(svd + 2 * q4), d23 = *(const f32x4*)(svd + 2 * q4 + 4);
+            const f32x4 lm = *(const f32x4*)(svm + q4);
+            const float lse1[4] = {l01[0], l01[2], l23[0], l23[2]}, lse2[4] = {l01[1], l01[3], l23[1], l23[3]};
+            const float dd1[4] = {d01[0], d01[2], d23[0], d23[2]}, dd2[4] = {d01[1], d01[3], d23[1], d23[3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * gq + j;
+                p1[r] = fast_exp2(fmaf(s1[r], c, -lse1[j]));
+                p2[r] = fast_exp2(fmaf(s2[r], c, -lse2[j]));
+                dm1[r] = dp[r] - dd1[j];
+                dm2[r] = dp[r] - dd2[j];
+                nl[r] = -lm[j];
+            }
+        }
+        if (!full) {
+            asm volatile("");   // keeps this a branch: full tiles skip the test
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int q = i0 + (r >> 2) * 8 + 4 * h2 + (r & 3);
+                const bool vis = q < a.seq && key < a.seq && (!a.causal || key <= q);
+                p1[r] = vis ? p1[r] : 0.f;
+                p2[r] = vis ? p2[r] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            ds1[r] = p1[r] * dm1[r];
+            ds2[r] = nl[r] * p2[r] * dm2[r];
+            pc[r] = fmaf(nl[r], p2[r], p1[r]);
+        }
+        // dK^T += Q_{2p}^T dS_{2p} + Q_{2p+1}^T dS_{2p+1} and dV^T += go^T (A_{2p} - lambda A_{2p+1})
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 b1 = c_to_b(ds1, kb), b2 = c_to_b(ds2, kb), bp = c_to_b(pc, kb);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                mfma_agpr(dk[mt], tr_pair(Q1s, trop<kD>(lane, kb, mt, 0), trop<kD>(lane, kb, mt, 1)), b1);
+                mfma_agpr(dk[mt], tr_pair(Q2s, trop<kD>(lane, kb, mt, 0), trop<kD>(lane, kb, mt, 1)), b2);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+                mfma_agpr(dv[ct], tr_pair(Gs, trop<kD>(lane, kb, ct, 0), trop<kD>(lane, kb, ct, 1)), bp);
+        }
+    };
+    auto step = [&](auto ST, int it) __attribute__((always_inline)) {
+        constexpr int st = decltype(ST)::value;
+        // this thread's DMA of item it has landed (the next item's loads may be in flight)
+        if (it + 1 < nit) {
+            if (wave == 0) __builtin_amdgcn_s_waitcnt(kVmcnt[9]);   // 9 loads per item, one item in flight
+            else __builtin_amdgcn_s_waitcnt(kVmcnt[6]);
+        } else {
+            __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+        }
+        __syncthreads();   // every thread's loads of item it landed; the stage of item it-1 is free
+        if (it + kStages - 1 < nit) issue(it + kStages - 1, (st + kStages - 1) % kStages);
+        const int i0 = (qt0 + it / npair) * kBN;
+        // skip the tile if it ends before this wave's first key (causal)
+        if (!wave_active || (a.causal && i0 + kBN - 1 < kw0)) return;
+        compute(ST, i0 + kBN <= a.seq && kw0 + kBN <= a.seq && (!a.causal || kw0 + kBN - 1 <= i0), i0);
+    };
+    for (int it = 0; it < nit && it < kStages - 1; ++it) issue(it, it);
+    // the key operands and the first tiles have landed: from here on the compiler sees no
+    // outstanding loads of its own and adds no waits on the query-tile DMA
+    __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+    for (int it = 0; it < nit; it += kStages) {
+        step(IC<0>{}, it);
+        if (it + 1 < nit) step(IC<1>{}, it + 1);
+        if (it + 2 < nit) step(IC<2>{}, it + 2);
+    }
+    agpr_drain(dk[0], dk[1], dk[2], dk[3]);
+    agpr_drain(dv[0], dv[1], dv[2], dv[3]);
+    if (key >= a.seq) return;
+    bf16* kp = (bf16*)a.dk + b * a.dks[0] + (int64_t)key * a.dks[1] + (int64_t)g * a.dks[2];
+    bf16* vp = (bf16*)a.dv + b * a.dvs[0] + (int64_t)key * a.dvs[1] + (int64_t)g * a.dvs[2];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bf16x4 xk, xv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xk[j] = (bf16)(dk[t][gq * 4 + j] * a.scale);
+                xv[j] = (bf16)dv[t][gq * 4 + j];
+            }
+            *(bf16x4*)(kp + t * 32 + gq * 8 + h2 * 4) = xk;
+            *(bf16x4*)(vp + t * 32 + gq * 8 + h2 * 4) = xv;
+        }
+    }
+}
+
+}  // namespace
+
+size_t v2_bwd_workspace_bytes(int batch, int h, int seq) {
+    const size_t rows = (size_t)batch * h * seq;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return up(rows * kD * 2) + up(rows * 2 * sizeof(float)) + up(rows * sizeof(float));
+}
+
+hipError_t launch_v2_bwd(V2BwdArgs a, void* workspace, hipStream_t stream) {
+    const size_t rows = (size_t)a.batch * a.h * a.seq;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    unsigned char* w = (unsigned char*)workspace;
+    a.go = (bf16*)w;
+    w += up(rows * kD * 2);
+    a.dd = (float*)w;
+    w += up(rows * 2 * sizeof(float));
+    a.lamr = (float*)w;
+
+    hipLaunchKernelGGL(bwd_v2_pre_kernel, dim3((a.seq + kPreRows - 1) / kPreRows, a.h, a.batch), dim3(256), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_v2_dq_kernel, dim3(a.h * a.batch, (a.seq + 127) / 128), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_v2_dkdv_kernel, dim3(a.h_kv * a.batch, (a.seq + 127) / 128), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace diffattn

@@ -264,9 +264,16 @@ diffattn_status diffattn_decode_paged(diffattn_dtype dtype, diffattn_tensor q1, 
 
 static bool valid_lam_mode(diffattn_lambda_mode m) { return m == DIFFATTN_LAMBDA_VALUE || m == DIFFATTN_LAMBDA_SIGMOID; }
 
-diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k, diffattn_tensor v,
-                                const float* lam, diffattn_lambda_mode lam_mode, int batch, int seq, int h, int h_kv,
-                                int d, int causal, float scale, diffattn_tensor out, void* stream) {
+// Conditions of the V2 MFMA kernels (forward, training forward, backward).
+static bool v2_mfma_ok(diffattn_dtype dtype, int d, int group) {
+    const int ppg = group / 2;
+    return dtype == DIFFATTN_BF16 && d == 128 && (ppg == 1 || ppg == 2 || ppg == 4 || ppg == 8);
+}
+
+static diffattn_status v2_fwd_impl(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k, diffattn_tensor v,
+                                   const float* lam, diffattn_lambda_mode lam_mode, int batch, int seq, int h,
+                                   int h_kv, int d, int causal, float scale, diffattn_tensor out, float* lse,
+                                   float* maps, void* stream) {
     if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd: unknown dtype %d", (int)dtype);
     const diffattn_tensor* ts[4] = {&q, &k, &v, &out};
     const char* names[4] = {"q", "k", "v", "out"};
@@ -289,8 +296,12 @@ diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
     const int group = (2 * h) / h_kv;
     const int ppg = group / 2;
 
-    const bool mfma = dtype == DIFFATTN_BF16 && d == 128 && (ppg == 1 || ppg == 2 || ppg == 4 || ppg == 8) &&
-                      vec16_ok(q) && vec16_ok(k) && vec16_ok(v) && vec16_ok(out);
+    const bool mfma = v2_mfma_ok(dtype, d, group) && vec16_ok(q) && vec16_ok(k) && vec16_ok(v) && vec16_ok(out);
+    (void)ppg;
+    if (lse && !mfma)
+        return fail(DIFFATTN_ERR_UNSUPPORTED,
+                    "diffattn_v2_fwd_train: serves bf16 with d = 128, 1, 2, 4 or 8 pairs per KV head and 16-byte "
+                    "aligned tensors");
     if (mfma) {
         diffattn::MfmaFwdArgs a{};
         a.q1 = q.ptr; a.q2 = q.ptr; a.k1 = k.ptr; a.k2 = k.ptr; a.v = v.ptr; a.out = out.ptr;
@@ -306,6 +317,8 @@ diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
         a.epi = 0;
         a.eps = 0.f; a.lambda_init = 0.f;
         a.scale_log2 = sc * 1.4426950408889634f;
+        a.lse = lse;
+        a.maps = maps;
         return hip_status(diffattn::launch_v2_fwd_mfma(a, st), "diffattn_v2_fwd launch");
     }
     diffattn::GenericArgs a{};
@@ -322,6 +335,80 @@ diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
     a.epi = 0;
     a.norm_w = nullptr; a.eps = 0.f; a.lambda_init = 0.f; a.scale = sc;
     return hip_status(diffattn::launch_generic(a, batch, h, dtype == DIFFATTN_BF16, st), "diffattn_v2_fwd launch");
+}
+
+diffattn_status diffattn_v2_fwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k, diffattn_tensor v,
+                                const float* lam, diffattn_lambda_mode lam_mode, int batch, int seq, int h, int h_kv,
+                                int d, int causal, float scale, diffattn_tensor out, void* stream) {
+    return v2_fwd_impl(dtype, q, k, v, lam, lam_mode, batch, seq, h, h_kv, d, causal, scale, out, nullptr, nullptr,
+                       stream);
+}
+
+diffattn_status diffattn_v2_fwd_train(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k, diffattn_tensor v,
+                                      const float* lam, diffattn_lambda_mode lam_mode, int batch, int seq, int h,
+                                      int h_kv, int d, int causal, float scale, diffattn_tensor out, float* lse,
+                                      float* maps, void* stream) {
+    if (!lse || !maps) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd_train: lse and maps must be non-null");
+    if (((uintptr_t)maps) % 16 != 0 || ((uintptr_t)lse) % 8 != 0)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_v2_fwd_train: maps must be 16-byte and lse 8-byte aligned");
+    return v2_fwd_impl(dtype, q, k, v, lam, lam_mode, batch, seq, h, h_kv, d, causal, scale, out, lse, maps, stream);
+}
+
+size_t diffattn_v2_bwd_workspace_size(int batch, int h, int seq) {
+    if (batch < 1 || h < 1 || seq < 1) return 0;
+    return diffattn::v2_bwd_workspace_bytes(batch, h, seq);
+}
+
+diffattn_status diffattn_v2_bwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k, diffattn_tensor v,
+                                diffattn_tensor dout, const float* lam, diffattn_lambda_mode lam_mode, int batch,
+                                int seq, int h, int h_kv, int d, int causal, float scale, const float* lse,
+                                const float* maps, diffattn_tensor dq, diffattn_tensor dk, diffattn_tensor dv,
+                                float* dlam, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: unknown dtype %d", (int)dtype);
+    const diffattn_tensor* ts[7] = {&q, &k, &v, &dout, &dq, &dk, &dv};
+    const char* names[7] = {"q", "k", "v", "dout", "dq", "dk", "dv"};
+    for (int i = 0; i < 7; ++i)
+        if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
+    if (!lam || !lse || !maps || !dlam)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: lam, lse, maps and dlam must be non-null");
+    if (!valid_lam_mode(lam_mode)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: unknown lam_mode %d", (int)lam_mode);
+    if (batch < 1 || seq < 1 || h < 1 || h_kv < 1 || d < 1)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: sizes must be >= 1 (batch=%d seq=%d h=%d h_kv=%d d=%d)", batch,
+                    seq, h, h_kv, d);
+    if (batch > 65535 || h > 65535) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: batch and h must be <= 65535");
+    if ((2 * h) % h_kv != 0 || ((2 * h) / h_kv) % 2 != 0)
+        return fail(DIFFATTN_ERR_ARG,
+                    "diffattn_v2_bwd: 2h=%d query heads must split into h_kv=%d groups of an even size", 2 * h, h_kv);
+    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: scale must be finite");
+    const size_t need = diffattn_v2_bwd_workspace_size(batch, h, seq);
+    if (workspace_bytes < need)
+        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_v2_bwd: workspace of %zu bytes < required %zu", workspace_bytes,
+                    need);
+    if (!workspace || ((uintptr_t)workspace) % 256 != 0)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: workspace must be non-null and 256-byte aligned");
+    const int group = (2 * h) / h_kv;
+    if (!v2_mfma_ok(dtype, d, group))
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_v2_bwd: serves bf16 with d = 128 and 1, 2, 4 or 8 pairs per KV head");
+    for (int i = 0; i < 7; ++i)
+        if (!vec16_ok(*ts[i]))
+            return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_v2_bwd: %s needs a 16-byte aligned base and strides that "
+                        "are multiples of 8 elements", names[i]);
+    diffattn::V2BwdArgs a{};
+    a.q = q.ptr; a.k = k.ptr; a.v = v.ptr; a.dout = dout.ptr;
+    copy_strides(a.qs, q); copy_strides(a.ks, k); copy_strides(a.vs, v); copy_strides(a.dos, dout);
+    a.dq = dq.ptr; a.dk = dk.ptr; a.dv = dv.ptr;
+    copy_strides(a.dqs, dq); copy_strides(a.dks, dk); copy_strides(a.dvs, dv);
+    a.lam = lam;
+    a.lam_sigmoid = lam_mode == DIFFATTN_LAMBDA_SIGMOID;
+    a.lse = lse;
+    a.maps = maps;
+    a.dlam = dlam;
+    a.batch = batch; a.h = h; a.h_kv = h_kv; a.group = group; a.seq = seq;
+    a.causal = causal ? 1 : 0;
+    const float sc = resolve_scale(scale, d);
+    a.scale = sc;
+    a.scale_log2 = sc * 1.4426950408889634f;
+    return hip_status(diffattn::launch_v2_bwd(a, workspace, (hipStream_t)stream), "diffattn_v2_bwd launch");
 }
 
 size_t diffattn_v2_decode_workspace_size(int batch, int h, int h_kv, int cache_len) {

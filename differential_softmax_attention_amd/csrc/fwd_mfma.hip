@@ -390,7 +390,7 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     }
     const float r1 = 1.f / l1;
     const float r2 = lam / l2;
-    if (!V2 && a.lse && qrow < a.seq_q) {
+    if (a.lse && qrow < a.seq_q) {
         // training outputs for the backward pass: each map's log-sum-exp in base 2 (in the units
         // of the scaled scores, so a weight is exp2(c s - lse)) and its normalised output A_k V
         const int64_t row = ((int64_t)b * a.heads + hout) * a.seq_q + qrow;

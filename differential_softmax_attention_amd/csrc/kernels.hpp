@@ -45,9 +45,9 @@ struct MfmaFwdArgs {
     int kv_group;     // V2: query heads per KV head (2h / h_kv); V1: unused
     int causal, epi;
     float eps, lambda_init, scale_log2;  // softmax scale * log2(e)
-    // V1 training outputs, both optional (null in inference): lse [batch, heads, seq_q, 2] holds each
+    // training outputs, both optional (null in inference): lse [batch, heads, seq_q, 2] holds each
     // map's log-sum-exp in base 2 of the scaled scores; maps [batch, seq_q, heads, 2, 128] holds
-    // A1 V and A2 V in fp32
+    // A1 V and A2 V in fp32 (V2: heads = pairs, the maps of query heads 2p and 2p+1)
     float* lse;
     float* maps;
 };
@@ -141,5 +141,30 @@ hipError_t launch_lambda_bwd(const float* lq1, const float* lk1, const float* lq
 
 hipError_t launch_lambda(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
                          int n, int dim, float lambda_init, float* out, hipStream_t stream);
+
+// DIFF V2 backward (bf16, d = 128): q [batch, seq, 2h, d], k, v [batch, seq, h_kv, d], dout
+// [batch, seq, h, d]; lam [batch, seq, h] (values, or logits with lam_sigmoid); the training
+// forward's lse [batch, h, seq, 2] and maps [batch, seq, h, 2, 128]; gradients dq, dk, dv like
+// the inputs and dlam like lam.
+struct V2BwdArgs {
+    const void *q, *k, *v, *dout;
+    int64_t qs[3], ks[3], vs[3], dos[3];
+    void *dq, *dk, *dv;
+    int64_t dqs[3], dks[3], dvs[3];
+    const float* lam;
+    int lam_sigmoid;
+    const float* lse;
+    const float* maps;
+    float* dlam;
+    // workspace: go [batch, h, seq, 128] bf16, dd [batch, h, seq, 2], lambda per row [batch, h, seq]
+    bf16* go;
+    float* dd;
+    float* lamr;
+    int batch, h, h_kv, group, seq, causal;
+    float scale_log2, scale;
+};
+
+size_t v2_bwd_workspace_bytes(int batch, int h, int seq);
+hipError_t launch_v2_bwd(V2BwdArgs a, void* workspace, hipStream_t stream);
 
 }  // namespace diffattn

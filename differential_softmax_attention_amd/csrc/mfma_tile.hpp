@@ -24,8 +24,9 @@ __device__ __forceinline__ int v_logical(int row, int p) {
     return y ^ ((y & 2) << 2);
 }
 
-// s_waitcnt immediates for vmcnt(n) with the other counters left unconstrained
-constexpr unsigned kVmcnt[9] = {0x0F70, 0x0F71, 0x0F72, 0x0F73, 0x0F74, 0x0F75, 0x0F76, 0x0F77, 0x0F78};
+// s_waitcnt immediates for vmcnt(n), n < 16, with the other counters left unconstrained
+constexpr unsigned kVmcnt[16] = {0x0F70, 0x0F71, 0x0F72, 0x0F73, 0x0F74, 0x0F75, 0x0F76, 0x0F77,
+                                 0x0F78, 0x0F79, 0x0F7A, 0x0F7B, 0x0F7C, 0x0F7D, 0x0F7E, 0x0F7F};
 
 // 16-byte global -> LDS DMA for one wave: lane i reads sbase + voff (voff per lane) and the
 // chunk lands at LDS address lds_wave_base + 16 i. Issued from inline asm so that the compiler

@@ -264,6 +264,49 @@ diffattn_status diffattn_lambda_bwd(const float* lq1, const float* lk1, const fl
                                     void* stream);
 
 /*
+ * DIFF V2 training forward: diffattn_v2_fwd plus what diffattn_v2_bwd needs.
+ *  lse:  DEVICE fp32 [batch, h, seq, 2], 8-byte aligned: per row and pair the base-2 log-sum-exp
+ *        of query heads 2p and 2p+1 (units of scale * log2(e) * q.k, as in diffattn_fwd_train).
+ *  maps: DEVICE fp32 [batch, seq, h, 2, d], 16-byte aligned: A_{2p} V and A_{2p+1} V per row.
+ *  The output and every other argument are those of diffattn_v2_fwd.
+ *  Serves bf16 with d = 128, 1, 2, 4 or 8 pairs per KV head and aligned strides (the MFMA
+ *  kernel); ERR_UNSUPPORTED else.
+ */
+diffattn_status diffattn_v2_fwd_train(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k,
+                                      diffattn_tensor v, const float* lam, diffattn_lambda_mode lam_mode,
+                                      int batch, int seq, int h, int h_kv, int d, int causal, float scale,
+                                      diffattn_tensor out, float* lse, float* maps, void* stream);
+
+/* Bytes of device workspace diffattn_v2_bwd needs (0 on invalid sizes): dout copied head-major
+ * in bf16, two fp32 row statistics and lambda per row. */
+size_t diffattn_v2_bwd_workspace_size(int batch, int h, int seq);
+
+/*
+ * DIFF V2 backward: the gradients of L = sum(dout * out) for the forward of diffattn_v2_fwd_train
+ * (same inputs and options), by the chain rule through "softmax can't say zero, so it subtracts",
+ * section "DIFF V2: what the authors changed" (out_p = A_{2p} V - lambda A_{2p+1} V with the
+ * pair's GQA K and V, no norm): both softmaxes, the difference and the products.
+ *  dout: [batch, seq, h, d];  lse, maps: the training forward's outputs for these inputs.
+ *  dq: like q ([batch, seq, 2h, d]);  dk, dv: like k and v ([batch, seq, h_kv, d]), each summed
+ *  over the query heads of its group; all written (bf16), fp32 accumulation inside.
+ *  dlam: DEVICE fp32 [batch, seq, h], written with dL/dlam for what lam holds: dL/dlambda for
+ *  DIFFATTN_LAMBDA_VALUE, dL/dz = dL/dlambda * lambda (1 - lambda) for DIFFATTN_LAMBDA_SIGMOID.
+ *  workspace: DEVICE buffer of at least diffattn_v2_bwd_workspace_size(...) bytes, 256-byte
+ *  aligned; its contents on entry do not matter.
+ *  Kernels: a row pass (the per-row dot products and dlam), a query-tile MFMA kernel for dQ and a
+ *  key-tile MFMA kernel for dK and dV that walks every pair of the KV head's group. No atomics:
+ *  results are bitwise reproducible.
+ *  Errors: ERR_ARG (null pointers, sizes, groups, lam_mode), ERR_WORKSPACE, ERR_UNSUPPORTED
+ *  (other than bf16, d = 128, 1, 2, 4 or 8 pairs per KV head, aligned views), ERR_HIP.
+ */
+diffattn_status diffattn_v2_bwd(diffattn_dtype dtype, diffattn_tensor q, diffattn_tensor k,
+                                diffattn_tensor v, diffattn_tensor dout, const float* lam,
+                                diffattn_lambda_mode lam_mode, int batch, int seq, int h, int h_kv, int d,
+                                int causal, float scale, const float* lse, const float* maps,
+                                diffattn_tensor dq, diffattn_tensor dk, diffattn_tensor dv, float* dlam,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace diffattn_v2_decode needs for these sizes (0 on invalid sizes). The
  * workspace holds, per cache slice and query head, the slice's shift, weight sum and 128-wide
  * accumulator in fp32.

@@ -361,3 +361,62 @@ def v1_train_stats(q1, q2, k1, k2, v, causal=True, scale=None):
                     mx = zi.max()
                     lse[b, h, i, m] = (mx + np.log(np.sum(np.exp(zi - mx)))) / np.log(2.0)
     return lse, maps
+
+
+def v2_backward(q, k, v, lam_tok, dy, causal=True, scale=None, lam_logits=False):
+    """Gradients of the DIFF V2 forward (v2_forward) for L = sum(dy * out).
+
+    Pair p is the V1 head difference of query heads 2p and 2p+1 over the group's K and V with a
+    per-row lambda and no norm ("softmax can't say zero", section "DIFF V2: what the authors
+    changed"), so each pair is oracle_diff_head_bwd with K1 = K2 = K_g and go = dy; K and V
+    gradients add up over the heads of the group. With lam_logits the lambda gradient is carried
+    through the sigmoid: dL/dz = dL/dlambda * lambda (1 - lambda).
+    q: [B, Nq, 2h, d]; k, v: [B, Nk, h_kv, d]; lam_tok: [B, Nq, h]; dy: [B, Nq, h, d]. Nq may be
+    smaller than Nk: the queries are then the last Nq rows of the sequence (query i sees keys
+    j <= i + Nk - Nq), whose gradients are exact for them and, for keys past Nk - Nq, complete
+    (no earlier query sees those keys).
+    Returns a dict with dq, dk, dv (shaped like the inputs) and dlam [B, Nq, h].
+    """
+    q, k, v, dy = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dy))
+    lam_tok = np.asarray(lam_tok, dtype=np.float64)
+    lam_val = sigmoid(lam_tok) if lam_logits else lam_tok
+    B, N, H2, d = q.shape
+    Nk = k.shape[1]
+    h, hkv = H2 // 2, k.shape[2]
+    group = H2 // hkv
+    s = default_scale(d) if scale is None else float(scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dlam = np.zeros((B, N, h))
+    L = _load()
+    for b in range(B):
+        for p in range(h):
+            g = (2 * p) // group
+            args = [_f64(q[b, :, 2 * p]), _f64(q[b, :, 2 * p + 1]), _f64(k[b, :, g]), _f64(k[b, :, g]),
+                    _f64(v[b, :, g])]
+            lam_rows = _f64(lam_val[b, :, p])
+            outs = [np.empty((N, d)), np.empty((N, d)), np.empty((Nk, d)), np.empty((Nk, d)),
+                    np.empty((Nk, v.shape[3])), np.empty(N)]
+            rc = L.oracle_diff_head_bwd(*(_ptr(x) for x in args), N, Nk, d, v.shape[3], _ptr(lam_rows),
+                                        int(bool(causal)), s, _ptr(_f64(dy[b, :, p])), *(_ptr(x) for x in outs))
+            if rc != 0:
+                raise ValueError("oracle_diff_head_bwd failed")
+            dq[b, :, 2 * p] = outs[0]
+            dq[b, :, 2 * p + 1] = outs[1]
+            dk[b, :, g] += outs[2] + outs[3]
+            dv[b, :, g] += outs[4]
+            dlam[b, :, p] = outs[5] * (lam_rows * (1.0 - lam_rows) if lam_logits else 1.0)
+    return dict(dq=dq, dk=dk, dv=dv, dlam=dlam)
+
+
+def v2_train_stats(q, k, v, causal=True, scale=None):
+    """What the V2 training forward saves, from the definitions: lse [B, h, N, 2], the base-2
+    log-sum-exp of query heads 2p and 2p+1 over their group's keys, and maps [B, N, h, 2, d], the
+    two heads' attention outputs A_{2p} V and A_{2p+1} V. It is v1_train_stats with Q1, Q2 the
+    pair's heads and K1 = K2 = K_g, V = V_g."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, N, H2, d = q.shape
+    h, hkv = H2 // 2, k.shape[2]
+    group = H2 // hkv
+    gk = np.stack([k[:, :, (2 * p) // group] for p in range(h)], axis=2)      # [B, N, h, d]
+    gv = np.stack([v[:, :, (2 * p) // group] for p in range(h)], axis=2)
+    return v1_train_stats(q[:, :, 0::2], q[:, :, 1::2], gk, gk, gv, causal=causal, scale=scale)

@@ -114,3 +114,102 @@ def test_lambda_backward_matches_finite_differences():
             vm[i][idx] -= h
             num[idx] = (np.sum(dlam * oracle.lam(*vp, 12)) - np.sum(dlam * oracle.lam(*vm, 12))) / (2 * h)
         assert np.allclose(got[name], num, atol=1e-8, rtol=0), name
+
+
+# ------------------------------------------------------------------------------------------------
+# DIFF V2 ("softmax can't say zero", section "DIFF V2: what the authors changed"): per-row lambda,
+# query heads 2p and 2p+1 sharing the group's K and V, no norm
+# ------------------------------------------------------------------------------------------------
+
+def _v2_loss(x, dy, lam, causal, logits):
+    y = oracle.v2_forward(x["q"], x["k"], x["v"], lam, causal=causal, lam_logits=logits)
+    return float(np.sum(dy * y))
+
+
+@pytest.mark.parametrize("causal,logits", [(True, False), (False, False), (True, True)])
+def test_v2_backward_matches_finite_differences(causal, logits):
+    # one KV head shared by two pairs (a group of four query heads), so dK and dV must add up
+    # over every head of the group
+    rng = np.random.default_rng(40 + 2 * causal + logits)
+    B, N, H2, hkv, d = 1, 5, 4, 1, 3
+    x = {"q": rng.standard_normal((B, N, H2, d)), "k": rng.standard_normal((B, N, hkv, d)),
+         "v": rng.standard_normal((B, N, hkv, d))}
+    lam = rng.standard_normal((B, N, H2 // 2)) if logits else rng.uniform(0.1, 0.9, (B, N, H2 // 2))
+    dy = rng.standard_normal((B, N, H2 // 2, d))
+    got = oracle.v2_backward(x["q"], x["k"], x["v"], lam, dy, causal=causal, lam_logits=logits)
+    h = 1e-6
+    for name in ("q", "k", "v"):
+        num = np.zeros_like(x[name])
+        for idx in np.ndindex(*x[name].shape):
+            xp = {k: a.copy() for k, a in x.items()}
+            xm = {k: a.copy() for k, a in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            num[idx] = (_v2_loss(xp, dy, lam, causal, logits) - _v2_loss(xm, dy, lam, causal, logits)) / (2 * h)
+        assert np.allclose(got["d" + name], num, atol=2e-7, rtol=0), name
+    num = np.zeros_like(lam)
+    for idx in np.ndindex(*lam.shape):
+        lp, lm = lam.copy(), lam.copy()
+        lp[idx] += h
+        lm[idx] -= h
+        num[idx] = (_v2_loss(x, dy, lp, causal, logits) - _v2_loss(x, dy, lm, causal, logits)) / (2 * h)
+    assert np.allclose(got["dlam"], num, atol=2e-7, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_v2_backward_lambda_zero_is_gqa_attention_gradient(causal):
+    # lambda = 0: each pair's output is query head 2p's GQA attention; torch autograd of SDPA over
+    # the KV heads repeated per query head gives dQ of the even heads and, summed, dK and dV
+    rng = np.random.default_rng(50 + causal)
+    B, N, H2, hkv, d = 2, 8, 8, 2, 5
+    q = rng.standard_normal((B, N, H2, d))
+    k, v = rng.standard_normal((B, N, hkv, d)), rng.standard_normal((B, N, hkv, d))
+    dy = rng.standard_normal((B, N, H2 // 2, d))
+    got = oracle.v2_backward(q, k, v, np.zeros((B, N, H2 // 2)), dy, causal=causal)
+    group = H2 // hkv
+    tq = torch.from_numpy(q[:, :, 0::2]).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).contiguous().requires_grad_(True)
+    rep = lambda a: a.repeat_interleave(group // 2, dim=1)     # KV head of each even query head
+    o = torch.nn.functional.scaled_dot_product_attention(tq, rep(tk), rep(tv), is_causal=causal)
+    o.backward(torch.from_numpy(dy).permute(0, 2, 1, 3))
+    assert np.allclose(got["dq"][:, :, 0::2], tq.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=0)
+    assert np.all(got["dq"][:, :, 1::2] == 0)
+    assert np.allclose(got["dk"], tk.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=0)
+    assert np.allclose(got["dv"], tv.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=0)
+
+
+def test_v2_train_stats_definitions():
+    # maps are the two heads' own attention outputs (lambda = 0 and the forward's difference),
+    # and the weights exp2(c s - lse) of each row sum to one
+    rng = np.random.default_rng(60)
+    B, N, H2, hkv, d = 1, 7, 4, 2, 4
+    q = rng.standard_normal((B, N, H2, d))
+    k, v = rng.standard_normal((B, N, hkv, d)), rng.standard_normal((B, N, hkv, d))
+    lse, maps = oracle.v2_train_stats(q, k, v, causal=True)
+    lam = rng.uniform(0, 1, (B, N, H2 // 2))
+    out = oracle.v2_forward(q, k, v, lam, causal=True)
+    assert np.allclose(out, maps[..., 0, :] - lam[..., None] * maps[..., 1, :], atol=1e-13, rtol=0)
+    c = np.log2(np.e) / np.sqrt(d)
+    for p in range(H2 // 2):
+        for m in range(2):
+            s = q[0, :, 2 * p + m] @ k[0, :, (2 * p) // (H2 // hkv)].T
+            w = np.exp2(c * s - lse[0, p, :, m][:, None]) * np.tri(N)
+            assert np.allclose(w.sum(axis=1), 1.0, atol=1e-13)
+
+
+def test_v2_backward_query_suffix():
+    # the last Nq query rows against all keys give those rows' dQ and dlambda, and the complete dK
+    # and dV of the keys only they see, exactly as the full problem does
+    rng = np.random.default_rng(70)
+    B, N, H2, hkv, d, M = 1, 12, 4, 2, 3, 4
+    q = rng.standard_normal((B, N, H2, d))
+    k, v = rng.standard_normal((B, N, hkv, d)), rng.standard_normal((B, N, hkv, d))
+    lam = rng.uniform(0, 1, (B, N, H2 // 2))
+    dy = rng.standard_normal((B, N, H2 // 2, d))
+    full = oracle.v2_backward(q, k, v, lam, dy, causal=True)
+    part = oracle.v2_backward(q[:, -M:], k, v, lam[:, -M:], dy[:, -M:], causal=True)
+    assert np.allclose(part["dq"], full["dq"][:, -M:], atol=1e-13, rtol=0)
+    assert np.allclose(part["dlam"], full["dlam"][:, -M:], atol=1e-13, rtol=0)
+    assert np.allclose(part["dk"][:, -M:], full["dk"][:, -M:], atol=1e-13, rtol=0)
+    assert np.allclose(part["dv"][:, -M:], full["dv"][:, -M:], atol=1e-13, rtol=0)

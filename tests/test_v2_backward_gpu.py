@@ -1,0 +1,148 @@
+"""GPU parity of the DIFF V2 training forward's saved statistics and of the V2 backward pass,
+against the fp64 oracle (oracle.v2_train_stats, oracle.v2_backward)."""
+import numpy as np
+import pytest
+import torch
+
+import differential_softmax_attention_amd as da
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL_REL = 2e-2    # bf16 gradients: max error within 2% of the tensor's largest reference value,
+TOL_ABS = 1e-4    # plus bf16 rounding noise where the exact gradient is 0
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def rand(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (scale * torch.randn(shape, generator=g)).to(torch.bfloat16).to(DEV)
+
+
+def f64(x):
+    return x.double().cpu().numpy() if isinstance(x, torch.Tensor) else x
+
+
+def relerr(got, ref):
+    got, ref = f64(got), np.asarray(ref)
+    err = max(float(np.max(np.abs(got - ref))) - TOL_ABS, 0.0)
+    return err / max(float(np.max(np.abs(ref))), 1e-30)
+
+
+def case(B, N, hq, hkv, seed, causal=True, logits=False, qscale=1.0):
+    q = rand((B, N, hq, 128), seed, qscale)
+    k = rand((B, N, hkv, 128), seed + 1)
+    v = rand((B, N, hkv, 128), seed + 2)
+    dy = rand((B, N, hq // 2, 128), seed + 3)
+    if logits:
+        lam = W.lambda_logits((B, N, hq // 2), seed=seed + 4)
+    else:
+        lam = torch.rand((B, N, hq // 2), generator=torch.Generator().manual_seed(seed + 4))
+    return dict(q=q, k=k, v=v, dy=dy, lam=lam, causal=causal, logits=logits)
+
+
+def run(c):
+    note(f"v2 bwd case q={tuple(c['q'].shape)} k={tuple(c['k'].shape)} causal={c['causal']} logits={c['logits']}")
+    lam = c["lam"].to(DEV)
+    out, lse, maps = da.diffattn_v2_fwd_train(c["q"], c["k"], c["v"], lam, causal=c["causal"], lam_logits=c["logits"])
+    g = da.diffattn_v2_bwd(c["q"], c["k"], c["v"], c["dy"], lam, lse, maps, causal=c["causal"],
+                           lam_logits=c["logits"])
+    torch.cuda.synchronize()
+    ref = oracle.v2_backward(*(f64(c[k]) for k in ("q", "k", "v")), c["lam"].numpy(), f64(c["dy"]),
+                             causal=c["causal"], lam_logits=c["logits"])
+    return out, lse, maps, g, ref
+
+
+def check(g, ref):
+    for k in ("dq", "dk", "dv", "dlam"):
+        e = relerr(g[k], ref[k])
+        assert e <= TOL_REL, (k, e)
+
+
+@pytest.mark.parametrize("N,causal", [(1, True), (31, True), (33, False), (200, True)])
+def test_v2_train_stats(N, causal):
+    c = case(2, N, 8, 2, 5000 + N, causal=causal)
+    lam = c["lam"].to(DEV)
+    out, lse, maps = da.diffattn_v2_fwd_train(c["q"], c["k"], c["v"], lam, causal=causal)
+    plain = da.diffattn_v2_fwd(c["q"], c["k"], c["v"], lam, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)                     # training outputs leave the output unchanged
+    rl, rm = oracle.v2_train_stats(*(f64(c[k]) for k in ("q", "k", "v")), causal=causal)
+    assert np.max(np.abs(f64(lse) - rl)) <= 2e-3 * max(1.0, np.max(np.abs(rl)))
+    assert np.max(np.abs(f64(maps) - rm)) <= 2e-2
+
+
+@pytest.mark.parametrize("N", [1, 31, 33, 100, 257])
+def test_v2_bwd_causal(N):
+    *_, g, ref = run(case(2, N, 8, 2, 5100 + N))
+    check(g, ref)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (16, 2), (32, 2)])
+def test_v2_bwd_groupings(hq, hkv):
+    # 1, 4, 4 and 8 pairs per KV head: dK and dV sum over every head of the group
+    *_, g, ref = run(case(1, 130, hq, hkv, 5200 + hq + hkv))
+    check(g, ref)
+
+
+def test_v2_bwd_noncausal_and_logits():
+    *_, g, ref = run(case(2, 150, 8, 2, 5300, causal=False))
+    check(g, ref)
+    *_, g, ref = run(case(2, 150, 8, 2, 5301, logits=True))
+    check(g, ref)
+
+
+def test_v2_bwd_large_logits():
+    *_, g, ref = run(case(1, 200, 8, 2, 5400, qscale=6.0))
+    check(g, ref)
+
+
+def test_v2_bwd_deterministic():
+    c = case(1, 300, 8, 2, 5500)
+    lam = c["lam"].to(DEV)
+    _, lse, maps = da.diffattn_v2_fwd_train(c["q"], c["k"], c["v"], lam)
+    a = da.diffattn_v2_bwd(c["q"], c["k"], c["v"], c["dy"], lam, lse, maps)
+    b = da.diffattn_v2_bwd(c["q"], c["k"], c["v"], c["dy"], lam, lse, maps)
+    torch.cuda.synchronize()
+    for k in ("dq", "dk", "dv", "dlam"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_full_v2_bwd_8k_sampled():
+    # the V2 prefill workload (B=2, N=8192, 64 query / 8 KV heads, d=128, causal) in the launch
+    # configuration the benchmark times, checked where the oracle can take a part of the problem:
+    #  - the first 256 rows of one pair depend on the first 256 keys only (dQ and dlambda there);
+    #  - the last 64 rows of every pair of one KV group, against all 8192 keys, give those rows'
+    #    dQ and dlambda and the complete dK and dV of the last 64 keys (no earlier row sees them)
+    cfg = W.V2_GQA_8K
+    x = W.v2_inputs(cfg, device=DEV)
+    note(f"full v2 bwd: {cfg.name}")
+    g7 = torch.Generator(device=DEV).manual_seed(9)
+    dy = torch.randn((cfg.B, cfg.N, cfg.hq // 2, cfg.d), generator=g7, device=DEV).to(torch.bfloat16)
+    lam = x["lam"]
+    out, lse, maps = da.diffattn_v2_fwd_train(x["q"], x["k"], x["v"], lam, causal=True)
+    g = da.diffattn_v2_bwd(x["q"], x["k"], x["v"], dy, lam, lse, maps, causal=True)
+    torch.cuda.synchronize()
+    group = cfg.hq // cfg.hkv
+    M = 256
+    b, p = 0, 3
+    gk = (2 * p) // group
+    ref = oracle.v2_backward(f64(x["q"][b:b + 1, :M, 2 * p:2 * p + 2]), f64(x["k"][b:b + 1, :M, gk:gk + 1]),
+                             f64(x["v"][b:b + 1, :M, gk:gk + 1]), lam[b:b + 1, :M, p:p + 1].cpu().numpy(),
+                             f64(dy[b:b + 1, :M, p:p + 1]), causal=True)
+    assert relerr(g["dq"][b:b + 1, :M, 2 * p:2 * p + 2], ref["dq"]) <= TOL_REL
+    assert relerr(g["dlam"][b:b + 1, :M, p:p + 1], ref["dlam"]) <= TOL_REL
+    M = 64
+    b, gk = cfg.B - 1, cfg.hkv - 1
+    hs, ps = slice(gk * group, (gk + 1) * group), slice(gk * group // 2, (gk + 1) * group // 2)
+    ref = oracle.v2_backward(f64(x["q"][b:b + 1, -M:, hs]), f64(x["k"][b:b + 1, :, gk:gk + 1]),
+                             f64(x["v"][b:b + 1, :, gk:gk + 1]), lam[b:b + 1, -M:, ps].cpu().numpy(),
+                             f64(dy[b:b + 1, -M:, ps]), causal=True)
+    assert relerr(g["dq"][b:b + 1, -M:, hs], ref["dq"]) <= TOL_REL
+    assert relerr(g["dlam"][b:b + 1, -M:, ps], ref["dlam"]) <= TOL_REL
+    assert relerr(g["dk"][b:b + 1, -M:, gk:gk + 1], ref["dk"][:, -M:]) <= TOL_REL
+    assert relerr(g["dv"][b:b + 1, -M:, gk:gk + 1], ref["dv"][:, -M:]) <= TOL_REL
