@@ -34,6 +34,9 @@ FLOP_PER_PAIR_V2 = 512
 # backward: recomputed scores (2 x 2d), dP = go V^T (2 dv), dV (2 dv), dK and dQ of both maps
 # (2 x 2d each): 1280 per visible pair at d = 64, dv = 128
 FLOP_PER_PAIR_V1_BWD = 1280
+# V2 backward, per visible pair and query head at d = 128: recomputed scores (2d), dQ (2d), dK
+# (2d), and dP and dV (2d each per pair of heads, so d per head)
+FLOP_PER_PAIR_V2_BWD = 1024
 PAGE_SIZE = 256                # tokens per page of the paged decode legs
 DECODE_BYTES_PER_TOKEN = 2 * (64 + 64 + 128)
 
@@ -83,8 +86,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--secondary", default="32k,decode,v2,v2decode,bwd",
-                    help="comma list of extra workloads to time (32k, decode, v2, v2decode, bwd) or 'none'")
+    ap.add_argument("--secondary", default="32k,decode,v2,v2decode,bwd,v2bwd,fp8",
+                    help="comma list of extra workloads to time (32k, decode, v2, v2decode, bwd, v2bwd, fp8) or 'none'")
     ap.add_argument("--secondary-reps", type=int, default=10)
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the fp64 oracle on a sample (1) or not (0)")
     ap.add_argument("--copy-calibration", type=int, default=1,
@@ -300,6 +303,56 @@ def main():
         log(f"[bench]   training forward {avg_f:.3f} ms, backward {avg_b:.3f} ms -> "
             f"{fl_b / (avg_b * 1e-3) / 1e12:.1f} TFLOP/s")
         del x7, dy7, lse7, maps7, ws7
+    if "fp8" in which:
+        # the main workload with the score operands in fp8 (e4m3, dynamic absmax per (batch, head))
+        c9 = W.V1_PREFILL_2K
+        log(f"[bench] fp8 score operands, {c9.name}")
+        x9 = W.v1_inputs(c9, device=dev)
+        lam9 = da.diffattn_lambda(*(x9[k].to(dev) for k in ("lq1", "lk1", "lq2", "lk2")), c9.layer)
+        li9 = da.lambda_init(c9.layer)
+        o9 = torch.empty((c9.B, c9.N, c9.H, c9.dv), dtype=torch.bfloat16, device=dev)
+        qs9 = [da.diffattn_quantize_fp8(x9[k]) for k in ("q1", "q2", "k1", "k2")]
+        fq9 = lambda: [da.diffattn_quantize_fp8(x9[k], out=q[0]) for k, q in zip(("q1", "q2", "k1", "k2"), qs9)]
+        ff9 = lambda: da.diffattn_fwd_fp8(*(q[0] for q in qs9), *(q[1] for q in qs9), x9["v"], lam9, causal=True,
+                                          epilogue=True, lambda_init_value=li9, out=o9)
+        fq9()
+        ff9()
+        torch.cuda.synchronize()
+        avg_q, _ = time_launches(fq9, args.secondary_reps, torch)
+        avg, mn = time_launches(ff9, args.secondary_reps, torch)
+        fl9 = FLOP_PER_PAIR_V1 * c9.B * c9.H * causal_pairs(c9.N)
+        tf = fl9 / (avg * 1e-3) / 1e12
+        secondary["v1_prefill_2k_fp8_logits"] = {
+            "workload": c9.name + ", Q1 Q2 K1 K2 in fp8 e4m3", "kernel_avg_ms": round(avg, 4),
+            "kernel_min_ms": round(mn, 4), "flop": fl9, "TFLOP/s": round(tf, 2),
+            "quantize_four_operands_avg_ms": round(avg_q, 4)}
+        log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s (quantising Q1, Q2, K1, K2: {avg_q:.3f} ms)")
+        del x9, o9, qs9
+    if "v2bwd" in which:
+        # training step of the V2 prefill workload: the V2 training forward and the V2 backward
+        c8 = W.V2_GQA_8K
+        log(f"[bench] V2 backward, {c8.name}")
+        x8 = W.v2_inputs(c8, device=dev)
+        g8 = torch.Generator(device=dev).manual_seed(9)
+        dy8 = torch.randn((c8.B, c8.N, c8.hq // 2, c8.d), generator=g8, device=dev).to(torch.bfloat16)
+        ft8 = lambda: da.diffattn_v2_fwd_train(x8["q"], x8["k"], x8["v"], x8["lam"], causal=True)
+        _, lse8, maps8 = ft8()
+        ws8 = torch.empty(da.diffattn_v2_bwd_workspace_size(c8.B, c8.hq // 2, c8.N), dtype=torch.uint8, device=dev)
+        fb8 = lambda: da.diffattn_v2_bwd(x8["q"], x8["k"], x8["v"], dy8, x8["lam"], lse8, maps8, causal=True,
+                                         workspace=ws8)
+        fb8()
+        torch.cuda.synchronize()
+        avg_f, _ = time_launches(ft8, args.secondary_reps, torch)
+        avg_b, mn_b = time_launches(fb8, args.secondary_reps, torch)
+        fl8 = FLOP_PER_PAIR_V2_BWD * c8.B * c8.hq * causal_pairs(c8.N)
+        secondary["v2_backward_8k"] = {"workload": c8.name, "train_forward_avg_ms": round(avg_f, 4),
+                                       "backward_avg_ms": round(avg_b, 4), "backward_min_ms": round(mn_b, 4),
+                                       "flop": fl8, "flop_per_visible_pair_and_query_head": FLOP_PER_PAIR_V2_BWD,
+                                       "TFLOP/s": round(fl8 / (avg_b * 1e-3) / 1e12, 2),
+                                       "frac_of_bf16_peak": round(fl8 / (avg_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench]   training forward {avg_f:.3f} ms, backward {avg_b:.3f} ms -> "
+            f"{fl8 / (avg_b * 1e-3) / 1e12:.1f} TFLOP/s")
+        del x8, dy8, lse8, maps8, ws8
     if "v2decode" in which:
         c6 = W.V2_DECODE_64K
         log(f"[bench] {c6.name} (generating the cache on the device)")

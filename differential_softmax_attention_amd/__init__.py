@@ -37,7 +37,8 @@ EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "
             "diffattn_fwd", "diffattn_decode_workspace_size", "diffattn_decode", "diffattn_v2_fwd",
             "diffattn_v2_decode_workspace_size", "diffattn_v2_decode", "diffattn_fwd_train",
             "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd", "diffattn_decode_paged",
-            "diffattn_v2_decode_paged", "diffattn_v2_fwd_train", "diffattn_v2_bwd_workspace_size", "diffattn_v2_bwd")
+            "diffattn_v2_decode_paged", "diffattn_v2_fwd_train", "diffattn_v2_bwd_workspace_size", "diffattn_v2_bwd",
+            "diffattn_quantize_fp8", "diffattn_fwd_fp8")
 
 
 class DiffAttnError(RuntimeError):
@@ -103,6 +104,10 @@ def lib():
         L.diffattn_v2_bwd_workspace_size.argtypes = [i, i, i]
         L.diffattn_v2_bwd.restype = i
         L.diffattn_v2_bwd.argtypes = [i, T, T, T, T, vp, i, i, i, i, i, i, i, f, vp, vp, T, T, T, vp, vp, sz, vp]
+        L.diffattn_quantize_fp8.restype = i
+        L.diffattn_quantize_fp8.argtypes = [T, i, i, i, i, T, vp, vp, vp]
+        L.diffattn_fwd_fp8.restype = i
+        L.diffattn_fwd_fp8.argtypes = [T, T, T, T, vp, vp, vp, vp, T, i, i, i, i, i, i, vp, f, i, i, vp, f, f, T, vp]
         L.diffattn_v2_decode_paged.restype = i
         L.diffattn_v2_decode_paged.argtypes = [i, T, T, T, vp, i64, i, i, vp, vp, i, i, i, i, i, i, f, T, vp, sz,
                                                vp]
@@ -242,6 +247,38 @@ def diffattn_fwd_train(q1, q2, k1, k2, v, lam: torch.Tensor, causal: bool = True
                                     EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
                                     float(scale), _t4(out), lse.data_ptr(), maps.data_ptr(), _stream(q1.device)))
     return out, lse, maps
+
+
+def diffattn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None):
+    """Dynamic absmax fp8 (OCP e4m3) codes of a bf16 [B, N, H, dim] tensor, one scale per (b, h).
+    Returns (codes torch.float8_e4m3fn [B, N, H, dim], scales fp32 [B, H], amax fp32 [B, H])."""
+    B, N, H, dim = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if out is None:
+        out = torch.empty((B, N, H, dim), dtype=torch.float8_e4m3fn, device=x.device)
+    scales = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    amax = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    _check(lib().diffattn_quantize_fp8(_t4(x), B, N, H, dim, _t4(out), scales.data_ptr(), amax.data_ptr(),
+                                       _stream(x.device)))
+    return out, scales, amax
+
+
+def diffattn_fwd_fp8(q1, q2, k1, k2, sq1, sq2, sk1, sk2, v, lam: torch.Tensor, causal: bool = True,
+                     epilogue: bool = True, lambda_init_value: float = 0.8, norm_w: torch.Tensor | None = None,
+                     eps: float = 1e-5, scale: float = 0.0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """DIFF V1 forward with fp8 (e4m3) score operands and their [B, H] scales; v bf16 [B, Nk, H, dv].
+    Returns bf16 [B, Nq, H, dv]."""
+    B, Nq, H, d = q1.shape
+    Nk, dv = k1.shape[1], v.shape[3]
+    if out is None:
+        out = torch.empty((B, Nq, H, dv), dtype=torch.bfloat16, device=v.device)
+    _check(lib().diffattn_fwd_fp8(_t4(q1), _t4(q2), _t4(k1), _t4(k2), sq1.data_ptr(), sq2.data_ptr(),
+                                  sk1.data_ptr(), sk2.data_ptr(), _t4(v), B, H, Nq, Nk, d, dv, lam.data_ptr(),
+                                  float(lambda_init_value), int(bool(causal)),
+                                  EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps), float(scale),
+                                  _t4(out), _stream(v.device)))
+    return out
 
 
 def diffattn_v2_fwd_train(q, k, v, lam: torch.Tensor, causal: bool = True, scale: float = 0.0,

@@ -588,6 +588,84 @@ diffattn_status diffattn_bwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_
     return hip_status(diffattn::launch_bwd(a, workspace, (hipStream_t)stream), "diffattn_bwd launch");
 }
 
+// What the MFMA kernels read as 16-byte vectors of one-byte elements.
+static bool vec16_bytes_ok(const diffattn_tensor& t) {
+    return ((uintptr_t)t.ptr) % 16 == 0 && t.s_batch % 16 == 0 && t.s_seq % 16 == 0 && t.s_head % 16 == 0;
+}
+
+diffattn_status diffattn_quantize_fp8(diffattn_tensor x, int batch, int tokens, int heads, int dim,
+                                      diffattn_tensor out, float* scales, float* amax, void* stream) {
+    if (diffattn_status s = check_tensor(x, "x", DIFFATTN_BF16)) return s;
+    if (!out.ptr) return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8: out is null");
+    if (out.s_batch < 0 || out.s_seq < 0 || out.s_head < 0)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8: negative stride in out");
+    if (!scales || !amax) return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8: scales and amax must be non-null");
+    if (batch < 1 || tokens < 1 || heads < 1 || dim < 2 || dim % 2 != 0)
+        return fail(DIFFATTN_ERR_ARG,
+                    "diffattn_quantize_fp8: sizes must be >= 1 and dim even (batch=%d tokens=%d heads=%d dim=%d)",
+                    batch, tokens, heads, dim);
+    if (batch > 65535 || heads > 65535)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8: batch and heads must be <= 65535");
+    if (((uintptr_t)out.ptr) % 2 != 0 || out.s_batch % 2 != 0 || out.s_seq % 2 != 0 || out.s_head % 2 != 0)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8: out base and strides must be even (two codes per store)");
+    diffattn::Fp8QuantArgs a{};
+    a.x = x.ptr; a.out = out.ptr;
+    copy_strides(a.xs, x); copy_strides(a.os, out);
+    a.scales = scales; a.amax = amax;
+    a.batch = batch; a.tokens = tokens; a.heads = heads; a.dim = dim;
+    return hip_status(diffattn::launch_quantize_fp8(a, (hipStream_t)stream), "diffattn_quantize_fp8 launch");
+}
+
+diffattn_status diffattn_fwd_fp8(diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1, diffattn_tensor k2,
+                                 const float* sq1, const float* sq2, const float* sk1, const float* sk2,
+                                 diffattn_tensor v, int batch, int heads, int seq_q, int seq_k, int d, int dv,
+                                 const float* lambda, float lambda_init, int causal, diffattn_epilogue epi,
+                                 const float* norm_w, float eps, float scale, diffattn_tensor out, void* stream) {
+    const diffattn_tensor* f8[4] = {&q1, &q2, &k1, &k2};
+    const char* f8n[4] = {"q1", "q2", "k1", "k2"};
+    for (int i = 0; i < 4; ++i) {
+        if (!f8[i]->ptr) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: %s is null", f8n[i]);
+        if (f8[i]->s_batch < 0 || f8[i]->s_seq < 0 || f8[i]->s_head < 0)
+            return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: negative stride in %s", f8n[i]);
+    }
+    if (diffattn_status s = check_tensor(v, "v", DIFFATTN_BF16)) return s;
+    if (diffattn_status s = check_tensor(out, "out", DIFFATTN_BF16)) return s;
+    if (!sq1 || !sq2 || !sk1 || !sk2) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: scale arrays must be non-null");
+    if (!lambda) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: lambda is null");
+    if (batch < 1 || heads < 1 || seq_q < 1 || seq_k < 1 || d < 1 || dv < 1)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: sizes must be >= 1 (batch=%d heads=%d seq_q=%d seq_k=%d d=%d dv=%d)",
+                    batch, heads, seq_q, seq_k, d, dv);
+    if (heads > 65535 || batch > 65535) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: batch and heads must be <= 65535");
+    if (causal && seq_q > seq_k)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: causal needs seq_q (%d) <= seq_k (%d)", seq_q, seq_k);
+    if (epi != DIFFATTN_EPI_NONE && epi != DIFFATTN_EPI_RMSNORM_SCALE)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: unknown epilogue %d", (int)epi);
+    if (epi == DIFFATTN_EPI_RMSNORM_SCALE && !(std::isfinite(eps) && eps >= 0.f && std::isfinite(lambda_init)))
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: eps must be finite and >= 0, lambda_init finite");
+    if (!std::isfinite(scale)) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_fp8: scale must be finite");
+    if (d != 64 || dv != 128) return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_fwd_fp8: serves d = 64, dv = 128");
+    for (int i = 0; i < 4; ++i)
+        if (!vec16_bytes_ok(*f8[i]))
+            return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_fwd_fp8: %s needs a 16-byte aligned base and strides that "
+                        "are multiples of 16", f8n[i]);
+    if (!vec16_ok(v) || !vec16_ok(out))
+        return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_fwd_fp8: v and out need 16-byte alignment and strides that are "
+                    "multiples of 8 elements");
+    diffattn::MfmaFwdArgs a{};
+    a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.out = out.ptr;
+    copy_strides(a.q1s, q1); copy_strides(a.q2s, q2); copy_strides(a.k1s, k1); copy_strides(a.k2s, k2);
+    copy_strides(a.vs, v); copy_strides(a.os, out);
+    a.lam = lambda;
+    a.norm_w = norm_w;
+    a.batch = batch; a.heads = heads; a.seq_q = seq_q; a.seq_k = seq_k;
+    a.causal = causal ? 1 : 0;
+    a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
+    a.eps = eps; a.lambda_init = lambda_init;
+    a.scale_log2 = resolve_scale(scale, d) * 1.4426950408889634f;
+    a.sq1 = sq1; a.sq2 = sq2; a.sk1 = sk1; a.sk2 = sk2;
+    return hip_status(diffattn::launch_v1_fwd_fp8(a, (hipStream_t)stream), "diffattn_fwd_fp8 launch");
+}
+
 diffattn_status diffattn_lambda_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
                                     const float* dlambda, int n, int dim, float* dlq1, float* dlk1, float* dlq2,
                                     float* dlk2, void* stream) {

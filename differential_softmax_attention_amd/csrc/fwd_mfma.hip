@@ -55,30 +55,38 @@ constexpr float kRescaleThreshold = 8.0f;
 #define DA_PRIO_V2 0
 #endif
 
-template <int D, bool V2>
+template <int D, bool V2, bool F8 = false>
 struct Cfg {
     static constexpr int NW = V2 ? 8 : 4;              // waves per block
     static constexpr int NT = NW * 64;
     static constexpr int NK = V2 ? 1 : 2;               // K tiles per stage (V2 shares K)
-    static constexpr int K_CPR = D / 8;                 // 16-byte chunks per K row
+    static constexpr int K_ELT = F8 ? 1 : 2;            // bytes per K element (fp8 or bf16)
+    static constexpr int K_CPR = D * K_ELT / 16;        // 16-byte chunks per K row
     static constexpr int V_CPR = kDV / 8;
-    static constexpr int K_BYTES = kBN * D * 2;
+    static constexpr int K_BYTES = kBN * D * K_ELT;
     static constexpr int V_BYTES = kBN * kDV * 2;
     static constexpr int STAGE_BYTES = NK * K_BYTES + V_BYTES;
-    static constexpr int K_LOADS = kBN * K_CPR / NT;    // DMA loads per thread per K tile
+    // DMA loads per thread per K tile; fp8: the K1 and K2 tiles together take one load per thread
+    static constexpr int K_LOADS = F8 ? 1 : kBN * K_CPR / NT;
     static constexpr int V_LOADS = kBN * V_CPR / NT;
     static_assert(K_LOADS >= 1 && V_LOADS >= 1, "tile must cover every thread");
+    static_assert(!F8 || (!V2 && NK * kBN * K_CPR == NT), "fp8 K tiles: one 16-byte slot per thread");
 };
+
+// fp8 K tiles (32 rows of 64 bytes): chunk c of row r at c ^ ((r >> 2) & 3), so 16 consecutive
+// rows of one chunk fall on distinct banks
+__device__ __forceinline__ int f8_swz(int row) { return (row >> 2) & 3; }
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // offset of (b, token, head)'s two maps in the [batch, seq_q, heads, 2, 128] training output
 __device__ __forceinline__ int64_t row_major_maps(const MfmaFwdArgs& a, int b, int qrow, int h) {
     return (((int64_t)b * a.seq_q + qrow) * a.heads + h) * 2 * kDV;
 }
 
-template <int D, bool V2, bool CAUSAL, bool EPI>
+template <int D, bool V2, bool CAUSAL, bool EPI, bool F8 = false>
 __global__ __launch_bounds__(V2 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(V2 ? 1 : 2, 2)))
 void fwd_mfma_kernel(MfmaFwdArgs a) {
-    using C = Cfg<D, V2>;
+    using C = Cfg<D, V2, F8>;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x;
@@ -131,16 +139,32 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     // ---- Q fragments (B operand of S^T = K Q^T): lane (n, h2) holds q[n][16kk + 8h2 .. +7]
     constexpr int NKK = D / 16;
     bf16x8 bq1[NKK], bq2[NKK];
+    // fp8: lane (n, h2) holds q[n][32 h2 .. +31] (the fp8 MFMA takes k = 64 in one step; A and B
+    // operands use the same lane-to-k assignment, so any fixed one gives the dot product)
+    i32x8 fq1 = {}, fq2 = {};
     {
         const bool ok = qrow < a.seq_q;
         const int qr = ok ? qrow : 0;
-        const bf16* q1p = (const bf16*)a.q1 + b * a.q1s[0] + (int64_t)qr * a.q1s[1] + (int64_t)hq1 * a.q1s[2] + 8 * h2;
-        const bf16* q2p = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)qr * a.q2s[1] + (int64_t)hq2 * a.q2s[2] + 8 * h2;
+        if (F8) {
+            const unsigned char* q1p = (const unsigned char*)a.q1 + b * a.q1s[0] + (int64_t)qr * a.q1s[1] +
+                                       (int64_t)hq1 * a.q1s[2] + 32 * h2;
+            const unsigned char* q2p = (const unsigned char*)a.q2 + b * a.q2s[0] + (int64_t)qr * a.q2s[1] +
+                                       (int64_t)hq2 * a.q2s[2] + 32 * h2;
+            if (ok) {
+                const u32x4 x0 = *(const u32x4*)q1p, x1 = *(const u32x4*)(q1p + 16);
+                const u32x4 y0 = *(const u32x4*)q2p, y1 = *(const u32x4*)(q2p + 16);
+                fq1 = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+                fq2 = i32x8{(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3], (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
+            }
+        } else {
+            const bf16* q1p = (const bf16*)a.q1 + b * a.q1s[0] + (int64_t)qr * a.q1s[1] + (int64_t)hq1 * a.q1s[2] + 8 * h2;
+            const bf16* q2p = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)qr * a.q2s[1] + (int64_t)hq2 * a.q2s[2] + 8 * h2;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const bf16x8 z = {};
-            bq1[kk] = ok ? ld_global_bf16x8(q1p + 16 * kk) : z;
-            bq2[kk] = ok ? ld_global_bf16x8(q2p + 16 * kk) : z;
+            for (int kk = 0; kk < NKK; ++kk) {
+                const bf16x8 z = {};
+                bq1[kk] = ok ? ld_global_bf16x8(q1p + 16 * kk) : z;
+                bq2[kk] = ok ? ld_global_bf16x8(q2p + 16 * kk) : z;
+            }
         }
     }
 
@@ -165,11 +189,20 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     uint32_t koff1[C::K_LOADS], koff2[C::K_LOADS], voffg[C::V_LOADS];
 #pragma unroll
     for (int j = 0; j < C::K_LOADS; ++j) {
-        const int s = tid + j * C::NT;
-        krow[j] = s / C::K_CPR;
-        kcol[j] = (s % C::K_CPR) ^ k_swz<D>(krow[j]);
-        koff1[j] = (uint32_t)(krow[j] * a.k1s[1] + kcol[j] * 8) * 2u;
-        koff2[j] = (uint32_t)(krow[j] * a.k2s[1] + kcol[j] * 8) * 2u;
+        if (F8) {
+            // thread tid fills slot tid % 128 of the K1 (tid < 128) or K2 tile: byte offsets
+            const int s = tid & 127;
+            krow[j] = s / C::K_CPR;
+            kcol[j] = (s % C::K_CPR) ^ f8_swz(krow[j]);
+            koff1[j] = (uint32_t)(krow[j] * a.k1s[1] + kcol[j] * 16);
+            koff2[j] = (uint32_t)(krow[j] * a.k2s[1] + kcol[j] * 16);
+        } else {
+            const int s = tid + j * C::NT;
+            krow[j] = s / C::K_CPR;
+            kcol[j] = (s % C::K_CPR) ^ k_swz<D>(krow[j]);
+            koff1[j] = (uint32_t)(krow[j] * a.k1s[1] + kcol[j] * 8) * 2u;
+            koff2[j] = (uint32_t)(krow[j] * a.k2s[1] + kcol[j] * 8) * 2u;
+        }
     }
 #pragma unroll
     for (int j = 0; j < C::V_LOADS; ++j) {
@@ -183,15 +216,26 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         const uint32_t st = smem_lds + stage * C::STAGE_BYTES + wave_u * 64 * 16;
         const bool full = (kt + 1) * kBN <= a.seq_k;
         const int rows_left = a.seq_k - 1 - kt * kBN;   // last valid row within this tile
+        if (F8) {
+            // waves 0, 1 fill the K1 tile and waves 2, 3 the K2 tile (byte addressing)
+            const bool t1 = wave_u >= 2;
+            const int64_t rs = t1 ? a.k2s[1] : a.k1s[1];
+            const unsigned char* tb = (const unsigned char*)(t1 ? a.k2 : a.k1) + b * (t1 ? a.k2s[0] : a.k1s[0]) +
+                                      (int64_t)kvh * (t1 ? a.k2s[2] : a.k1s[2]) + (int64_t)kt * kBN * rs;
+            const uint32_t off = full ? (t1 ? koff2[0] : koff1[0])
+                                      : (uint32_t)(min(krow[0], rows_left) * rs + kcol[0] * 16);
+            dma16(tb, off, st);
+        } else {
 #pragma unroll
-        for (int t = 0; t < C::NK; ++t) {
-            const bf16* tb = (t == 0 ? kbase1 : kbase2) + (int64_t)kt * kBN * (t == 0 ? a.k1s[1] : a.k2s[1]);
-            const int64_t rs = t == 0 ? a.k1s[1] : a.k2s[1];
+            for (int t = 0; t < C::NK; ++t) {
+                const bf16* tb = (t == 0 ? kbase1 : kbase2) + (int64_t)kt * kBN * (t == 0 ? a.k1s[1] : a.k2s[1]);
+                const int64_t rs = t == 0 ? a.k1s[1] : a.k2s[1];
 #pragma unroll
-            for (int j = 0; j < C::K_LOADS; ++j) {
-                const uint32_t off = full ? (t == 0 ? koff1[j] : koff2[j])
-                                          : (uint32_t)(min(krow[j], rows_left) * rs + kcol[j] * 8) * 2u;
-                dma16(tb, off, st + t * C::K_BYTES + j * C::NT * 16);
+                for (int j = 0; j < C::K_LOADS; ++j) {
+                    const uint32_t off = full ? (t == 0 ? koff1[j] : koff2[j])
+                                              : (uint32_t)(min(krow[j], rows_left) * rs + kcol[j] * 8) * 2u;
+                    dma16(tb, off, st + t * C::K_BYTES + j * C::NT * 16);
+                }
             }
         }
         const bf16* vb = vbase + (int64_t)kt * kBN * a.vs[1];
@@ -206,13 +250,17 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     auto zero_tail = [&](int kt, int stage) {
         unsigned char* st = smem + stage * C::STAGE_BYTES;
         const u32x4 z = {0u, 0u, 0u, 0u};
+        if (F8) {
+            if (kt * kBN + krow[0] >= a.seq_k) *(u32x4*)(st + tid * 16) = z;
+        } else {
 #pragma unroll
-        for (int t = 0; t < C::NK; ++t)
+            for (int t = 0; t < C::NK; ++t)
 #pragma unroll
-            for (int j = 0; j < C::K_LOADS; ++j) {
-                const int s = tid + j * C::NT;
-                if (kt * kBN + krow[j] >= a.seq_k) *(u32x4*)(st + t * C::K_BYTES + s * 16) = z;
-            }
+                for (int j = 0; j < C::K_LOADS; ++j) {
+                    const int s = tid + j * C::NT;
+                    if (kt * kBN + krow[j] >= a.seq_k) *(u32x4*)(st + t * C::K_BYTES + s * 16) = z;
+                }
+        }
 #pragma unroll
         for (int j = 0; j < C::V_LOADS; ++j) {
             const int s = tid + j * C::NT;
@@ -225,6 +273,8 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     int koff[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) koff[kk] = n * (D * 2) + (((2 * kk + h2) ^ k_swz<D>(n)) * 16);
+    // fp8 K (A operand): row n, bytes 32 h2 .. +31 = logical chunks 2 h2 and 2 h2 + 1
+    const int kf0 = n * D + (((2 * h2) ^ f8_swz(n)) * 16), kf1 = n * D + (((2 * h2 + 1) ^ f8_swz(n)) * 16);
     // V^T (A operand of O^T) through the transposing read: 16-lane group G = lane/16 covers
     // channels ct*32 + (G&1)*16 .. +15 and key half h2 = G>>1; lane L supplies row
     // key0 + L/4 (key0 = 16kb + 8t + 4h2) and channels cbase + 4(L%4) .. +3.
@@ -242,7 +292,13 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) { o1[ct] = f32x16{}; o2[ct] = f32x16{}; }
     float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
-    const float c2 = a.scale_log2;
+    // score scale per map: softmax scale * log2(e), times the two fp8 dequantisation scales
+    float c2a = a.scale_log2, c2b = a.scale_log2;
+    if (F8) {
+        const int64_t sh = (int64_t)b * a.heads + hout;
+        c2a *= a.sq1[sh] * a.sk1[sh];
+        c2b *= a.sq2[sh] * a.sk2[sh];
+    }
 
     issue_tile(0, 0);
 
@@ -263,15 +319,25 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
 
         // S^T = K Q^T for both maps (fp32 accumulate)
         f32x16 s1 = f32x16{}, s2 = f32x16{};
+        if (F8) {
+            // one v_mfma_f32_32x32x64_f8f6f4 per map (OCP e4m3 operands, k = 64 = d)
+            auto frag = [&](const unsigned char* t) __attribute__((always_inline)) {
+                const u32x4 x0 = *(const u32x4*)(t + kf0), x1 = *(const u32x4*)(t + kf1);
+                return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+            };
+            s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag(Ks1), fq1, s1, 0, 0, 0, 0, 0, 0);
+            s2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag(Ks2), fq2, s2, 0, 0, 0, 0, 0, 0);
+        } else {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const bf16x8 ka = lds16(Ks1 + koff[kk]);
-            s1 = mfma32x32x16(ka, bq1[kk], s1);
-            if (V2) {
-                s2 = mfma32x32x16(ka, bq2[kk], s2);
-            } else {
-                const bf16x8 kb2 = lds16(Ks2 + koff[kk]);
-                s2 = mfma32x32x16(kb2, bq2[kk], s2);
+            for (int kk = 0; kk < NKK; ++kk) {
+                const bf16x8 ka = lds16(Ks1 + koff[kk]);
+                s1 = mfma32x32x16(ka, bq1[kk], s1);
+                if (V2) {
+                    s2 = mfma32x32x16(ka, bq2[kk], s2);
+                } else {
+                    const bf16x8 kb2 = lds16(Ks2 + koff[kk]);
+                    s2 = mfma32x32x16(kb2, bq2[kk], s2);
+                }
             }
         }
 
@@ -290,8 +356,8 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         float mx1 = s1[0], mx2 = s2[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) { mx1 = fmax_nc(mx1, s1[r]); mx2 = fmax_nc(mx2, s2[r]); }
-        mx1 = max_halves(mx1) * c2;
-        mx2 = max_halves(mx2) * c2;
+        mx1 = max_halves(mx1) * c2a;
+        mx2 = max_halves(mx2) * c2b;
         const bool need = (mx1 > m1 + kRescaleThreshold) || (mx2 > m2 + kRescaleThreshold);
         if (__builtin_amdgcn_ballot_w64(need)) {
             const float mn1 = fmax_nc(m1, mx1), mn2 = fmax_nc(m2, mx2);
@@ -317,8 +383,8 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = kb * 8 + 2 * j;
-                q1p[j] = bf16x2{(bf16)fast_exp2(fmaf(s1[r], c2, -m1)), (bf16)fast_exp2(fmaf(s1[r + 1], c2, -m1))};
-                q2p[j] = bf16x2{(bf16)fast_exp2(fmaf(s2[r], c2, -m2)), (bf16)fast_exp2(fmaf(s2[r + 1], c2, -m2))};
+                q1p[j] = bf16x2{(bf16)fast_exp2(fmaf(s1[r], c2a, -m1)), (bf16)fast_exp2(fmaf(s1[r + 1], c2a, -m1))};
+                q2p[j] = bf16x2{(bf16)fast_exp2(fmaf(s2[r], c2b, -m2)), (bf16)fast_exp2(fmaf(s2[r + 1], c2b, -m2))};
                 if (j & 1) {
                     lb1 = __builtin_amdgcn_fdot2_f32_bf16(q1p[j], ones, lb1, false);
                     lb2 = __builtin_amdgcn_fdot2_f32_bf16(q2p[j], ones, lb2, false);
@@ -457,9 +523,9 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     }
 }
 
-template <int D, bool V2>
+template <int D, bool V2, bool F8 = false>
 hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
-    using C = Cfg<D, V2>;
+    using C = Cfg<D, V2, F8>;
     const int pairs_per_block = V2 ? a.kv_group / 2 : 1;
     const int BM = 32 * (C::NW / pairs_per_block);
     const int n_units = V2 ? a.batch * (a.heads * 2 / a.kv_group) : a.batch * a.heads;
@@ -467,11 +533,11 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)(nqt * n_units));
     const size_t smem = 2 * C::STAGE_BYTES;
     if (a.causal) {
-        if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, true>), grid, dim3(C::NT), smem, stream, a);
-        else hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, false>), grid, dim3(C::NT), smem, stream, a);
+        if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, true, F8>), grid, dim3(C::NT), smem, stream, a);
+        else hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, false, F8>), grid, dim3(C::NT), smem, stream, a);
     } else {
-        if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, false, true>), grid, dim3(C::NT), smem, stream, a);
-        else hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, false, false>), grid, dim3(C::NT), smem, stream, a);
+        if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, false, true, F8>), grid, dim3(C::NT), smem, stream, a);
+        else hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, false, false, F8>), grid, dim3(C::NT), smem, stream, a);
     }
     return hipGetLastError();
 }
@@ -480,5 +546,6 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream) { return launch_fwd<64, false>(a, stream); }
 hipError_t launch_v2_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream) { return launch_fwd<128, true>(a, stream); }
+hipError_t launch_v1_fwd_fp8(const MfmaFwdArgs& a, hipStream_t stream) { return launch_fwd<64, false, true>(a, stream); }
 
 }  // namespace diffattn

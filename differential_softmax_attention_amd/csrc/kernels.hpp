@@ -50,10 +50,14 @@ struct MfmaFwdArgs {
     // A1 V and A2 V in fp32 (V2: heads = pairs, the maps of query heads 2p and 2p+1)
     float* lse;
     float* maps;
+    // fp8 score operands (launch_v1_fwd_fp8): Q1, Q2, K1, K2 hold OCP e4m3 codes (strides in bytes)
+    // and these [batch, heads] factors turn the codes back into values
+    const float *sq1, *sq2, *sk1, *sk2;
 };
 
 hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
+hipError_t launch_v1_fwd_fp8(const MfmaFwdArgs& a, hipStream_t stream);
 
 // Split-K decode (bf16, d = 64, dv = 128).
 // Paged KV cache (block_table non-null): each cache tensor is a pool of pages whose batch stride
@@ -166,5 +170,18 @@ struct V2BwdArgs {
 
 size_t v2_bwd_workspace_bytes(int batch, int h, int seq);
 hipError_t launch_v2_bwd(V2BwdArgs a, void* workspace, hipStream_t stream);
+
+// fp8 quantisation of a bf16 [batch, tokens, heads, dim] view (dim even): per (batch, head)
+// amax = max |x|, scale s = amax / 448 (1 if amax = 0), out = OCP e4m3 codes of x / s.
+struct Fp8QuantArgs {
+    const void* x;
+    void* out;
+    int64_t xs[3], os[3];   // element strides (out: bytes)
+    float* scales;          // [batch, heads], written
+    float* amax;            // [batch, heads], written
+    int batch, tokens, heads, dim;
+};
+
+hipError_t launch_quantize_fp8(const Fp8QuantArgs& a, hipStream_t stream);
 
 }  // namespace diffattn

@@ -124,6 +124,44 @@ diffattn_status diffattn_fwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_
                              void* stream);
 
 /*
+ * Dynamic absmax quantisation of a score operand (Q1, Q2, K1 or K2) to fp8, OCP e4m3 (4 exponent
+ * bits, bias 7, 3 mantissa bits, largest finite value 448), for diffattn_fwd_fp8. The pages report
+ * DIFF's advantage for attention logits under dynamic absmax post-training quantisation
+ * ("softmax can't say zero, so it subtracts", section "Outliers, and the low-bit claim"); the
+ * granularity they leave open is taken here as one scale per (batch, head) slice:
+ *   amax[b, h] = max |x[b, :, h, :]|,  scales[b, h] = amax / 448 (1 when amax = 0),
+ *   out = e4m3 code of x / scales[b, h], rounded to nearest even (fp32 division).
+ *  x: bf16 [batch, tokens, heads, dim] view, finite values; dim even.
+ *  out: one-byte [batch, tokens, heads, dim] view (strides in bytes, even), written with the codes.
+ *  scales, amax: DEVICE fp32 [batch, heads] contiguous, written.
+ *  Kernels: per-block maxima merged by an atomic max on the fp32 bit pattern (exact, so the result
+ *  does not depend on the order), then the conversion (v_cvt_pk_fp8_f32).
+ *  Errors: ERR_ARG (null pointers, sizes, odd dim or strides), ERR_HIP.
+ */
+diffattn_status diffattn_quantize_fp8(diffattn_tensor x, int batch, int tokens, int heads, int dim,
+                                      diffattn_tensor out, float* scales, float* amax, void* stream);
+
+/*
+ * DIFF V1 forward with the attention logits taken on the fp8 matrix cores: S_k = Q_k K_k^T with
+ * e4m3 operands (one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 tile and map), each product scaled
+ * back by sq_k[b, h] * sk_k[b, h] in fp32; the softmaxes, the difference, the products with V
+ * (bf16) and the epilogue as in diffattn_fwd.
+ *  q1, q2: fp8 [batch, seq_q, heads, d];  k1, k2: fp8 [batch, seq_k, heads, d] (codes as written
+ *  by diffattn_quantize_fp8; strides in bytes, multiples of 16, 16-byte aligned bases).
+ *  sq1, sq2, sk1, sk2: DEVICE fp32 [batch, heads], the codes' scales.
+ *  v, out, lambda, lambda_init, causal, epi, norm_w, eps, scale: as in diffattn_fwd (bf16).
+ *  Serves d = 64, dv = 128 only. Errors: ERR_ARG, ERR_UNSUPPORTED (other d, dv, alignments),
+ *  ERR_HIP.
+ */
+diffattn_status diffattn_fwd_fp8(diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,
+                                 diffattn_tensor k2, const float* sq1, const float* sq2,
+                                 const float* sk1, const float* sk2, diffattn_tensor v, int batch,
+                                 int heads, int seq_q, int seq_k, int d, int dv, const float* lambda,
+                                 float lambda_init, int causal, diffattn_epilogue epi,
+                                 const float* norm_w, float eps, float scale, diffattn_tensor out,
+                                 void* stream);
+
+/*
  * Bytes of device workspace diffattn_decode needs for these sizes (0 on invalid sizes).
  * The workspace holds per-split partial results of both maps (running max, sum and a dv-wide
  * accumulator per map) in fp32.

@@ -420,3 +420,55 @@ def v2_train_stats(q, k, v, causal=True, scale=None):
     gk = np.stack([k[:, :, (2 * p) // group] for p in range(h)], axis=2)      # [B, N, h, d]
     gv = np.stack([v[:, :, (2 * p) // group] for p in range(h)], axis=2)
     return v1_train_stats(q[:, :, 0::2], q[:, :, 1::2], gk, gk, gv, causal=causal, scale=scale)
+
+
+# ------------------------------------------------------------------------------------------------
+# fp8 score operands. OCP e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+# holds the subnormals m * 2^-9; the largest finite value is 448 (field 15, mantissa 6); field 15
+# with mantissa 7 is NaN; there is no infinity.
+# ------------------------------------------------------------------------------------------------
+
+def e4m3_encode(x):
+    """Codes (uint8) of fp32 values, rounded to nearest with ties to even. Magnitudes from 464 up
+    (448 plus half a step) have no finite code and give NaN (0x7f), as does NaN."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x.astype(np.float64))
+    code = np.zeros(x.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)          # 0..8; 8 is the first normal
+    nrm = ~sub & np.isfinite(a)
+    mant, ex = np.frexp(a[nrm])                                          # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex - 1                                                           # a = (2 mant) * 2^e, 2 mant in [1, 2)
+    q = np.rint((2.0 * mant - 1.0) * 8.0).astype(np.int64)              # 0..8
+    e = e + (q == 8)
+    q = np.where(q == 8, 0, q)
+    code[nrm] = ((e + 7) << 3) | q
+    code[(a >= 464.0) | np.isnan(a)] = 0x7F
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def e4m3_decode(code):
+    """Values (float64) of e4m3 codes; NaN for 0x7f and 0xff."""
+    c = np.asarray(code, dtype=np.int64)
+    E, m = (c >> 3) & 15, c & 7
+    v = np.where(E == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (E - 7))
+    v = np.where((E == 15) & (m == 7), np.nan, v)
+    return np.where(c & 0x80, -v, v)
+
+
+def quantize_fp8(x):
+    """Dynamic absmax quantisation of a [B, N, H, dim] score operand, one scale per (batch, head)
+    slice (the granularity the pages leave open): amax = max |x|, s = amax / 448 in fp32 (1 when
+    amax is 0), code = e4m3(x / s) with the division in fp32. Returns (codes uint8, s [B, H] fp32).
+    "softmax can't say zero, so it subtracts", section "Outliers, and the low-bit claim"."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=(1, 3))                               # [B, H]
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    codes = e4m3_encode(x / s[:, None, :, None])
+    return codes, s
+
+
+def dequantize_fp8(codes, s):
+    """code * s per (batch, head) slice, in float64."""
+    return e4m3_decode(codes) * np.asarray(s, dtype=np.float64)[:, None, :, None]
