@@ -7,9 +7,10 @@ forward. Inputs are synthetic (seeded) and resident in HBM before timing starts.
 line on stdout; progress goes to stderr.
 
 Also measured in the same run (reported under "secondary"): the 32K-token prefill with a planted
-needle, the 64K-entry V1 decode and the V2 decode (GB/s against HBM), the V2 GQA prefill and the
-V1 backward pass on the main workload; and the fp64 oracle on a bounded sample of the main
-workload, timed on the host cores ("cpu_baseline").
+needle, the 64K-entry V1 decode and the V2 decode, each also on a paged cache (GB/s against HBM),
+the V2 GQA prefill (lambda given and from its logits), the V1 backward on the main workload, the
+V2 backward on the V2 prefill workload, the main workload with fp8 score operands; and the fp64
+oracle on a bounded sample of the main workload, timed on the host cores ("cpu_baseline").
 
 Throughput counts algorithmic work only: 768 flop per visible (query, key) pair for V1 (two
 QK^T products of width 64 and two PV products of width 128), 512 per visible pair and query head
