@@ -38,7 +38,7 @@ EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "
             "diffattn_v2_decode_workspace_size", "diffattn_v2_decode", "diffattn_fwd_train",
             "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd", "diffattn_decode_paged",
             "diffattn_v2_decode_paged", "diffattn_v2_fwd_train", "diffattn_v2_bwd_workspace_size", "diffattn_v2_bwd",
-            "diffattn_quantize_fp8", "diffattn_fwd_fp8")
+            "diffattn_quantize_fp8", "diffattn_fwd_fp8", "diffattn_fwd_lambda")
 
 
 class DiffAttnError(RuntimeError):
@@ -104,6 +104,9 @@ def lib():
         L.diffattn_v2_bwd_workspace_size.argtypes = [i, i, i]
         L.diffattn_v2_bwd.restype = i
         L.diffattn_v2_bwd.argtypes = [i, T, T, T, T, vp, i, i, i, i, i, i, i, f, vp, vp, T, T, T, vp, vp, sz, vp]
+        L.diffattn_fwd_lambda.restype = i
+        L.diffattn_fwd_lambda.argtypes = [i, T, T, T, T, T, i, i, i, i, i, i, vp, vp, vp, vp, i, i, vp, i, i, vp, f, f,
+                                          T, vp]
         L.diffattn_quantize_fp8.restype = i
         L.diffattn_quantize_fp8.argtypes = [T, i, i, i, i, T, vp, vp, vp]
         L.diffattn_fwd_fp8.restype = i
@@ -247,6 +250,26 @@ def diffattn_fwd_train(q1, q2, k1, k2, v, lam: torch.Tensor, causal: bool = True
                                     EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
                                     float(scale), _t4(out), lse.data_ptr(), maps.data_ptr(), _stream(q1.device)))
     return out, lse, maps
+
+
+def diffattn_fwd_lambda(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, causal: bool = True,
+                        epilogue: bool = True, norm_w: torch.Tensor | None = None, eps: float = 1e-5,
+                        scale: float = 0.0, out: torch.Tensor | None = None, lam_out: torch.Tensor | None = None):
+    """DIFF V1 forward with lambda from its four fp32 [H, lam_dim] vectors computed in the same pass.
+    Returns (out [B, Nq, H, dv], lambda [H] fp32)."""
+    B, Nq, H, d = q1.shape
+    Nk, dv = k1.shape[1], v.shape[3]
+    vecs = [x.reshape(H, -1).contiguous() for x in (lq1, lk1, lq2, lk2)]
+    if out is None:
+        out = torch.empty((B, Nq, H, dv), dtype=q1.dtype, device=q1.device)
+    if lam_out is None:
+        lam_out = torch.empty((H,), dtype=torch.float32, device=q1.device)
+    _check(lib().diffattn_fwd_lambda(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1), _t4(k2), _t4(v), B, H, Nq, Nk, d,
+                                     dv, *(x.data_ptr() for x in vecs), vecs[0].shape[1], int(layer),
+                                     lam_out.data_ptr(), int(bool(causal)),
+                                     EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
+                                     float(scale), _t4(out), _stream(q1.device)))
+    return out, lam_out
 
 
 def diffattn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None):

@@ -63,7 +63,8 @@ static diffattn_status fwd_impl(diffattn_dtype dtype, diffattn_tensor q1, diffat
                                 diffattn_tensor k2, diffattn_tensor v, int batch, int heads, int seq_q, int seq_k,
                                 int d, int dv, const float* lambda, float lambda_init, int causal,
                                 diffattn_epilogue epi, const float* norm_w, float eps, float scale,
-                                diffattn_tensor out, float* lse, float* maps, void* stream, const char* fn) {
+                                diffattn_tensor out, float* lse, float* maps, void* stream, const char* fn,
+                                const float* const* lamvec = nullptr, int lam_dim = 0) {
     if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     const diffattn_tensor* ts[6] = {&q1, &q2, &k1, &k2, &v, &out};
     const char* names[6] = {"q1", "q2", "k1", "k2", "v", "out"};
@@ -104,7 +105,18 @@ static diffattn_status fwd_impl(diffattn_dtype dtype, diffattn_tensor q1, diffat
         a.scale_log2 = sc * 1.4426950408889634f;
         a.lse = lse;
         a.maps = maps;
+        if (lamvec) {
+            // lambda from its vectors inside the kernel; `lambda` receives it
+            a.lq1 = lamvec[0]; a.lk1 = lamvec[1]; a.lq2 = lamvec[2]; a.lk2 = lamvec[3];
+            a.lam_dim = lam_dim;
+            a.lam_out = const_cast<float*>(lambda);
+        }
         return hip_status(diffattn::launch_v1_fwd_mfma(a, st), fn);
+    }
+    if (lamvec) {
+        hipError_t e = diffattn::launch_lambda(lamvec[0], lamvec[1], lamvec[2], lamvec[3], heads, lam_dim, lambda_init,
+                                               const_cast<float*>(lambda), st);
+        if (e != hipSuccess) return hip_status(e, fn);
     }
     diffattn::GenericArgs a{};
     a.q1 = q1.ptr; a.q2 = q2.ptr; a.k1 = k1.ptr; a.k2 = k2.ptr; a.v = v.ptr; a.out = out.ptr;
@@ -150,6 +162,22 @@ diffattn_status diffattn_fwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_
                              diffattn_tensor out, void* stream) {
     return fwd_impl(dtype, q1, q2, k1, k2, v, batch, heads, seq_q, seq_k, d, dv, lambda, lambda_init, causal, epi,
                     norm_w, eps, scale, out, nullptr, nullptr, stream, "diffattn_fwd");
+}
+
+diffattn_status diffattn_fwd_lambda(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,
+                                    diffattn_tensor k2, diffattn_tensor v, int batch, int heads, int seq_q, int seq_k,
+                                    int d, int dv, const float* lq1, const float* lk1, const float* lq2,
+                                    const float* lk2, int lam_dim, int layer, float* lambda_out, int causal,
+                                    diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                                    diffattn_tensor out, void* stream) {
+    if (!lq1 || !lk1 || !lq2 || !lk2 || !lambda_out)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_lambda: lambda vectors and lambda_out must be non-null");
+    if (lam_dim < 1) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_lambda: lam_dim=%d must be >= 1", lam_dim);
+    if (layer < 1) return fail(DIFFATTN_ERR_ARG, "diffattn_fwd_lambda: layer=%d must be >= 1", layer);
+    const float* vecs[4] = {lq1, lk1, lq2, lk2};
+    return fwd_impl(dtype, q1, q2, k1, k2, v, batch, heads, seq_q, seq_k, d, dv, lambda_out,
+                    (float)diffattn_lambda_init(layer), causal, epi, norm_w, eps, scale, out, nullptr, nullptr, stream,
+                    "diffattn_fwd_lambda", vecs, lam_dim);
 }
 
 size_t diffattn_decode_workspace_size(int batch, int heads, int cache_len, int dv) {

@@ -83,7 +83,7 @@ __device__ __forceinline__ int64_t row_major_maps(const MfmaFwdArgs& a, int b, i
     return (((int64_t)b * a.seq_q + qrow) * a.heads + h) * 2 * kDV;
 }
 
-template <int D, bool V2, bool CAUSAL, bool EPI, bool F8 = false>
+template <int D, bool V2, bool CAUSAL, bool EPI, bool F8 = false, bool LAMF = false>
 __global__ __launch_bounds__(V2 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(V2 ? 1 : 2, 2)))
 void fwd_mfma_kernel(MfmaFwdArgs a) {
     using C = Cfg<D, V2, F8>;
@@ -302,6 +302,24 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
 
     issue_tile(0, 0);
 
+    // V1 lambda from its re-parameterisation (LAMF): the lambda kernel's arithmetic (lane-strided
+    // fp32 dot products, the wave butterfly, expf), so the value is the one diffattn_lambda
+    // writes; one block per head stores it. Placed after the first tile's DMA is issued, so the
+    // vector loads overlap it.
+    float lam_fused = 0.f;
+    if (LAMF) {
+        const int64_t base = (int64_t)hout * a.lam_dim;
+        float d1 = 0.f, d2 = 0.f;
+        for (int c = lane; c < a.lam_dim; c += 64) {
+            d1 = fmaf(a.lq1[base + c], a.lk1[base + c], d1);
+            d2 = fmaf(a.lq2[base + c], a.lk2[base + c], d2);
+        }
+        d1 = wave_sum(d1);
+        d2 = wave_sum(d2);
+        lam_fused = expf(d1) - expf(d2) + a.lambda_init;
+        if (a.lam_out && b == 0 && qt == 0 && tid == 0) a.lam_out[hout] = lam_fused;
+    }
+
     for (int kt = 0; kt < nkt; ++kt) {
         const int stage = kt & 1;
         __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this thread's DMA landed
@@ -452,7 +470,7 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         lam = (qrow < a.seq_q) ? a.lam[b * a.lams[0] + (int64_t)qrow * a.lams[1] + (int64_t)hout * a.lams[2]] : 0.f;
         if (a.lam_sigmoid) lam = sigmoid_f32(lam);
     } else {
-        lam = a.lam[hout];
+        lam = LAMF ? lam_fused : a.lam[hout];
     }
     const float r1 = 1.f / l1;
     const float r2 = lam / l2;
@@ -532,6 +550,16 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
     const int nqt = (a.seq_q + BM - 1) / BM;
     const dim3 grid((unsigned)(nqt * n_units));
     const size_t smem = 2 * C::STAGE_BYTES;
+    if (!V2 && !F8 && a.lq1) {   // lambda from its vectors inside the kernel
+        if (a.causal) {
+            if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, true, F8, true>), grid, dim3(C::NT), smem, stream, a);
+            else hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, false, F8, true>), grid, dim3(C::NT), smem, stream, a);
+        } else {
+            if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, false, true, F8, true>), grid, dim3(C::NT), smem, stream, a);
+            else hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, false, false, F8, true>), grid, dim3(C::NT), smem, stream, a);
+        }
+        return hipGetLastError();
+    }
     if (a.causal) {
         if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, true, F8>), grid, dim3(C::NT), smem, stream, a);
         else hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, false, F8>), grid, dim3(C::NT), smem, stream, a);

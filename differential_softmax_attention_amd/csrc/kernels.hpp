@@ -53,6 +53,11 @@ struct MfmaFwdArgs {
     // fp8 score operands (launch_v1_fwd_fp8): Q1, Q2, K1, K2 hold OCP e4m3 codes (strides in bytes)
     // and these [batch, heads] factors turn the codes back into values
     const float *sq1, *sq2, *sk1, *sk2;
+    // V1 lambda computed in the kernel (lq1 non-null): exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init
+    // from the four [heads, lam_dim] vector sets, written to lam_out (optional)
+    const float *lq1, *lk1, *lq2, *lk2;
+    int lam_dim;
+    float* lam_out;
 };
 
 hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);

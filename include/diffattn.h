@@ -124,6 +124,26 @@ diffattn_status diffattn_fwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_
                              void* stream);
 
 /*
+ * DIFF V1 forward with lambda computed from its re-parameterisation in the same pass ("Noise-
+ * Canceling Attention by Subtraction", section "Making lambda learnable and stable"): for head h,
+ * lambda_h = exp(lq1[h] . lk1[h]) - exp(lq2[h] . lk2[h]) + lambda_init(layer), then diffattn_fwd
+ * with lambda_init = lambda_init(layer) in the epilogue. The whole forward step is one kernel.
+ *  lq1, lk1, lq2, lk2: DEVICE fp32 [heads, lam_dim] contiguous.  layer >= 1.
+ *  lambda_out: DEVICE fp32 [heads], written with lambda (bit-identical to diffattn_lambda's
+ *  output for the same vectors), as the backward pass needs it.
+ *  Other arguments as in diffattn_fwd. The bf16 d = 64, dv = 128 MFMA kernel computes lambda in
+ *  the kernel; other shapes run the lambda kernel, then the generic kernel.
+ *  Errors: as diffattn_fwd, and ERR_ARG for null vectors or lambda_out, lam_dim < 1, layer < 1.
+ */
+diffattn_status diffattn_fwd_lambda(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,
+                                    diffattn_tensor k1, diffattn_tensor k2, diffattn_tensor v,
+                                    int batch, int heads, int seq_q, int seq_k, int d, int dv,
+                                    const float* lq1, const float* lk1, const float* lq2,
+                                    const float* lk2, int lam_dim, int layer, float* lambda_out,
+                                    int causal, diffattn_epilogue epi, const float* norm_w,
+                                    float eps, float scale, diffattn_tensor out, void* stream);
+
+/*
  * Dynamic absmax quantisation of a score operand (Q1, Q2, K1 or K2) to fp8, OCP e4m3 (4 exponent
  * bits, bias 7, 3 mantissa bits, largest finite value 448), for diffattn_fwd_fp8. The pages report
  * DIFF's advantage for attention logits under dynamic absmax post-training quantisation
