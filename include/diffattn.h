@@ -150,12 +150,14 @@ diffattn_status diffattn_fwd_lambda(diffattn_dtype dtype, diffattn_tensor q1, di
  * ("softmax can't say zero, so it subtracts", section "Outliers, and the low-bit claim"); the
  * granularity they leave open is taken here as one scale per (batch, head) slice:
  *   amax[b, h] = max |x[b, :, h, :]|,  scales[b, h] = amax / 448 (1 when amax = 0),
- *   out = e4m3 code of x / scales[b, h], rounded to nearest even (fp32 division).
+ *   out = e4m3 code of x * (448 / amax) (fp32 product; 1 when amax = 0), rounded to nearest
+ *   even, so x is about out * scales[b, h].
  *  x: bf16 [batch, tokens, heads, dim] view, finite values; dim even.
  *  out: one-byte [batch, tokens, heads, dim] view (strides in bytes, even), written with the codes.
  *  scales, amax: DEVICE fp32 [batch, heads] contiguous, written.
- *  Kernels: per-block maxima merged by an atomic max on the fp32 bit pattern (exact, so the result
- *  does not depend on the order), then the conversion (v_cvt_pk_fp8_f32).
+ *  Kernels: one block per (batch, head) slice when there are at least 256 short slices (up to
+ *  4096 x 128 elements), else per-block maxima merged by an atomic max on the fp32 bit pattern (exact, so the result
+ *  does not depend on the order) and a conversion kernel; conversion by v_cvt_pk_fp8_f32.
  *  Errors: ERR_ARG (null pointers, sizes, odd dim or strides), ERR_HIP.
  */
 diffattn_status diffattn_quantize_fp8(diffattn_tensor x, int batch, int tokens, int heads, int dim,

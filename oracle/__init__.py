@@ -459,13 +459,17 @@ def e4m3_decode(code):
 
 def quantize_fp8(x):
     """Dynamic absmax quantisation of a [B, N, H, dim] score operand, one scale per (batch, head)
-    slice (the granularity the pages leave open): amax = max |x|, s = amax / 448 in fp32 (1 when
-    amax is 0), code = e4m3(x / s) with the division in fp32. Returns (codes uint8, s [B, H] fp32).
+    slice (the granularity the pages leave open): amax = max |x|, s = amax / 448 and
+    r = 448 / amax in fp32 (both 1 when amax is 0), code = e4m3(x * r) with the product in fp32;
+    x is about code * s. Returns (codes uint8, s [B, H] fp32).
     "softmax can't say zero, so it subtracts", section "Outliers, and the low-bit claim"."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x), axis=(1, 3))                               # [B, H]
-    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
-    codes = e4m3_encode(x / s[:, None, :, None])
+    pos = amax > 0
+    safe = np.where(pos, amax, np.float32(1.0)).astype(np.float32)
+    s = np.where(pos, safe / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    r = np.where(pos, np.float32(448.0) / safe, np.float32(1.0)).astype(np.float32)
+    codes = e4m3_encode(x * r[:, None, :, None])
     return codes, s
 
 

@@ -39,7 +39,9 @@ def gpu_codes(x):
     return codes.view(torch.uint8).cpu().numpy(), s.cpu().numpy(), amax.cpu().numpy()
 
 
-@pytest.mark.parametrize("B,N,H,dim,seed", [(1, 1, 1, 2, 1), (2, 100, 3, 64, 2), (1, 333, 2, 128, 3)])
+@pytest.mark.parametrize("B,N,H,dim,seed", [(1, 1, 1, 2, 1), (2, 100, 3, 64, 2), (1, 333, 2, 128, 3),
+                                             (1, 5000, 2, 128, 4),    # long slices: the multi-block path
+                                             (4, 40, 64, 64, 5)])     # 256 slices: one block per slice
 def test_quantize_codes_bit_exact(B, N, H, dim, seed):
     note(f"fp8 quantise B={B} N={N} H={H} dim={dim}")
     # slices of very different magnitudes, so small values fall into the subnormal codes
