@@ -38,7 +38,7 @@ EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "
             "diffattn_v2_decode_workspace_size", "diffattn_v2_decode", "diffattn_fwd_train",
             "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd", "diffattn_decode_paged",
             "diffattn_v2_decode_paged", "diffattn_v2_fwd_train", "diffattn_v2_bwd_workspace_size", "diffattn_v2_bwd",
-            "diffattn_quantize_fp8", "diffattn_fwd_fp8", "diffattn_fwd_lambda")
+            "diffattn_quantize_fp8", "diffattn_fwd_fp8", "diffattn_fwd_lambda", "diffattn_probe_mfma_peak")
 
 
 class DiffAttnError(RuntimeError):
@@ -104,6 +104,8 @@ def lib():
         L.diffattn_v2_bwd_workspace_size.argtypes = [i, i, i]
         L.diffattn_v2_bwd.restype = i
         L.diffattn_v2_bwd.argtypes = [i, T, T, T, T, vp, i, i, i, i, i, i, i, f, vp, vp, T, T, T, vp, vp, sz, vp]
+        L.diffattn_probe_mfma_peak.restype = i
+        L.diffattn_probe_mfma_peak.argtypes = [vp, i, i, ctypes.POINTER(ctypes.c_double), vp]
         L.diffattn_fwd_lambda.restype = i
         L.diffattn_fwd_lambda.argtypes = [i, T, T, T, T, T, i, i, i, i, i, i, vp, vp, vp, vp, i, i, vp, i, i, vp, f, f,
                                           T, vp]
@@ -492,6 +494,15 @@ def diffattn_v2_decode_paged(q, k_pages, v_pages, block_table: torch.Tensor, lam
                                           float(scale), _t4(out),
                                           workspace.data_ptr(), workspace.numel(), _stream(q.device)))
     return out.squeeze(1)
+
+
+def diffattn_probe_mfma_peak(blocks: int = 4096, iters: int = 2000, device="cuda") -> tuple:
+    """Launch the dense bf16 MFMA rate probe once; returns (output tensor, flop of the launch)."""
+    out = torch.empty((blocks * 256,), dtype=torch.float32, device=device)
+    flop = ctypes.c_double(0.0)
+    _check(lib().diffattn_probe_mfma_peak(out.data_ptr(), int(blocks), int(iters), ctypes.byref(flop),
+                                          _stream(out.device)))
+    return out, flop.value
 
 
 def default_scale(d: int) -> float:

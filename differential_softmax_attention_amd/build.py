@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
-SOURCES = ["diffattn_api.cpp", "generic_kernel.hip", "fwd_mfma.hip", "decode.hip", "decode_v2.hip", "bwd.hip", "bwd_v2.hip", "quant_fp8.hip", "lambda_kernel.hip"]
+SOURCES = ["diffattn_api.cpp", "generic_kernel.hip", "fwd_mfma.hip", "decode.hip", "decode_v2.hip", "bwd.hip", "bwd_v2.hip", "quant_fp8.hip", "lambda_kernel.hip", "probe.hip"]
 HEADERS = ["common.hpp", "kernels.hpp", "mfma_tile.hpp", "bwd_tile.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

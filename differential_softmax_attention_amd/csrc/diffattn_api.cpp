@@ -694,6 +694,15 @@ diffattn_status diffattn_fwd_fp8(diffattn_tensor q1, diffattn_tensor q2, diffatt
     return hip_status(diffattn::launch_v1_fwd_fp8(a, (hipStream_t)stream), "diffattn_fwd_fp8 launch");
 }
 
+diffattn_status diffattn_probe_mfma_peak(float* out, int blocks, int iters, double* flop, void* stream) {
+    if (!out || !flop) return fail(DIFFATTN_ERR_ARG, "diffattn_probe_mfma_peak: out and flop must be non-null");
+    if (blocks < 1 || iters < 1 || blocks > (1 << 20))
+        return fail(DIFFATTN_ERR_ARG, "diffattn_probe_mfma_peak: blocks=%d iters=%d out of range", blocks, iters);
+    *flop = (double)blocks * 4 * 8 * (double)iters * 32768.0;
+    return hip_status(diffattn::launch_mfma_peak(out, blocks, iters, (hipStream_t)stream),
+                      "diffattn_probe_mfma_peak launch");
+}
+
 diffattn_status diffattn_lambda_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2,
                                     const float* dlambda, int n, int dim, float* dlq1, float* dlk1, float* dlq2,
                                     float* dlk2, void* stream) {

@@ -189,4 +189,8 @@ struct Fp8QuantArgs {
 
 hipError_t launch_quantize_fp8(const Fp8QuantArgs& a, hipStream_t stream);
 
+// Dense bf16 MFMA rate probe: `blocks` blocks of 4 waves, each wave 8 x iters MFMAs of 32x32x16
+// (32768 flop each); out receives blocks * 256 floats.
+hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t stream);
+
 }  // namespace diffattn

@@ -417,6 +417,15 @@ diffattn_status diffattn_v2_decode_paged(diffattn_dtype dtype, diffattn_tensor q
                                          int d, float scale, diffattn_tensor out, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement helper, not part of the method: runs `blocks` blocks of 4 waves, each wave issuing
+ * 8 x iters independent v_mfma_f32_32x32x16_bf16 (register operands only), so that the attainable
+ * dense bf16 rate of the device can be timed beside the published peak. *flop (HOST) receives
+ * the work of the launch. out: DEVICE fp32 [blocks * 256], written (keeps the work observable).
+ * Errors: ERR_ARG (null pointers, blocks outside 1..2^20, iters < 1), ERR_HIP.
+ */
+diffattn_status diffattn_probe_mfma_peak(float* out, int blocks, int iters, double* flop, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
