@@ -407,8 +407,9 @@ def main():
         mfma_tflops = probe_flop / (avg_p * 1e-3) / 1e12
         result["measured_peaks"] = {
             "hbm_torch_copy_GB/s": round(copy_gbs, 1), "mfma_bf16_TFLOP/s": round(mfma_tflops, 1),
-            "how": "torch copy_ of 1 GiB on the device (bytes read + written; the decode kernels stream faster than it) and diffattn_probe_mfma_peak (4096 blocks of 4 "
-                   "waves, 8 independent v_mfma_f32_32x32x16_bf16 chains each)"}
+            "how": "torch copy_ of 1 GiB on the device (bytes read + written; the decode kernels stream "
+                   "faster than it) and diffattn_probe_mfma_peak (4096 blocks of 4 waves, 8 independent "
+                   "v_mfma_f32_32x32x16_bf16 chains each)"}
         result["roofline"]["frac_of_measured_peak"] = round(result["roofline"]["achieved"] / mfma_tflops, 4)
         log(f"[bench] measured peaks: copy {copy_gbs:.0f} GB/s, bf16 MFMA {mfma_tflops:.0f} TFLOP/s")
         del probe_out
