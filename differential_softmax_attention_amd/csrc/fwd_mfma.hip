@@ -371,9 +371,16 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         }
 
         // tile maxima (raw score units), shared by lanes n and n+32
-        float mx1 = s1[0], mx2 = s2[0];
+        // a tree of 3-input maxima (depth 3, eight instructions per map): the maxima sit on the
+        // path from the score MFMAs to the exponentials, so their depth counts, not just their number
+        auto tile_max = [](const f32x16& x) __attribute__((always_inline)) {
+            float t[6];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) { mx1 = fmax_nc(mx1, s1[r]); mx2 = fmax_nc(mx2, s2[r]); }
+            for (int i = 0; i < 5; ++i) t[i] = fmax_nc(fmax_nc(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+            t[5] = x[15];
+            return fmax_nc(fmax_nc(fmax_nc(t[0], t[1]), t[2]), fmax_nc(fmax_nc(t[3], t[4]), t[5]));
+        };
+        float mx1 = tile_max(s1), mx2 = tile_max(s2);
         mx1 = max_halves(mx1) * c2a;
         mx2 = max_halves(mx2) * c2b;
         const bool need = (mx1 > m1 + kRescaleThreshold) || (mx2 > m2 + kRescaleThreshold);
