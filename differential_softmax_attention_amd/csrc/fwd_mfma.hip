@@ -55,6 +55,9 @@ constexpr float kRescaleThreshold = 8.0f;
 #define DA_PRIO_V2 0
 #endif
 
+template <int V>
+struct StageC { static constexpr int value = V; };
+
 template <int D, bool V2, bool F8 = false>
 struct Cfg {
     static constexpr int NW = V2 ? 8 : 4;              // waves per block
@@ -291,7 +294,10 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     f32x16 o1[4], o2[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) { o1[ct] = f32x16{}; o2[ct] = f32x16{}; }
-    float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
+    float m1 = -INFINITY, m2 = -INFINITY;
+    // row sums in two partial chains per map (la: even key pairs, lb: odd), kept across tiles and
+    // added once at the end
+    float la1 = 0.f, lb1 = 0.f, la2 = 0.f, lb2 = 0.f;
     // score scale per map: softmax scale * log2(e), times the two fp8 dequantisation scales
     float c2a = a.scale_log2, c2b = a.scale_log2;
     if (F8) {
@@ -320,8 +326,10 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         if (a.lam_out && b == 0 && qt == 0 && tid == 0) a.lam_out[hout] = lam_fused;
     }
 
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int stage = kt & 1;
+    // one tile; the loop below is unrolled by the two stages so that each stage's LDS base is a
+    // constant and folds into the operand reads' immediate offsets
+    auto tile_step = [&](int kt, auto stage_c) __attribute__((always_inline)) {
+        constexpr int stage = decltype(stage_c)::value;
         __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this thread's DMA landed
         if ((kt + 1) * kBN > a.seq_k) zero_tail(kt, stage);
         __syncthreads();                                    // every DMA of tile kt landed; stage^1 free
@@ -329,7 +337,7 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
 
         const int k0 = kt * kBN;
         const bool wave_needs = wave_active && (!CAUSAL || k0 <= wave_qlast + off);
-        if (!wave_needs) continue;
+        if (!wave_needs) return;
         const unsigned char* st = smem + stage * C::STAGE_BYTES;
         const unsigned char* Ks1 = st;
         const unsigned char* Ks2 = st + (C::NK - 1) * C::K_BYTES;
@@ -389,8 +397,10 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
             const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
             m1 = mn1;
             m2 = mn2;
-            l1 *= al1;
-            l2 *= al2;
+            la1 *= al1;
+            lb1 *= al1;
+            la2 *= al2;
+            lb2 *= al2;
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) { o1[ct] *= al1; o2[ct] *= al2; }
         }
@@ -402,7 +412,6 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         // exponentials of the second half.
         const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
         bf16x8 p1[2], p2[2];
-        float la1 = 0.f, lb1 = 0.f, la2 = 0.f, lb2 = 0.f;
         auto softmax_half = [&](int kb) {
             bf16x2 q1p[4], q2p[4];
 #pragma unroll
@@ -450,8 +459,6 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         read_v(1);
         pv(1);
         if (kPrio) __builtin_amdgcn_s_setprio(0);
-        l1 += la1 + lb1;
-        l2 += la2 + lb2;
         if (kSched) {
         // 8 V reads, the first half's softmax, then each first-half MFMA followed by a sixth of
         // the second half's softmax, the second half's V reads, and its MFMAs
@@ -465,13 +472,17 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+        tile_step(kt, StageC<0>{});
+        if (kt + 1 < nkt) tile_step(kt + 1, StageC<1>{});
     }
 
     if (!wave_active) return;
 
     // ---- epilogue: O = O1/l1 - lambda O2/l2 (+ RMSNorm * w * (1 - lambda_init))
-    l1 = sum_halves(l1);
-    l2 = sum_halves(l2);
+    const float l1 = sum_halves(la1 + lb1);
+    const float l2 = sum_halves(la2 + lb2);
     float lam;
     if (V2) {
         lam = (qrow < a.seq_q) ? a.lam[b * a.lams[0] + (int64_t)qrow * a.lams[1] + (int64_t)hout * a.lams[2]] : 0.f;
