@@ -27,6 +27,10 @@
 //    half's exponentials; V1 raises the wave priority while it issues MFMAs.
 //  - Epilogue in registers: O1/l1 - lambda O2/l2, then (V1) RMSNorm over the 128 channels and the
 //    (1 - lambda_init) multiply, stored as bf16.
+//  - V2 (head dimension 128): the first head's Q fragments stay in registers, the second head's
+//    rows sit in an LDS region of the wave's own (filled once by DMA, read with the K offsets).
+//    Both in registers would need more than the 256 of two waves per SIMD, and the spill reloads
+//    inside the tile loop would each wait for the whole vector-memory count, prefetch included.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
@@ -69,6 +73,8 @@ struct Cfg {
     static constexpr int K_BYTES = kBN * D * K_ELT;
     static constexpr int V_BYTES = kBN * kDV * 2;
     static constexpr int STAGE_BYTES = NK * K_BYTES + V_BYTES;
+    static constexpr int Q2_OFF = 2 * STAGE_BYTES;                       // V2: Q_{2p+1} rows, per wave
+    static constexpr int Q2_BYTES = V2 ? NW * 32 * D * 2 : 0;
     // DMA loads per thread per K tile; fp8: the K1 and K2 tiles together take one load per thread
     static constexpr int K_LOADS = F8 ? 1 : kBN * K_CPR / NT;
     static constexpr int V_LOADS = kBN * V_CPR / NT;
@@ -166,7 +172,7 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
             for (int kk = 0; kk < NKK; ++kk) {
                 const bf16x8 z = {};
                 bq1[kk] = ok ? ld_global_bf16x8(q1p + 16 * kk) : z;
-                bq2[kk] = ok ? ld_global_bf16x8(q2p + 16 * kk) : z;
+                if (!V2) bq2[kk] = ok ? ld_global_bf16x8(q2p + 16 * kk) : z;
             }
         }
     }
@@ -306,6 +312,20 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         c2b *= a.sq2[sh] * a.sk2[sh];
     }
 
+    if (V2) {
+        // this wave's 32 rows of Q_{2p+1} into its LDS region (rows of 16 chunks, swizzled like K;
+        // rows past the end repeat the last row, whose outputs are not stored)
+        const int qb0 = min(qw0, a.seq_q - 1);
+        const bf16* qbase = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)qb0 * a.q2s[1] + (int64_t)hq2 * a.q2s[2];
+#pragma unroll
+        for (int i = 0; i < 32 * D * 2 / 1024; ++i) {
+            const int c = lane + 64 * i;
+            const int r = c / (D / 8), pc = c % (D / 8);
+            const int qr = min(qw0 + r, a.seq_q - 1) - qb0;
+            dma16(qbase, (uint32_t)(qr * a.q2s[1] + (pc ^ k_swz<D>(r)) * 8) * 2u,
+                  smem_lds + C::Q2_OFF + wave_u * 32 * D * 2 + i * 1024);
+        }
+    }
     issue_tile(0, 0);
 
     // V1 lambda from its re-parameterisation (LAMF): the lambda kernel's arithmetic (lane-strided
@@ -359,7 +379,7 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
                 const bf16x8 ka = lds16(Ks1 + koff[kk]);
                 s1 = mfma32x32x16(ka, bq1[kk], s1);
                 if (V2) {
-                    s2 = mfma32x32x16(ka, bq2[kk], s2);
+                    s2 = mfma32x32x16(ka, lds16(smem + C::Q2_OFF + wave_u * 32 * D * 2 + koff[kk]), s2);
                 } else {
                     const bf16x8 kb2 = lds16(Ks2 + koff[kk]);
                     s2 = mfma32x32x16(kb2, bq2[kk], s2);
@@ -567,7 +587,7 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
     const int n_units = V2 ? a.batch * (a.heads * 2 / a.kv_group) : a.batch * a.heads;
     const int nqt = (a.seq_q + BM - 1) / BM;
     const dim3 grid((unsigned)(nqt * n_units));
-    const size_t smem = 2 * C::STAGE_BYTES;
+    const size_t smem = 2 * C::STAGE_BYTES + C::Q2_BYTES;
     if (!V2 && !F8 && a.lq1) {   // lambda from its vectors inside the kernel
         if (a.causal) {
             if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, true, F8, true>), grid, dim3(C::NT), smem, stream, a);
