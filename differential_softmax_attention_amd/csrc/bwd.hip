@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             ds1[r] = p1[r] * (dp[r] - D1);
-            ds2[r] = -lam * p2[r] * (dp[r] - D2);
+            ds2[r] = p2[r] * (dp[r] - D2);   // the factor -lambda is applied to dQ2 once, at the store
         }
         // dQ_k^T += K_k^T dS_k^T (k index = keys)
 #pragma unroll
@@ -285,6 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (!qok) return;
     // dQ_k = s dS_k K_k; lane (n, h2) holds d = 32 mt + (r / 4) * 8 + 4 h2 + r % 4 of query n
+    const float sc2 = -lam * a.scale;   // dS2 was accumulated without its factor -lambda
     bf16* o1p = (bf16*)a.dq1 + b * a.dq1s[0] + (int64_t)qrow * a.dq1s[1] + (int64_t)h * a.dq1s[2];
     bf16* o2p = (bf16*)a.dq2 + b * a.dq2s[0] + (int64_t)qrow * a.dq2s[1] + (int64_t)h * a.dq2s[2];
 #pragma unroll
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 x1[j] = (bf16)(dq1[mt][g * 4 + j] * a.scale);
-                x2[j] = (bf16)(dq2[mt][g * 4 + j] * a.scale);
+                x2[j] = (bf16)(dq2[mt][g * 4 + j] * sc2);
             }
             *(bf16x4*)(o1p + mt * 32 + g * 8 + h2 * 4) = x1;
             *(bf16x4*)(o2p + mt * 32 + g * 8 + h2 * 4) = x2;
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             ds1[r] = p1[r] * dm1[r];
-            ds2[r] = -lam * p2[r] * dm2[r];
+            ds2[r] = p2[r] * dm2[r];   // the factor -lambda is applied to dK2 once, at the store
             pc[r] = fmaf(-lam, p2[r], p1[r]);
         }
         // dK_k^T += Q_k^T dS_k and dV^T += go^T (A1 - lambda A2) (k index = queries)
@@ -470,6 +471,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     agpr_drain(dk1[0], dk1[1], dk2[0], dk2[1]);
     agpr_drain(dv[0], dv[1], dv[2], dv[3]);
     if (key >= a.seq_k) return;
+    const float sc2 = -lam * a.scale;   // dS2 was accumulated without its factor -lambda
     bf16* k1p = (bf16*)a.dk1 + b * a.dk1s[0] + (int64_t)key * a.dk1s[1] + (int64_t)h * a.dk1s[2];
     bf16* k2p = (bf16*)a.dk2 + b * a.dk2s[0] + (int64_t)key * a.dk2s[1] + (int64_t)h * a.dk2s[2];
     bf16* vp = (bf16*)a.dv + b * a.dvs[0] + (int64_t)key * a.dvs[1] + (int64_t)h * a.dvs[2];
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 x1[j] = (bf16)(dk1[mt][g * 4 + j] * a.scale);
-                x2[j] = (bf16)(dk2[mt][g * 4 + j] * a.scale);
+                x2[j] = (bf16)(dk2[mt][g * 4 + j] * sc2);
             }
             *(bf16x4*)(k1p + mt * 32 + g * 8 + h2 * 4) = x1;
             *(bf16x4*)(k2p + mt * 32 + g * 8 + h2 * 4) = x2;

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             ds1[r] = p1[r] * (dp[r] - D1);
-            ds2[r] = nlam * p2[r] * (dp[r] - D2);
+            ds2[r] = p2[r] * (dp[r] - D2);   // the row's factor -lambda is applied to dQ_{2p+1} at the store
         }
         // dQ_j^T += K^T dS_j^T (k index = keys); one transposed K fragment serves both heads
 #pragma unroll
@@ -206,6 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     agpr_drain(dq2[0], dq2[1], dq2[2], dq2[3]);
     if (!qok) return;
     // dQ_j = s dS_j K; lane (n, h2) holds d = 32 mt + (r / 4) * 8 + 4 h2 + r % 4 of query n
+    const float sc2 = nlam * a.scale;   // dS_{2p+1} was accumulated without the row's factor -lambda
     bf16* o1p = (bf16*)a.dq + b * a.dqs[0] + (int64_t)qrow * a.dqs[1] + (int64_t)(2 * p) * a.dqs[2];
     bf16* o2p = o1p + a.dqs[2];
 #pragma unroll
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 x1[j] = (bf16)(dq1[mt][gq * 4 + j] * a.scale);
-                x2[j] = (bf16)(dq2[mt][gq * 4 + j] * a.scale);
+                x2[j] = (bf16)(dq2[mt][gq * 4 + j] * sc2);
             }
             *(bf16x4*)(o1p + mt * 32 + gq * 8 + h2 * 4) = x1;
             *(bf16x4*)(o2p + mt * 32 + gq * 8 + h2 * 4) = x2;
