@@ -10,8 +10,9 @@
 //
 // Design (one pass over K/V, both maps at once):
 //  - A block owns a tile of query rows of one head (V1) or of every pair of one KV group (V2).
-//    Each wave owns 32 query rows of one pair. K/V tiles of 32 keys are staged through LDS,
-//    double buffered, so every tile is read from memory once per block and V once for both maps.
+//    Each wave owns 32 query rows of one pair. K/V tiles of 32 keys are staged through an LDS
+//    ring (V1: four stages, one block barrier per pair of tiles; V2: two stages), so every tile is
+//    read from memory once per block and V once for both maps.
 //  - Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane (n, h)
 //    then holds 16 keys of query n, so the running max and sum of each map are per-lane values
 //    (one exchange between lanes n and n+32 per tile).
@@ -73,7 +74,8 @@ struct Cfg {
     static constexpr int K_BYTES = kBN * D * K_ELT;
     static constexpr int V_BYTES = kBN * kDV * 2;
     static constexpr int STAGE_BYTES = NK * K_BYTES + V_BYTES;
-    static constexpr int Q2_OFF = 2 * STAGE_BYTES;                       // V2: Q_{2p+1} rows, per wave
+    static constexpr int NSTAGE = V2 ? 2 : 4;                            // LDS ring (V1: two pairs of tiles)
+    static constexpr int Q2_OFF = NSTAGE * STAGE_BYTES;                  // V2: Q_{2p+1} rows, per wave
     static constexpr int Q2_BYTES = V2 ? NW * 32 * D * 2 : 0;
     // DMA loads per thread per K tile; fp8: the K1 and K2 tiles together take one load per thread
     static constexpr int K_LOADS = F8 ? 1 : kBN * K_CPR / NT;
@@ -350,11 +352,6 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     // constant and folds into the operand reads' immediate offsets
     auto tile_step = [&](int kt, auto stage_c) __attribute__((always_inline)) {
         constexpr int stage = decltype(stage_c)::value;
-        __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this thread's DMA landed
-        if ((kt + 1) * kBN > a.seq_k) zero_tail(kt, stage);
-        __syncthreads();                                    // every DMA of tile kt landed; stage^1 free
-        if (kt + 1 < nkt) issue_tile(kt + 1, stage ^ 1);    // prefetch overlaps this tile's compute
-
         const int k0 = kt * kBN;
         const bool wave_needs = wave_active && (!CAUSAL || k0 <= wave_qlast + off);
         if (!wave_needs) return;
@@ -493,9 +490,40 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
     };
-    for (int kt = 0; kt < nkt; kt += 2) {
-        tile_step(kt, StageC<0>{});
-        if (kt + 1 < nkt) tile_step(kt + 1, StageC<1>{});
+    // V1: tiles in pairs, one block barrier per pair (half the barriers, and so half the waits for
+    // the slowest wave): a ring of four stages holds the pair being computed and the next pair in
+    // flight, 64 KB per block, two blocks per CU; unrolled by two pairs so every stage is a constant
+    if (!V2 && 1 < nkt) issue_tile(1, 1);
+    auto pair_step = [&](int kt, auto s0_c, auto s1_c, auto n0_c, auto n1_c) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this thread's DMA of tiles kt, kt + 1 landed
+        if ((kt + 1) * kBN > a.seq_k) zero_tail(kt, decltype(s0_c)::value);
+        if (kt + 1 < nkt && (kt + 2) * kBN > a.seq_k) zero_tail(kt + 1, decltype(s1_c)::value);
+        __syncthreads();                                    // both landed everywhere; the stages of the previous pair are free
+        if (kt + 2 < nkt) issue_tile(kt + 2, decltype(n0_c)::value);
+        if (kt + 3 < nkt) issue_tile(kt + 3, decltype(n1_c)::value);
+        tile_step(kt, s0_c);
+        if (kt + 1 < nkt) tile_step(kt + 1, s1_c);
+    };
+    if constexpr (!V2) {
+        for (int kt = 0; kt < nkt; kt += 4) {
+            pair_step(kt, StageC<0>{}, StageC<1>{}, StageC<2>{}, StageC<3>{});
+            if (kt + 2 < nkt) pair_step(kt + 2, StageC<2>{}, StageC<3>{}, StageC<0>{}, StageC<1>{});
+        }
+    } else {
+        // V2 (one block per CU, eight waves): two stages and a barrier per tile; pairing its tiles
+        // measured no faster
+        auto sync_step = [&](int kt, auto stage_c) __attribute__((always_inline)) {
+            constexpr int stage = decltype(stage_c)::value;
+            __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this thread's DMA landed
+            if ((kt + 1) * kBN > a.seq_k) zero_tail(kt, stage);
+            __syncthreads();                                    // every DMA of tile kt landed; stage^1 free
+            if (kt + 1 < nkt) issue_tile(kt + 1, stage ^ 1);    // prefetch overlaps this tile's compute
+            tile_step(kt, stage_c);
+        };
+        for (int kt = 0; kt < nkt; kt += 2) {
+            sync_step(kt, StageC<0>{});
+            if (kt + 1 < nkt) sync_step(kt + 1, StageC<1>{});
+        }
     }
 
     if (!wave_active) return;
@@ -587,7 +615,7 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
     const int n_units = V2 ? a.batch * (a.heads * 2 / a.kv_group) : a.batch * a.heads;
     const int nqt = (a.seq_q + BM - 1) / BM;
     const dim3 grid((unsigned)(nqt * n_units));
-    const size_t smem = 2 * C::STAGE_BYTES + C::Q2_BYTES;
+    const size_t smem = C::NSTAGE * C::STAGE_BYTES + C::Q2_BYTES;
     if (!V2 && !F8 && a.lq1) {   // lambda from its vectors inside the kernel
         if (a.causal) {
             if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, true, F8, true>), grid, dim3(C::NT), smem, stream, a);
