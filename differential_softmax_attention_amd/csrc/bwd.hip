@@ -16,8 +16,8 @@
 //  - bwd_pre: one wave per row: o, go (stored bf16 as an MFMA operand), D1, D2, and per-block
 //    partial sums of dL/dw and dlambda.
 //  - bwd_dq: query-tile parallel like the forward (S^T = K Q^T, lane = query): K1, K2, V tiles of
-//    32 keys staged through LDS; dP^T = V go^T; dQ_k^T += K_k^T dS_k^T with K^T read by the
-//    transposing LDS read.
+//    32 keys staged through LDS, one block barrier per pair of tiles; dP^T = V go^T;
+//    dQ_k^T += K_k^T dS_k^T with K^T read by the transposing LDS read.
 //  - bwd_dkdv: key-tile parallel (S = Q K^T, lane = key): each lane keeps its key's K1, K2, V rows
 //    in registers and the block walks the query tiles (Q1, Q2, go staged through LDS);
 //    dV^T += go^T (A1 - lambda A2) and dK_k^T += Q_k^T dS_k with the transposed operands again
@@ -45,7 +45,7 @@ constexpr int kQStats = 2 * kKTile + kVTile;
 constexpr int kQStage = kQStats + 2 * kBN * 2 * 4;
 constexpr int kQStages = 3;
 constexpr int kKStage = 2 * kKTile + kVTile;   // dQ key-tile stage: K1 | K2 (64 wide) | V
-constexpr int kKStages = 3;
+constexpr int kKStages = 4;                      // dQ ring: two pairs of key tiles
 
 __device__ __forceinline__ int rowop_b(int row, int kk, int h2) { return rowop<kD>(row, kk, h2); }
 __device__ __forceinline__ int trop_b(int lane, int kb, int mt, int hi) { return trop<kD>(lane, kb, mt, hi); }
@@ -263,25 +263,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     };
     auto tile = [&](auto ST, int kt) __attribute__((always_inline)) {
-        constexpr int st = decltype(ST)::value;
-        if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(kVmcnt[4]);   // tile kt+1's loads may stay in flight
-        else __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
-        __syncthreads();   // tile kt landed for every thread; the stage of tile kt-1 is free
-        if (kt + kKStages - 1 < nkt) issue(kt + kKStages - 1, (st + kKStages - 1) % kKStages);
         const int k0 = kt * kBN;
         if (!wave_active || (a.causal && k0 > wave_qlast + off)) return;
         compute(ST, qw0 + kBN <= a.seq_q && k0 + kBN <= a.seq_k && (!a.causal || k0 + kBN - 1 <= qw0 + off), k0);
     };
-    // the ring position of a tile is its index modulo 3, and the loop is unrolled by 3 so that
-    // every LDS address is a register plus a constant
-    for (int kt = 0; kt < nkt && kt < kKStages - 1; ++kt) issue(kt, kt);
+    // key tiles in pairs, one block barrier per pair: a ring of four stages holds the pair being
+    // worked on and the next pair in flight, unrolled by two pairs so that every LDS address is a
+    // register plus a constant
+    auto pair = [&](int kt, auto S0, auto S1, auto N0, auto N1) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt[0]);   // this thread's DMA of tiles kt, kt + 1 landed
+        __syncthreads();   // both landed everywhere; the stages of the previous pair are free
+        if (kt + 2 < nkt) issue(kt + 2, decltype(N0)::value);
+        if (kt + 3 < nkt) issue(kt + 3, decltype(N1)::value);
+        tile(S0, kt);
+        if (kt + 1 < nkt) tile(S1, kt + 1);
+    };
+    for (int kt = 0; kt < nkt && kt < 2; ++kt) issue(kt, kt);
     // the query operands and the first tiles have landed: from here on the compiler sees no
     // outstanding loads of its own and adds no waits on the key-tile DMA
     __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
-    for (int kt = 0; kt < nkt; kt += kKStages) {
-        tile(IC<0>{}, kt);
-        if (kt + 1 < nkt) tile(IC<1>{}, kt + 1);
-        if (kt + 2 < nkt) tile(IC<2>{}, kt + 2);
+    for (int kt = 0; kt < nkt; kt += 4) {
+        pair(kt, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        if (kt + 2 < nkt) pair(kt + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
     }
     if (!qok) return;
     // dQ_k = s dS_k K_k; lane (n, h2) holds d = 32 mt + (r / 4) * 8 + 4 h2 + r % 4 of query n
