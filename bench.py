@@ -32,6 +32,9 @@ METRIC = "diff-attn fwd TFLOP/s (bf16, N=2K/32K) + decode GB/s; % of MFMA/HBM pe
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 FLOP_PER_PAIR_V1 = 768
+# the work of ordinary attention on the same pairs (one QK^T of width 64, one PV of width 128),
+# printed beside the method's own for transparency; never the metric
+FLOP_PER_PAIR_V1_NAIVE_EQ = 512
 FLOP_PER_PAIR_V2 = 512
 # backward: recomputed scores (2 x 2d), dP = go V^T (2 dv), dV (2 dv), dK and dQ of both maps
 # (2 x 2d each): 1280 per visible pair at d = 64, dv = 128
@@ -182,7 +185,9 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.B, "heads": cfg.H, "seq_len": cfg.N, "d": cfg.d,
                    "dv": cfg.dv, "causal": True, "epilogue": "rmsnorm*(1-lambda_init)", "layer": cfg.layer,
                    "step": "diffattn_fwd_lambda (lambda re-parameterisation and the fused forward, one kernel)",
-                   "flop_per_step": flops, "flop_per_visible_pair": FLOP_PER_PAIR_V1},
+                   "flop_per_step": flops, "flop_per_visible_pair": FLOP_PER_PAIR_V1,
+                   "naive_equivalent_TFLOP/s": round(value * FLOP_PER_PAIR_V1_NAIVE_EQ / FLOP_PER_PAIR_V1, 2),
+                   "naive_equivalent_flop_per_visible_pair": FLOP_PER_PAIR_V1_NAIVE_EQ},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "fwd_mfma_kernel<64,V1,causal,epilogue,lambda in-kernel>",
