@@ -23,7 +23,6 @@ namespace diffattn {
 
 namespace {
 
-constexpr int kD = 64;
 constexpr int kDV = 128;
 constexpr int kPartial = 4 + 2 * kDV + 4;   // m1, l1, m2, l2, o1[128], o2[128], pad -> 264 floats
 constexpr int kSplitThreads = 256;
