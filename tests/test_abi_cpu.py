@@ -249,3 +249,13 @@ def test_product_does_not_import_oracle():
                 with open(os.path.join(dirpath, fn)) as f:
                     src = f.read()
                 assert "oracle" not in src, fn
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    # the Python layer has no fallback: without the built library every call must raise
+    monkeypatch.setattr(da, "LIB_PATH", str(tmp_path / "libdiffattn.so"))
+    monkeypatch.setattr(da, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        da.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        da.diffattn_bwd_workspace_size(1, 1, 1)
