@@ -349,6 +349,29 @@ def test_v2_decode_equals_last_prefill_row():
     assert maxerr(f64(dec), f64(fwd[:, -1])) <= TOL_BF16
 
 
+def test_v1_decode_deterministic():
+    # split partials are merged in a fixed order: repeated calls agree bit for bit
+    q1, q2 = rand((2, 4, 64), 1900, torch.bfloat16), rand((2, 4, 64), 1901, torch.bfloat16)
+    k1, k2 = rand((2, 5000, 4, 64), 1902, torch.bfloat16), rand((2, 5000, 4, 64), 1903, torch.bfloat16)
+    v = rand((2, 5000, 4, 128), 1904, torch.bfloat16)
+    lam = torch.tensor([0.2, 0.4, 0.6, 0.8], device=DEV)
+    a = da.diffattn_decode(q1, q2, k1, k2, v, lam)
+    b = da.diffattn_decode(q1, q2, k1, k2, v, lam)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_v2_forward_deterministic():
+    q = rand((1, 300, 8, 128), 1950, torch.bfloat16)
+    k = rand((1, 300, 2, 128), 1951, torch.bfloat16)
+    v = rand((1, 300, 2, 128), 1952, torch.bfloat16)
+    lam = torch.rand((1, 300, 4), generator=torch.Generator().manual_seed(1953)).to(DEV)
+    a = da.diffattn_v2_fwd(q, k, v, lam, causal=True)
+    b = da.diffattn_v2_fwd(q, k, v, lam, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 def test_v2_decode_deterministic():
     q = rand((2, 16, 128), 1800, torch.bfloat16)
     k = rand((2, 4000, 2, 128), 1801, torch.bfloat16)
