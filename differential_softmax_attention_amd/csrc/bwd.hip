@@ -21,19 +21,31 @@
 //  - bwd_dkdv: key-tile parallel (S = Q K^T, lane = key): each lane keeps its key's K1, K2, V rows
 //    in registers and the block walks the query tiles (Q1, Q2, go staged through LDS);
 //    dV^T += go^T (A1 - lambda A2) and dK_k^T += Q_k^T dS_k with the transposed operands again
-//    read by ds_read_b64_tr_b16.
+//    read by ds_read_b64_tr_b16. Query tiles come in pairs, one block barrier per pair; where the
+//    pair holds no masked (query, key) pair for any wave of the block, its 64 MFMAs run in a fixed
+//    order with the second tile's score MFMAs beside the first tile's vector work and the first
+//    tile's gradient MFMAs beside the second tile's, each operand read issued four MFMAs ahead.
 // Tiles that hold no masked (query, key) pair skip the per-element visibility test.
 //  - bwd_reduce: dlambda per head and dL/dw per channel from the partials.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
 #include "bwd_tile.hpp"
+#include <utility>
 
 namespace diffattn {
 
 namespace {
 
 using namespace bwdt;
+
+// f(IC<0>), f(IC<1>), ..., f(IC<N - 1>): a loop whose index is a compile-time constant
+template <int... I, class F> __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+    (f(IC<I>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
 
 constexpr int kD = 64;
 constexpr int kDV = 128;
@@ -43,7 +55,7 @@ constexpr int kPreRows = 16;            // rows per bwd_pre block (4 waves x 4 r
 // dK/dV query-tile stage: Q1 | Q2 (64 wide) | go (128 wide) | lse [32][2] | dd [32][2]
 constexpr int kQStats = 2 * kKTile + kVTile;
 constexpr int kQStage = kQStats + 2 * kBN * 2 * 4;
-constexpr int kQStages = 3;
+constexpr int kQStages = 4;
 constexpr int kKStage = 2 * kKTile + kVTile;   // dQ key-tile stage: K1 | K2 (64 wide) | V
 constexpr int kKStages = 4;                      // dQ ring: two pairs of key tiles
 
@@ -379,15 +391,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
 
-    // one query tile; !full: some (query, key) pair of the wave's 32 x 32 block is not visible
-    auto compute = [&](auto ST, bool full, int i0) __attribute__((always_inline)) {
-        const unsigned char* Q1s = sq + decltype(ST)::value * kQStage;
+    // S_k = Q_k K_k^T and dP = go V^T of one query tile (rows = queries, lane = key)
+    auto scores = [&](const unsigned char* Q1s, f32x16& dp, f32x16& s1, f32x16& s2) __attribute__((always_inline)) {
         const unsigned char* Q2s = Q1s + kKTile;
         const unsigned char* Gs = Q1s + 2 * kKTile;
-        const float* svl = (const float*)(Q1s + kQStats);   // lse [32][2]
-        const float* svd = svl + 64;                          // dd [32][2]
-        // dP = go V^T, S_k = Q_k K_k^T (rows = queries, lane = key)
-        f32x16 dp = f32x16{}, s1 = f32x16{}, s2 = f32x16{};
+        dp = f32x16{}; s1 = f32x16{}; s2 = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Gs + rowop_v(n, kk, h2)), vr[kk], dp);
 #pragma unroll
@@ -395,6 +403,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             s1 = mfma32x32x16(lds16(Q1s + rowop_b(n, kk, h2)), kr1[kk], s1);
             s2 = mfma32x32x16(lds16(Q2s + rowop_b(n, kk, h2)), kr2[kk], s2);
         }
+    };
+    // weights and score gradients of one tile as bf16 B operands (k index = queries)
+    auto weights = [&](const unsigned char* Q1s, bool full, int i0, const f32x16& dp, const f32x16& s1,
+                       const f32x16& s2, bf16x8* b1, bf16x8* b2, bf16x8* bp) __attribute__((always_inline)) {
+        const float* svl = (const float*)(Q1s + kQStats);   // lse [32][2]
+        const float* svd = svl + 64;                          // dd [32][2]
         // register r holds query row 8 (r / 4) + 4 h2 + r % 4
         f32x16 p1, p2, dm1, dm2, ds1, ds2, pc;
 #pragma unroll
@@ -430,46 +444,172 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             ds2[r] = p2[r] * dm2[r];   // the factor -lambda is applied to dK2 once, at the store
             pc[r] = fmaf(-lam, p2[r], p1[r]);
         }
-        // dK_k^T += Q_k^T dS_k and dV^T += go^T (A1 - lambda A2) (k index = queries)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) { b1[kb] = c_to_b(ds1, kb); b2[kb] = c_to_b(ds2, kb); bp[kb] = c_to_b(pc, kb); }
+    };
+    // dK_k^T += Q_k^T dS_k and dV^T += go^T (A1 - lambda A2) (k index = queries)
+    auto grads = [&](const unsigned char* Q1s, const bf16x8* b1, const bf16x8* b2, const bf16x8* bp) __attribute__((always_inline)) {
+        const unsigned char* Q2s = Q1s + kKTile;
+        const unsigned char* Gs = Q1s + 2 * kKTile;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 b1 = c_to_b(ds1, kb), b2 = c_to_b(ds2, kb), bp = c_to_b(pc, kb);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                mfma_agpr(dk1[mt], tr_pair(Q1s, trop_b(lane, kb, mt, 0), trop_b(lane, kb, mt, 1)), b1);
-                mfma_agpr(dk2[mt], tr_pair(Q2s, trop_b(lane, kb, mt, 0), trop_b(lane, kb, mt, 1)), b2);
+                mfma_agpr(dk1[mt], tr_pair(Q1s, trop_b(lane, kb, mt, 0), trop_b(lane, kb, mt, 1)), b1[kb]);
+                mfma_agpr(dk2[mt], tr_pair(Q2s, trop_b(lane, kb, mt, 0), trop_b(lane, kb, mt, 1)), b2[kb]);
             }
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
-                mfma_agpr(dv[ct], tr_pair(Gs, trop_v(lane, kb, ct, 0), trop_v(lane, kb, ct, 1)), bp);
+                mfma_agpr(dv[ct], tr_pair(Gs, trop_v(lane, kb, ct, 0), trop_v(lane, kb, ct, 1)), bp[kb]);
         }
     };
-    auto tile = [&](auto ST, int qt) __attribute__((always_inline)) {
-        constexpr int st = decltype(ST)::value;
-        // this thread's DMA of tile qt has landed (the next tile's loads may be in flight)
-        if (qt + 1 < nqt) {
-            if (wave == 0) __builtin_amdgcn_s_waitcnt(kVmcnt[6]);
-            else __builtin_amdgcn_s_waitcnt(kVmcnt[4]);
+    // one query tile; !full: some (query, key) pair of the wave's 32 x 32 block is not visible
+    auto compute = [&](const unsigned char* Q1s, bool full, int i0) __attribute__((always_inline)) {
+        f32x16 dp, s1, s2;
+        bf16x8 b1[2], b2[2], bp[2];
+        scores(Q1s, dp, s1, s2);
+        weights(Q1s, full, i0, dp, s1, s2, b1, b2, bp);
+        grads(Q1s, b1, b2, bp);
+    };
+    auto tile_full = [&](int i0) { return i0 + kBN <= a.seq_q && kw0 + kBN <= a.seq_k && (!a.causal || kw0 + kBN - 1 <= i0 + off); };
+    auto tile_skip = [&](int i0) { return !wave_active || (a.causal && i0 + kBN - 1 + off < kw0); };
+    // two query tiles per block barrier; slots S0, S1 hold them, N0, N1 take the pair after next.
+    // FAST: both tiles are unmasked for every wave of the block, and tile B's score MFMAs run
+    // beside tile A's vector work, tile A's gradient MFMAs beside tile B's.
+    auto pair = [&](auto FAST, int qt, auto S0, auto S1, auto N0, auto N1) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt[0]);   // this thread's DMA of tiles qt, qt + 1 landed
+        __syncthreads();   // every thread's loads landed; the slots of the previous pair are free
+        if (qt + 2 < nqt) issue_q(qt + 2, decltype(N0)::value);
+        if (qt + 3 < nqt) issue_q(qt + 3, decltype(N1)::value);
+        const unsigned char* QA = sq + decltype(S0)::value * kQStage;
+        const unsigned char* QB = sq + decltype(S1)::value * kQStage;
+        const int iA = qt * kBN, iB = iA + kBN;
+        if constexpr (decltype(FAST)::value) {
+            // 64 MFMAs in a fixed order: tile A's 16 score MFMAs, tile B's 16 (each followed by
+            // the vector work of one row of tile A), tile A's 16 gradient MFMAs (each followed by
+            // one row of tile B), tile B's 16. Every operand read is issued kLead MFMAs ahead of
+            // its use; a scheduling barrier after each step keeps the order.
+            constexpr int kLead = 4;
+            f32x16 dpA = {}, s1A = {}, s2A = {}, dpB = {}, s1B = {}, s2B = {};
+            f32x16 ds1A, ds2A, pcA, ds1B, ds2B, pcB;
+            bf16x8 b1A[2], b2A[2], bpA[2], b1B[2], b2B[2], bpB[2];
+            bf16x8 op[64];
+            f32x4 st[2][4];   // lse and dd of one group of four rows, for tile A then tile B
+            auto read_op = [&](int m) __attribute__((always_inline)) {
+                const unsigned char* T = (m < 16 || (m >= 32 && m < 48)) ? QA : QB;
+                const int i = m & 15;
+                if (m < 32) {
+                    if (i < 8) op[m] = lds16(T + 2 * kKTile + rowop_v(n, i, h2));
+                    else op[m] = lds16(T + (i & 1) * kKTile + rowop_b(n, (i - 8) >> 1, h2));
+                } else {
+                    const int kb = i >> 3, jj = i & 7;
+                    if (jj < 4) op[m] = tr_pair(T + (jj & 1) * kKTile, trop_b(lane, kb, jj >> 1, 0), trop_b(lane, kb, jj >> 1, 1));
+                    else op[m] = tr_pair(T + 2 * kKTile, trop_v(lane, kb, jj - 4, 0), trop_v(lane, kb, jj - 4, 1));
+                }
+            };
+            auto issue = [&](int m) __attribute__((always_inline)) {
+                const int i = m & 15;
+                if (m < 32) {
+                    f32x16& dp = m < 16 ? dpA : dpB;
+                    f32x16& s1 = m < 16 ? s1A : s1B;
+                    f32x16& s2 = m < 16 ? s2A : s2B;
+                    if (i < 8) dp = mfma32x32x16(op[m], vr[i], dp);
+                    else if (!(i & 1)) s1 = mfma32x32x16(op[m], kr1[(i - 8) >> 1], s1);
+                    else s2 = mfma32x32x16(op[m], kr2[(i - 8) >> 1], s2);
+                } else {
+                    const bf16x8* b1 = m < 48 ? b1A : b1B;
+                    const bf16x8* b2 = m < 48 ? b2A : b2B;
+                    const bf16x8* bp = m < 48 ? bpA : bpB;
+                    const int kb = i >> 3, jj = i & 7;
+                    if (jj < 4) {
+                        if (jj & 1) mfma_agpr(dk2[jj >> 1], op[m], b2[kb]);
+                        else mfma_agpr(dk1[jj >> 1], op[m], b1[kb]);
+                    } else {
+                        mfma_agpr(dv[jj - 4], op[m], bp[kb]);
+                    }
+                }
+            };
+            auto read_stats = [&](const unsigned char* T, int g, f32x4* out) __attribute__((always_inline)) {
+                const float* svl = (const float*)(T + kQStats);   // lse [32][2]
+                const float* svd = svl + 64;                        // dd [32][2]
+                const int q4 = 8 * g + 4 * h2;
+                out[0] = *(const f32x4*)(svl + 2 * q4);
+                out[1] = *(const f32x4*)(svl + 2 * q4 + 4);
+                out[2] = *(const f32x4*)(svd + 2 * q4);
+                out[3] = *(const f32x4*)(svd + 2 * q4 + 4);
+            };
+            // row r (query 8 (r / 4) + 4 h2 + r % 4) of one tile: weights, score gradients
+            auto row = [&](int r, const f32x4* sv, const f32x16& dp, const f32x16& s1, const f32x16& s2,
+                           f32x16& ds1, f32x16& ds2, f32x16& pc) __attribute__((always_inline)) {
+                const int j = r & 3;
+                const float lse1 = sv[j >> 1][2 * (j & 1)], lse2 = sv[j >> 1][2 * (j & 1) + 1];
+                const float dd1 = sv[2 + (j >> 1)][2 * (j & 1)], dd2 = sv[2 + (j >> 1)][2 * (j & 1) + 1];
+                const float p1 = fast_exp2(fmaf(s1[r], c, -lse1));
+                const float p2 = fast_exp2(fmaf(s2[r], c, -lse2));
+                ds1[r] = p1 * (dp[r] - dd1);
+                ds2[r] = p2 * (dp[r] - dd2);   // the factor -lambda is applied to dK2 once, at the store
+                pc[r] = fmaf(-lam, p2, p1);
+            };
+#pragma unroll
+            for (int m = 0; m < kLead; ++m) read_op(m);
+            read_stats(QA, 0, st[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<64>([&](auto M) __attribute__((always_inline)) {
+                constexpr int m = decltype(M)::value;
+                if (m + kLead < 64) read_op(m + kLead);
+                issue(m);
+                if (m >= 16 && m < 32) {
+                    const int r = m - 16;
+                    if ((r & 3) == 0 && r > 0) read_stats(QA, r >> 2, st[0]);
+                    row(r, st[0], dpA, s1A, s2A, ds1A, ds2A, pcA);
+                    if (r == 15) {
+                        read_stats(QB, 0, st[1]);
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) { b1A[kb] = c_to_b(ds1A, kb); b2A[kb] = c_to_b(ds2A, kb); bpA[kb] = c_to_b(pcA, kb); }
+                    }
+                } else if (m >= 32 && m < 48) {
+                    const int r = m - 32;
+                    if ((r & 3) == 0 && r > 0) read_stats(QB, r >> 2, st[1]);
+                    row(r, st[1], dpB, s1B, s2B, ds1B, ds2B, pcB);
+                    if (r == 15) {
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) { b1B[kb] = c_to_b(ds1B, kb); b2B[kb] = c_to_b(ds2B, kb); bpB[kb] = c_to_b(pcB, kb); }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
         } else {
-            __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+            if (!tile_skip(iA)) compute(QA, tile_full(iA), iA);
+            if (qt + 1 < nqt && !tile_skip(iB)) compute(QB, tile_full(iB), iB);
         }
-        __syncthreads();   // every thread's loads of tile qt landed; the stage of tile qt-1 is free
-        if (qt + kQStages - 1 < nqt) issue_q(qt + kQStages - 1, (st + kQStages - 1) % kQStages);
-        const int i0 = qt * kBN;
-        // skip the tile if it ends before this wave's first key (causal)
-        if (!wave_active || (a.causal && i0 + kBN - 1 + off < kw0)) return;
-        compute(ST, i0 + kBN <= a.seq_q && kw0 + kBN <= a.seq_k && (!a.causal || kw0 + kBN - 1 <= i0 + off), i0);
     };
-    // ring position = (tile - first tile) modulo 3; the loop is unrolled by 3 so that every LDS
-    // address is a register plus a constant
-    for (int qt = qt0; qt < nqt && qt < qt0 + kQStages - 1; ++qt) issue_q(qt, qt - qt0);
+    // Tiles [qs, qm) are unmasked for the whole block and go through the FAST pairs; the others
+    // (the causal diagonal, ragged ends) through the masked ones. Both bounds are qt0 plus a
+    // multiple of four, so ring slot = (tile - qt0) modulo 4 in every loop, each unrolled by two
+    // pairs so that every LDS address is a register plus a constant.
+    int qs = nqt, qm = nqt;
+    if (k0 + 128 <= a.seq_k) {
+        const int qf = a.causal ? max(qt0, (k0 + 127 - off + kBN - 1) / kBN) : qt0;
+        const int qe = a.seq_q / kBN;   // tiles below this one hold no row past the end
+        const int q4 = qt0 + (qf - qt0 + 3) / 4 * 4;
+        if (q4 + 4 <= qe) { qs = q4; qm = q4 + (qe - q4) / 4 * 4; }
+    }
+    for (int qt = qt0; qt < nqt && qt < qt0 + 2; ++qt) issue_q(qt, qt - qt0);
     // the key operands and the first tiles have landed: from here on the compiler sees no
     // outstanding loads of its own and adds no waits on the query-tile DMA
     __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
-    for (int qt = qt0; qt < nqt; qt += kQStages) {
-        tile(IC<0>{}, qt);
-        if (qt + 1 < nqt) tile(IC<1>{}, qt + 1);
-        if (qt + 2 < nqt) tile(IC<2>{}, qt + 2);
+    int qt = qt0;
+    for (; qt < qs; qt += 4) {
+        pair(std::false_type{}, qt, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        if (qt + 2 < nqt) pair(std::false_type{}, qt + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
+    }
+    for (; qt < qm; qt += 4) {
+        pair(std::true_type{}, qt, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        pair(std::true_type{}, qt + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
+    }
+    for (; qt < nqt; qt += 4) {
+        pair(std::false_type{}, qt, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        if (qt + 2 < nqt) pair(std::false_type{}, qt + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
     }
     agpr_drain(dk1[0], dk1[1], dk2[0], dk2[1]);
     agpr_drain(dv[0], dv[1], dv[2], dv[3]);

@@ -84,7 +84,7 @@ def test_bwd_causal_epilogue(N):
     assert relerr(g["dnorm_w"], ref["dg"]) <= TOL_REL
 
 
-@pytest.mark.parametrize("Nq,Nk,causal", [(64, 64, False), (70, 130, True), (40, 200, False)])
+@pytest.mark.parametrize("Nq,Nk,causal", [(64, 64, False), (70, 130, True), (40, 200, False), (300, 260, False), (200, 330, True)])
 def test_bwd_noepi_and_rect(Nq, Nk, causal):
     out, lse, maps, g, ref = run(case(1, Nq, Nk, 3, 3200 + Nq + Nk, causal=causal, epilogue=False))
     for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
