@@ -18,29 +18,48 @@
 //    a three-stage LDS ring); each K row fragment feeds both heads' scores and each transposed K
 //    fragment both heads' dQ.
 //  - bwd_v2_dkdv: 32 keys of one KV head per wave (K and V rows in registers), walking the query
-//    tiles of every pair of the group; dK gathers both heads of every pair, dV every pair.
+//    tiles of every pair of the group; dK gathers both heads of every pair, dV every pair. Items
+//    (query tile, pair) come two per block barrier; where neither holds a masked (query, key) pair
+//    for any wave of the block, their 96 MFMAs run in a fixed order with the second item's score
+//    MFMAs beside the first item's vector work and the first item's gradient MFMAs beside the
+//    second's, each operand read issued four MFMAs ahead.
 // The dQ and dK/dV accumulators sit in AGPRs (inline-asm MFMAs); tiles are 128 wide in the
 // backward layout of bwd_tile.hpp.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
 #include "bwd_tile.hpp"
+#include <utility>
 
 namespace diffattn {
 
 namespace {
 
 using namespace bwdt;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// f(IC<0>), f(IC<1>), ..., f(IC<N - 1>): a loop whose index is a compile-time constant
+template <int... I, class F> __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+    (f(IC<I>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
 
 constexpr int kD = 128;
 constexpr int kTile = kBN * kD * 2;          // bytes of one 32-row, 128-wide tile
 constexpr int kPreRows = 16;                 // rows per pre block (4 waves x 4 rows)
 // dQ key-tile stage: K | V
 constexpr int kKStage = 2 * kTile;
-// dK/dV query-tile stage: Q_{2p} | Q_{2p+1} | go_p | lse [32][2] | dd [32][2] | lambda [32] (+pad)
-constexpr int kQStats = 3 * kTile;
-constexpr int kQStage = kQStats + 3 * 256;
 constexpr int kStages = 3;
+// dK/dV LDS by operand type, four ring slots per region: Q_{2p} | Q_{2p+1} | go_p | statistics
+// (lse [32][2], dd [32][2], lambda [32]); every slot offset fits the LDS immediate
+constexpr int kQRing = 4;
+constexpr int kQ2Off = kQRing * kTile;
+constexpr int kGOff = 2 * kQRing * kTile;
+constexpr int kStOff = 3 * kQRing * kTile;
+constexpr int kStSlot = 3 * 256;
+constexpr int kDkdvLds = kStOff + kQRing * kStSlot;
 
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_v2_pre_kernel(V2BwdArgs a) {
@@ -230,7 +249,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // of every pair of the group. Each lane holds its key's K and V rows as MFMA B operands; dK^T and
 // dV^T of the wave's 32 keys (128 registers) sit in AGPRs. One wave per SIMD.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_v2_dkdv_kernel(V2BwdArgs a) {
-    __shared__ __align__(16) unsigned char sq[kStages * kQStage];
+    __shared__ __align__(16) unsigned char sq[kDkdvLds];
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = tid & 63;
     const int n = lane & 31, h2 = lane >> 5;
     // the first key tiles see the most queries under causal masking: they go first
@@ -273,7 +292,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int qt = qt0 + it / npair, p = g * npair + it % npair;
         const int i0 = qt * kBN;
         const int last = min(kBN, a.seq - i0) - 1;
-        const uint32_t st = lds_sq + stage * kQStage + wave * 1024;
+        const uint32_t st = lds_sq + stage * kTile + wave * 1024;
         const bf16* q1b = (const bf16*)a.q + b * a.qs[0] + (int64_t)i0 * a.qs[1] + (int64_t)(2 * p) * a.qs[2];
         const bf16* q2b = q1b + a.qs[2];
         const int64_t rowb = ((int64_t)b * a.h + p) * a.seq + i0;
@@ -281,12 +300,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int ra = min(r0, last), rb = min(r1, last);
         dma16(q1b, (uint32_t)(ra * a.qs[1] + c0 * 8) * 2u, st);
         dma16(q1b, (uint32_t)(rb * a.qs[1] + c1 * 8) * 2u, st + 4096);
-        dma16(q2b, (uint32_t)(ra * a.qs[1] + c0 * 8) * 2u, st + kTile);
-        dma16(q2b, (uint32_t)(rb * a.qs[1] + c1 * 8) * 2u, st + kTile + 4096);
-        dma16(gb, (uint32_t)(ra * kD + c0 * 8) * 2u, st + 2 * kTile);
-        dma16(gb, (uint32_t)(rb * kD + c1 * 8) * 2u, st + 2 * kTile + 4096);
+        dma16(q2b, (uint32_t)(ra * a.qs[1] + c0 * 8) * 2u, st + kQ2Off);
+        dma16(q2b, (uint32_t)(rb * a.qs[1] + c1 * 8) * 2u, st + kQ2Off + 4096);
+        dma16(gb, (uint32_t)(ra * kD + c0 * 8) * 2u, st + kGOff);
+        dma16(gb, (uint32_t)(rb * kD + c1 * 8) * 2u, st + kGOff + 4096);
         if (wave == 0) {
-            const uint32_t sst = lds_sq + stage * kQStage + kQStats;
+            const uint32_t sst = lds_sq + kStOff + stage * kStSlot;
             const uint32_t fo = (uint32_t)min(lane, 2 * last + 1) * 4u;
             dma4(a.lse + 2 * rowb, fo, sst);
             dma4(a.dd + 2 * rowb, fo, sst + 256);
@@ -294,41 +313,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
 
-    auto compute = [&](auto ST, bool full, int i0) __attribute__((always_inline)) {
-        const unsigned char* Q1s = sq + decltype(ST)::value * kQStage;
-        const unsigned char* Q2s = Q1s + kTile;
-        const unsigned char* Gs = Q1s + 2 * kTile;
-        const float* svl = (const float*)(Q1s + kQStats);   // lse [32][2]
-        const float* svd = svl + 64;                          // dd [32][2]
-        const float* svm = svl + 128;                         // lambda [32]
-        // dP = go V^T, S_j = Q_j K^T (rows = queries, lane = key)
-        f32x16 dp = f32x16{}, s1 = f32x16{}, s2 = f32x16{};
+    // Lane offsets of the LDS reads: the go tiles' carry their region base, hidden from the
+    // compiler so that it keeps one register per offset and puts only the slot offset into the
+    // instruction's immediate; Q_{2p} and Q_{2p+1} share theirs.
+    auto opaque = [](int x) __attribute__((always_inline)) { asm("" : "+v"(x)); return x; };
+    int ro[8], gro[8], tro[2][4][2], gtro[2][4][2];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) dp = mfma32x32x16(lds16(Gs + rowop<kD>(n, kk, h2)), vr[kk], dp);
+    for (int kk = 0; kk < 8; ++kk) { ro[kk] = rowop<kD>(n, kk, h2); gro[kk] = opaque(kGOff + ro[kk]); }
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            s1 = mfma32x32x16(lds16(Q1s + rowop<kD>(n, kk, h2)), kr[kk], s1);
-            s2 = mfma32x32x16(lds16(Q2s + rowop<kD>(n, kk, h2)), kr[kk], s2);
-        }
-        // register r holds query row 8 (r / 4) + 4 h2 + r % 4
-        f32x16 p1, p2, dm1, dm2, nl, ds1, ds2, pc;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int q4 = 8 * gq + 4 * h2;
-            const f32x4 l01 = *(const f32x4*)(svl + 2 * q4), l23 = *(const f32x4*)(svl + 2 * q4 + 4);
-            const f32x4 d01 = *(const f32x4*)(svd + 2 * q4), d23 = *(const f32x4*)(svd + 2 * q4 + 4);
-            const f32x4 lm = *(const f32x4*)(svm + q4);
-            const float lse1[4] = {l01[0], l01[2], l23[0], l23[2]}, lse2[4] = {l01[1], l01[3], l23[1], l23[3]};
-            const float dd1[4] = {d01[0], d01[2], d23[0], d23[2]}, dd2[4] = {d01[1], d01[3], d23[1], d23[3]};
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * gq + j;
-                p1[r] = fast_exp2(fmaf(s1[r], c, -lse1[j]));
-                p2[r] = fast_exp2(fmaf(s2[r], c, -lse2[j]));
-                dm1[r] = dp[r] - dd1[j];
-                dm2[r] = dp[r] - dd2[j];
-                nl[r] = -lm[j];
+            for (int hi = 0; hi < 2; ++hi) {
+                tro[kb][mt][hi] = trop<kD>(lane, kb, mt, hi);
+                gtro[kb][mt][hi] = opaque(kGOff + tro[kb][mt][hi]);
             }
+    const int sto = opaque(kStOff + 32 * h2);   // lse of rows 4 h2 + 8 g + 0..3 at + 64 g, dd at + 256
+    const int stm = opaque(kStOff + 512 + 16 * h2);   // lambda of the same rows at + 32 g
+    // operand of S / dP MFMA i (0-7: go rows for dP, 8-23: Q_{2p} and Q_{2p+1} rows alternately)
+    auto rd_s = [&](int slot, int i) __attribute__((always_inline)) -> bf16x8 {
+        if (i < 8) return lds16(sq + slot * kTile + gro[i]);
+        return lds16(sq + ((i & 1) ? kQ2Off : 0) + slot * kTile + ro[(i - 8) >> 1]);
+    };
+    // operand of gradient MFMA i (kb = i / 12; i % 12: dK mt 0 from Q_{2p}, from Q_{2p+1}, mt 1 ...,
+    // then dV ct 0-3)
+    auto rd_g = [&](int slot, int i) __attribute__((always_inline)) -> bf16x8 {
+        const int kb = i / 12, jj = i % 12;
+        if (jj < 8) return tr_pair(sq + ((jj & 1) ? kQ2Off : 0) + slot * kTile, tro[kb][jj >> 1][0], tro[kb][jj >> 1][1]);
+        return tr_pair(sq + slot * kTile, gtro[kb][jj - 8][0], gtro[kb][jj - 8][1]);
+    };
+    auto mfma_s = [&](int i, bf16x8 o, f32x16& dp, f32x16& s1, f32x16& s2) __attribute__((always_inline)) {
+        if (i < 8) dp = mfma32x32x16(o, vr[i], dp);
+        else if (!(i & 1)) s1 = mfma32x32x16(o, kr[(i - 8) >> 1], s1);
+        else s2 = mfma32x32x16(o, kr[(i - 8) >> 1], s2);
+    };
+    auto mfma_g = [&](int i, bf16x8 o, bf16x8 b1, bf16x8 b2, bf16x8 bp) __attribute__((always_inline)) {
+        const int jj = i % 12;
+        if (jj < 8) mfma_agpr(dk[jj >> 1], o, (jj & 1) ? b2 : b1);
+        else mfma_agpr(dv[jj - 8], o, bp);
+    };
+    // statistics of register row r (query 8 (r / 4) + 4 h2 + r % 4) of a slot's tile
+    auto st_lse = [&](int slot, int r) __attribute__((always_inline)) {
+        return *(const f32x2*)(sq + sto + slot * kStSlot + 64 * (r >> 2) + 8 * (r & 3));
+    };
+    auto st_dd = [&](int slot, int r) __attribute__((always_inline)) {
+        return *(const f32x2*)(sq + sto + slot * kStSlot + 256 + 64 * (r >> 2) + 8 * (r & 3));
+    };
+    auto st_lam = [&](int slot, int r) __attribute__((always_inline)) {
+        return *(const float*)(sq + stm + slot * kStSlot + 32 * (r >> 2) + 4 * (r & 3));
+    };
+    // one row: weights and score gradients (the factor -lambda inside dS_{2p+1}: the dK sum runs
+    // over rows with different lambda)
+    auto row_math = [&](float dp, float s1, float s2, f32x2 l, f32x2 d, float lm, float& ds1, float& ds2, float& pc) __attribute__((always_inline)) {
+        const float p1 = fast_exp2(fmaf(s1, c, -l[0]));
+        const float p2 = fast_exp2(fmaf(s2, c, -l[1]));
+        const float nl = -lm;
+        ds1 = p1 * (dp - d[0]);
+        ds2 = nl * p2 * (dp - d[1]);
+        pc = fmaf(nl, p2, p1);
+    };
+    // one item on its own; !full: some (query, key) pair of the wave's 32 x 32 block is not visible
+    auto compute = [&](int slot, bool full, int i0) __attribute__((always_inline)) {
+        f32x16 dp = {}, s1 = {}, s2 = {};
+#pragma unroll
+        for (int i = 0; i < 24; ++i) mfma_s(i, rd_s(slot, i), dp, s1, s2);
+        float p1[16], p2[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const f32x2 l = st_lse(slot, r);
+            p1[r] = fast_exp2(fmaf(s1[r], c, -l[0]));
+            p2[r] = fast_exp2(fmaf(s2[r], c, -l[1]));
         }
         if (!full) {
             asm volatile("");   // keeps this a branch: full tiles skip the test
@@ -340,50 +395,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 p2[r] = vis ? p2[r] : 0.f;
             }
         }
+        bf16x8 b1[2], b2[2], bp[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            ds1[r] = p1[r] * dm1[r];
-            ds2[r] = nl[r] * p2[r] * dm2[r];
-            pc[r] = fmaf(nl[r], p2[r], p1[r]);
+            const f32x2 d = st_dd(slot, r);
+            const float nl = -st_lam(slot, r);
+            b1[r >> 3][r & 7] = (bf16)(p1[r] * (dp[r] - d[0]));
+            b2[r >> 3][r & 7] = (bf16)(nl * p2[r] * (dp[r] - d[1]));
+            bp[r >> 3][r & 7] = (bf16)fmaf(nl, p2[r], p1[r]);
         }
-        // dK^T += Q_{2p}^T dS_{2p} + Q_{2p+1}^T dS_{2p+1} and dV^T += go^T (A_{2p} - lambda A_{2p+1})
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 b1 = c_to_b(ds1, kb), b2 = c_to_b(ds2, kb), bp = c_to_b(pc, kb);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                mfma_agpr(dk[mt], tr_pair(Q1s, trop<kD>(lane, kb, mt, 0), trop<kD>(lane, kb, mt, 1)), b1);
-                mfma_agpr(dk[mt], tr_pair(Q2s, trop<kD>(lane, kb, mt, 0), trop<kD>(lane, kb, mt, 1)), b2);
-            }
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                mfma_agpr(dv[ct], tr_pair(Gs, trop<kD>(lane, kb, ct, 0), trop<kD>(lane, kb, ct, 1)), bp);
-        }
+        for (int i = 0; i < 24; ++i) mfma_g(i, rd_g(slot, i), b1[i / 12], b2[i / 12], bp[i / 12]);
     };
-    auto step = [&](auto ST, int it) __attribute__((always_inline)) {
-        constexpr int st = decltype(ST)::value;
-        // this thread's DMA of item it has landed (the next item's loads may be in flight)
-        if (it + 1 < nit) {
-            if (wave == 0) __builtin_amdgcn_s_waitcnt(kVmcnt[9]);   // 9 loads per item, one item in flight
-            else __builtin_amdgcn_s_waitcnt(kVmcnt[6]);
+    auto item_i0 = [&](int it) { return (qt0 + it / npair) * kBN; };
+    auto item_full = [&](int i0) { return i0 + kBN <= a.seq && kw0 + kBN <= a.seq && (!a.causal || kw0 + kBN - 1 <= i0); };
+    auto item_skip = [&](int i0) { return !wave_active || (a.causal && i0 + kBN - 1 < kw0); };
+    // two items per block barrier; slots S0, S1 hold them, N0, N1 take the pair after next.
+    // FAST: both items are unmasked for every wave of the block; their 96 MFMAs run in a fixed
+    // order: item A's 24 score MFMAs, item B's 24 beside item A's rows, item A's 24 gradient
+    // MFMAs beside item B's rows, item B's 24, every operand read four MFMAs ahead and a
+    // scheduling barrier after each MFMA.
+    auto pair = [&](auto FAST, int it, auto S0, auto S1, auto N0, auto N1) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt[0]);   // this thread's DMA of items it, it + 1 landed
+        __syncthreads();   // every thread's loads landed; the slots of the previous pair are free
+        if (it + 2 < nit) issue(it + 2, decltype(N0)::value);
+        if (it + 3 < nit) issue(it + 3, decltype(N1)::value);
+        constexpr int sa = decltype(S0)::value, sb = decltype(S1)::value;
+        if constexpr (decltype(FAST)::value) {
+            constexpr int kLead = 4;
+            f32x16 dpA = {}, s1A = {}, s2A = {}, dpB = {}, s1B = {}, s2B = {};
+            float ds1A[16], ds2A[16], pcA[16], ds1B[16], ds2B[16], pcB[16];
+            bf16x8 b1A[2], b2A[2], bpA[2], b1B[2], b2B[2], bpB[2];
+            bf16x8 op[96];
+            f32x2 sl[32], sd[32];
+            float sm[32];
+            // MFMA m: [0,24) scores of A, [24,48) scores of B, [48,72) gradients of A, [72,96) of B
+            auto read_op = [&](int m) __attribute__((always_inline)) {
+                if (m < 24) op[m] = rd_s(sa, m);
+                else if (m < 48) op[m] = rd_s(sb, m - 24);
+                else if (m < 72) op[m] = rd_g(sa, m - 48);
+                else op[m] = rd_g(sb, m - 72);
+            };
+            auto issue_mfma = [&](int m) __attribute__((always_inline)) {
+                if (m < 24) mfma_s(m, op[m], dpA, s1A, s2A);
+                else if (m < 48) mfma_s(m - 24, op[m], dpB, s1B, s2B);
+                else if (m < 72) { const int kb = (m - 48) / 12; mfma_g(m - 48, op[m], b1A[kb], b2A[kb], bpA[kb]); }
+                else { const int kb = (m - 72) / 12; mfma_g(m - 72, op[m], b1B[kb], b2B[kb], bpB[kb]); }
+            };
+            // row job j: [0,16) rows of A (beside B's scores), [16,32) rows of B (beside A's
+            // gradients); job j follows MFMA 24 + (3 j) / 2; its statistics are read two jobs ahead
+            auto read_row = [&](int j) __attribute__((always_inline)) {
+                const int slot = j < 16 ? sa : sb, r = j & 15;
+                sl[j] = st_lse(slot, r); sd[j] = st_dd(slot, r); sm[j] = st_lam(slot, r);
+            };
+            auto job = [&](int j) __attribute__((always_inline)) {
+                const int r = j & 15;
+                if (j < 16) {
+                    row_math(dpA[r], s1A[r], s2A[r], sl[j], sd[j], sm[j], ds1A[r], ds2A[r], pcA[r]);
+                    if ((r & 7) == 7) {
+                        const int kb = r >> 3;
+                        for (int t = 0; t < 8; ++t) {
+                            b1A[kb][t] = (bf16)ds1A[8 * kb + t]; b2A[kb][t] = (bf16)ds2A[8 * kb + t]; bpA[kb][t] = (bf16)pcA[8 * kb + t];
+                        }
+                    }
+                } else {
+                    row_math(dpB[r], s1B[r], s2B[r], sl[j], sd[j], sm[j], ds1B[r], ds2B[r], pcB[r]);
+                    if ((r & 7) == 7) {
+                        const int kb = r >> 3;
+                        for (int t = 0; t < 8; ++t) {
+                            b1B[kb][t] = (bf16)ds1B[8 * kb + t]; b2B[kb][t] = (bf16)ds2B[8 * kb + t]; bpB[kb][t] = (bf16)pcB[8 * kb + t];
+                        }
+                    }
+                }
+            };
+            static_for<kLead>([&](auto M) __attribute__((always_inline)) { read_op(decltype(M)::value); });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<96>([&](auto M) __attribute__((always_inline)) {
+                constexpr int m = decltype(M)::value;
+                if (m + kLead < 96) read_op(m + kLead);
+                issue_mfma(m);
+                // jobs after MFMA 24 + floor(3 j / 2): j = 0 at 24, 1 at 25, 2 at 27, 3 at 28, ...
+                if (m == 22) { read_row(0); read_row(1); }
+                if (m >= 24 && m < 72) {
+                    const int u = m - 24;   // u = floor(3 j / 2) has a solution j iff u % 3 != 2
+                    if (u % 3 != 2) {
+                        const int j = (2 * u + 2) / 3;
+                        if (j + 2 < 32) read_row(j + 2);
+                        job(j);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
         } else {
-            __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
+            const int iA = item_i0(it);
+            if (!item_skip(iA)) compute(sa, item_full(iA), iA);
+            if (it + 1 < nit) {
+                const int iB = item_i0(it + 1);
+                if (!item_skip(iB)) compute(sb, item_full(iB), iB);
+            }
         }
-        __syncthreads();   // every thread's loads of item it landed; the stage of item it-1 is free
-        if (it + kStages - 1 < nit) issue(it + kStages - 1, (st + kStages - 1) % kStages);
-        const int i0 = (qt0 + it / npair) * kBN;
-        // skip the tile if it ends before this wave's first key (causal)
-        if (!wave_active || (a.causal && i0 + kBN - 1 < kw0)) return;
-        compute(ST, i0 + kBN <= a.seq && kw0 + kBN <= a.seq && (!a.causal || kw0 + kBN - 1 <= i0), i0);
     };
-    for (int it = 0; it < nit && it < kStages - 1; ++it) issue(it, it);
+    // Items [is, ie) are unmasked for the whole block and go through the FAST pairs, the others
+    // through the masked ones. Both bounds are multiples of four, so ring slot = item modulo 4 in
+    // every loop, each unrolled by two pairs so that every LDS address is a register plus a
+    // constant.
+    int is = nit, ie = nit;
+    if (k0 + 128 <= a.seq) {
+        const int qf = a.causal ? (k0 + 127 + kBN - 1) / kBN : 0;   // first tile unmasked for all waves
+        const int qe = a.seq / kBN;                                    // tiles below hold no row past the end
+        const int i_f = (max(qf, qt0) - qt0) * npair, i_e = (qe - qt0) * npair;
+        const int i4 = (i_f + 3) / 4 * 4;
+        if (i4 + 4 <= i_e) { is = i4; ie = i4 + (i_e - i4) / 4 * 4; }
+    }
+    for (int it = 0; it < nit && it < 2; ++it) issue(it, it);
     // the key operands and the first tiles have landed: from here on the compiler sees no
     // outstanding loads of its own and adds no waits on the query-tile DMA
     __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
-    for (int it = 0; it < nit; it += kStages) {
-        step(IC<0>{}, it);
-        if (it + 1 < nit) step(IC<1>{}, it + 1);
-        if (it + 2 < nit) step(IC<2>{}, it + 2);
+    int it = 0;
+    for (; it < is; it += 4) {
+        pair(std::false_type{}, it, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        if (it + 2 < nit) pair(std::false_type{}, it + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
+    }
+    for (; it < ie; it += 4) {
+        pair(std::true_type{}, it, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        pair(std::true_type{}, it + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
+    }
+    for (; it < nit; it += 4) {
+        pair(std::false_type{}, it, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        if (it + 2 < nit) pair(std::false_type{}, it + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
     }
     agpr_drain(dk[0], dk[1], dk[2], dk[3]);
     agpr_drain(dv[0], dv[1], dv[2], dv[3]);

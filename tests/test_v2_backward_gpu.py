@@ -89,6 +89,13 @@ def test_v2_bwd_groupings(hq, hkv):
     check(g, ref)
 
 
+@pytest.mark.parametrize("hq,hkv,N", [(4, 2, 200), (32, 2, 130)])
+def test_v2_bwd_groupings_noncausal(hq, hkv, N):
+    # one and eight pairs per KV head with every tile unmasked but the ragged last one
+    *_, g, ref = run(case(1, N, hq, hkv, 5250 + hq + N, causal=False))
+    check(g, ref)
+
+
 def test_v2_bwd_noncausal_and_logits():
     *_, g, ref = run(case(2, 150, 8, 2, 5300, causal=False))
     check(g, ref)
