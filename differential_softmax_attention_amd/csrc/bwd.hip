@@ -31,21 +31,12 @@
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
 #include "bwd_tile.hpp"
-#include <utility>
 
 namespace diffattn {
 
 namespace {
 
 using namespace bwdt;
-
-// f(IC<0>), f(IC<1>), ..., f(IC<N - 1>): a loop whose index is a compile-time constant
-template <int... I, class F> __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
-    (f(IC<I>{}), ...);
-}
-template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(std::make_integer_sequence<int, N>{}, f);
-}
 
 constexpr int kD = 64;
 constexpr int kDV = 128;

@@ -11,6 +11,7 @@
 #pragma once
 #include "common.hpp"
 #include "mfma_tile.hpp"
+#include <utility>
 
 namespace diffattn {
 namespace bwdt {
@@ -67,6 +68,14 @@ __device__ __forceinline__ void agpr_drain(f32x16& x0, f32x16& x1, f32x16& x2, f
 }
 
 template <int V> struct IC { static constexpr int value = V; };
+
+// f(IC<0>), f(IC<1>), ..., f(IC<N - 1>): a loop whose index is a compile-time constant
+template <int... I, class F> __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+    (f(IC<I>{}), ...);
+}
+template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
 
 }  // namespace bwdt
 }  // namespace diffattn

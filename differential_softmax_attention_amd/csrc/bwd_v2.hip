@@ -15,8 +15,9 @@
 //  - bwd_v2_pre: one wave per (row, pair): go (a copy of dout, head-major for the DMA), D_1, D_2,
 //    lambda after the sigmoid, and dlambda.
 //  - bwd_v2_dq: 32 queries of one pair per wave, walking key tiles (K and V of the group through
-//    a three-stage LDS ring); each K row fragment feeds both heads' scores and each transposed K
-//    fragment both heads' dQ.
+//    a four-slot LDS ring, two tiles per block barrier); each K row fragment feeds both heads'
+//    scores and each transposed K fragment both heads' dQ. Pairs of unmasked tiles run their 80
+//    MFMAs in a fixed order, the second tile's score MFMAs beside the first tile's vector work.
 //  - bwd_v2_dkdv: 32 keys of one KV head per wave (K and V rows in registers), walking the query
 //    tiles of every pair of the group; dK gathers both heads of every pair, dV every pair. Items
 //    (query tile, pair) come two per block barrier; where neither holds a masked (query, key) pair
@@ -29,7 +30,6 @@
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
 #include "bwd_tile.hpp"
-#include <utility>
 
 namespace diffattn {
 
@@ -38,20 +38,11 @@ namespace {
 using namespace bwdt;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// f(IC<0>), f(IC<1>), ..., f(IC<N - 1>): a loop whose index is a compile-time constant
-template <int... I, class F> __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
-    (f(IC<I>{}), ...);
-}
-template <int N, class F> __device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(std::make_integer_sequence<int, N>{}, f);
-}
-
 constexpr int kD = 128;
 constexpr int kTile = kBN * kD * 2;          // bytes of one 32-row, 128-wide tile
 constexpr int kPreRows = 16;                 // rows per pre block (4 waves x 4 rows)
 // dQ key-tile stage: K | V
 constexpr int kKStage = 2 * kTile;
-constexpr int kStages = 3;
 // dK/dV LDS by operand type, four ring slots per region: Q_{2p} | Q_{2p+1} | go_p | statistics
 // (lse [32][2], dd [32][2], lambda [32]); every slot offset fits the LDS immediate
 constexpr int kQRing = 4;
@@ -96,7 +87,7 @@ __global__ __launch_bounds__(256) void bwd_v2_pre_kernel(V2BwdArgs a) {
 // ------------------------------------------------------------------------------------------------
 // dQ: a block of 4 waves owns 128 queries of one pair, 32 per wave, and walks the key tiles.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_v2_dq_kernel(V2BwdArgs a) {
-    __shared__ __align__(16) unsigned char smem[kStages * kKStage];
+    __shared__ __align__(16) unsigned char smem[4 * kKStage];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, h2 = lane >> 5;
     // the last query tiles see the most keys under causal masking: they go first
@@ -156,8 +147,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dma16(vt_p, (uint32_t)(min(r1, last) * a.vs[1] + c1 * 8) * 2u, st + kTile + 4096);
     };
 
-    auto compute = [&](auto ST, bool full, int k0) __attribute__((always_inline)) {
-        const unsigned char* Ks = smem + decltype(ST)::value * kKStage;
+    auto compute = [&](int slot, bool full, int k0) __attribute__((always_inline)) {
+        const unsigned char* Ks = smem + slot * kKStage;
         const unsigned char* Vs = Ks + kTile;
         // S_j^T = K Q_j^T (lane = query n, 16 keys), dP^T = V go^T
         f32x16 s1 = f32x16{}, s2 = f32x16{}, dp = f32x16{};
@@ -202,24 +193,123 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
     };
-    auto tile = [&](auto ST, int kt) __attribute__((always_inline)) {
-        constexpr int st = decltype(ST)::value;
-        if (kt + 1 < nkt) __builtin_amdgcn_s_waitcnt(kVmcnt[4]);   // tile kt+1's loads may stay in flight
-        else __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
-        __syncthreads();   // tile kt landed for every thread; the stage of tile kt-1 is free
-        if (kt + kStages - 1 < nkt) issue(kt + kStages - 1, (st + kStages - 1) % kStages);
-        const int k0 = kt * kBN;
-        if (!wave_active || (a.causal && k0 > wave_qlast)) return;
-        compute(ST, qw0 + kBN <= a.seq && k0 + kBN <= a.seq && (!a.causal || k0 + kBN - 1 <= qw0), k0);
+    auto tile_full = [&](int k0) { return qw0 + kBN <= a.seq && k0 + kBN <= a.seq && (!a.causal || k0 + kBN - 1 <= qw0); };
+    auto tile_skip = [&](int k0) { return !wave_active || (a.causal && k0 > wave_qlast); };
+    // two key tiles per block barrier; slots S0, S1 hold them, N0, N1 take the pair after next.
+    // FAST: both tiles are unmasked for every wave of the block; their 80 MFMAs run in a fixed
+    // order: tile A's 24 score and dP MFMAs, tile B's 24 beside tile A's rows, tile A's 16 dQ
+    // MFMAs beside tile B's rows, tile B's 16, operand reads issued about four MFMAs ahead and a
+    // scheduling barrier after each MFMA.
+    auto pair = [&](auto FAST, int kt, auto S0, auto S1, auto N0, auto N1) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt[0]);   // this thread's DMA of tiles kt, kt + 1 landed
+        __syncthreads();   // every thread's loads landed; the slots of the previous pair are free
+        if (kt + 2 < nkt) issue(kt + 2, decltype(N0)::value);
+        if (kt + 3 < nkt) issue(kt + 3, decltype(N1)::value);
+        const unsigned char* KA = smem + decltype(S0)::value * kKStage;
+        const unsigned char* KB = smem + decltype(S1)::value * kKStage;
+        if constexpr (decltype(FAST)::value) {
+            constexpr int kLead = 4;
+            f32x16 s1A = {}, s2A = {}, dpA = {}, s1B = {}, s2B = {}, dpB = {};
+            float ds1A[16], ds2A[16], ds1B[16], ds2B[16];
+            bf16x8 b1A[2], b2A[2], b1B[2], b2B[2];
+            bf16x8 op[48];
+            // operands: [0,8) K rows of A, [8,16) V rows of A, [16,32) the same of B, [32,40)
+            // transposed K of A, [40,48) of B
+            auto opidx = [](int m) constexpr {
+                return m < 16 ? (m >> 1) : m < 24 ? 8 + (m - 16) : m < 40 ? 16 + ((m - 24) >> 1)
+                     : m < 48 ? 24 + (m - 40) : m < 64 ? 32 + ((m - 48) >> 1) : 40 + ((m - 64) >> 1);
+            };
+            auto read_op = [&](int o) __attribute__((always_inline)) {
+                const unsigned char* T = (o < 16 || (o >= 32 && o < 40)) ? KA : KB;
+                if (o < 32) {
+                    const int u = o & 15;
+                    op[o] = u < 8 ? lds16(T + rowop<kD>(n, u, h2)) : lds16(T + kTile + rowop<kD>(n, u - 8, h2));
+                } else {
+                    const int u = o & 7, kb = u >> 2, mt = u & 3;
+                    op[o] = tr_pair(T, trop<kD>(lane, kb, mt, 0), trop<kD>(lane, kb, mt, 1));
+                }
+            };
+            auto issue_mfma = [&](int m) __attribute__((always_inline)) {
+                const bf16x8 o = op[opidx(m)];
+                if (m < 48) {
+                    const int i = m < 24 ? m : m - 24;
+                    f32x16& s1 = m < 24 ? s1A : s1B;
+                    f32x16& s2 = m < 24 ? s2A : s2B;
+                    f32x16& dp = m < 24 ? dpA : dpB;
+                    if (i < 16) {
+                        if (i & 1) s2 = mfma32x32x16(o, bq2[i >> 1], s2);
+                        else s1 = mfma32x32x16(o, bq1[i >> 1], s1);
+                    } else {
+                        dp = mfma32x32x16(o, bg[i - 16], dp);
+                    }
+                } else {
+                    const int i = m < 64 ? m - 48 : m - 64, kb = i >> 3, mt = (i >> 1) & 3;
+                    if (i & 1) mfma_agpr(dq2[mt], o, m < 64 ? b2A[kb] : b2B[kb]);
+                    else mfma_agpr(dq1[mt], o, m < 64 ? b1A[kb] : b1B[kb]);
+                }
+            };
+            // row r of a tile (its 16 registers hold keys k0 + 8 (r / 4) + 4 h2 + r % 4)
+            auto row = [&](const f32x16& s1, const f32x16& s2, const f32x16& dp, int r, float* ds1, float* ds2) __attribute__((always_inline)) {
+                const float p1 = fast_exp2(fmaf(s1[r], c, -lse1));
+                const float p2 = fast_exp2(fmaf(s2[r], c, -lse2));
+                ds1[r] = p1 * (dp[r] - D1);
+                ds2[r] = p2 * (dp[r] - D2);   // the row's factor -lambda is applied to dQ_{2p+1} at the store
+            };
+            auto pack = [&](const float* ds1, const float* ds2, int kb, bf16x8* b1, bf16x8* b2) __attribute__((always_inline)) {
+                for (int t = 0; t < 8; ++t) { b1[kb][t] = (bf16)ds1[8 * kb + t]; b2[kb][t] = (bf16)ds2[8 * kb + t]; }
+            };
+            static_for<48>([&](auto O) __attribute__((always_inline)) {
+                constexpr int o = decltype(O)::value;
+                if (o <= opidx(kLead)) read_op(o);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<80>([&](auto M) __attribute__((always_inline)) {
+                constexpr int m = decltype(M)::value;
+                if (m + kLead < 80) {
+                    static_for<48>([&](auto O) __attribute__((always_inline)) {
+                        constexpr int o = decltype(O)::value;
+                        if (o > opidx(m + kLead - 1) && o <= opidx(m + kLead)) read_op(o);
+                    });
+                }
+                issue_mfma(m);
+                if (m >= 24 && m < 48) {
+                    const int u = m - 24;   // rows of A: row j after MFMA 24 + floor(3 j / 2)
+                    if (u % 3 != 2) {
+                        const int r = (2 * u + 2) / 3;
+                        row(s1A, s2A, dpA, r, ds1A, ds2A);
+                        if ((r & 7) == 7) pack(ds1A, ds2A, r >> 3, b1A, b2A);
+                    }
+                } else if (m >= 48 && m < 64) {
+                    const int r = m - 48;   // rows of B, one after each of A's dQ MFMAs
+                    row(s1B, s2B, dpB, r, ds1B, ds2B);
+                    if ((r & 7) == 7) pack(ds1B, ds2B, r >> 3, b1B, b2B);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        } else {
+            const int kA = kt * kBN, kB = kA + kBN;
+            if (!tile_skip(kA)) compute(decltype(S0)::value, tile_full(kA), kA);
+            if (kt + 1 < nkt && !tile_skip(kB)) compute(decltype(S1)::value, tile_full(kB), kB);
+        }
     };
-    for (int kt = 0; kt < nkt && kt < kStages - 1; ++kt) issue(kt, kt);
+    // Key tiles [0, kf) are unmasked for every wave of the block (the causal diagonal and a ragged
+    // end come last); the fast pairs take them in whole ring periods of four tiles, so ring slot =
+    // tile modulo 4 in both loops, each unrolled by two pairs so that every LDS address is a
+    // register plus a constant.
+    int kf = 0;
+    if (q0 + 128 <= a.seq) kf = (a.causal ? q0 : a.seq) / kBN / 4 * 4;
+    for (int kt = 0; kt < nkt && kt < 2; ++kt) issue(kt, kt);
     // the query operands and the first tiles have landed: from here on the compiler sees no
     // outstanding loads of its own and adds no waits on the key-tile DMA
     __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
-    for (int kt = 0; kt < nkt; kt += kStages) {
-        tile(IC<0>{}, kt);
-        if (kt + 1 < nkt) tile(IC<1>{}, kt + 1);
-        if (kt + 2 < nkt) tile(IC<2>{}, kt + 2);
+    int kt = 0;
+    for (; kt < kf; kt += 4) {
+        pair(std::true_type{}, kt, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        pair(std::true_type{}, kt + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
+    }
+    for (; kt < nkt; kt += 4) {
+        pair(std::false_type{}, kt, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
+        if (kt + 2 < nkt) pair(std::false_type{}, kt + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
     }
     agpr_drain(dq1[0], dq1[1], dq1[2], dq1[3]);
     agpr_drain(dq2[0], dq2[1], dq2[2], dq2[3]);
