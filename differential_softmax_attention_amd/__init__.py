@@ -133,17 +133,25 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
 
 
+def _dp(x: torch.Tensor) -> int:
+    """Device address of a GPU tensor. Every pointer the library receives is dereferenced on the
+    GPU, so a host tensor is refused here rather than handed over."""
+    if not x.is_cuda:
+        raise ValueError(f"expected a tensor on the GPU, got one on {x.device}")
+    return x.data_ptr()
+
+
 def _t4(x: torch.Tensor) -> Tensor:
     """A [B, N, H, dim] tensor (last dim contiguous) as a diffattn_tensor."""
     if x.dim() != 4:
         raise ValueError(f"expected a 4-d [batch, tokens, heads, dim] tensor, got shape {tuple(x.shape)}")
     if x.stride(3) != 1 and x.shape[3] > 1:
         raise ValueError("the last dimension must be contiguous")
-    return Tensor(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2))
+    return Tensor(_dp(x), x.stride(0), x.stride(1), x.stride(2))
 
 
 def _ptr(x):
-    return None if x is None else x.data_ptr()
+    return None if x is None else _dp(x)
 
 
 def _stream(device) -> int:
@@ -164,7 +172,7 @@ def diffattn_lambda(lq1, lk1, lq2, lk2, layer: int, out: torch.Tensor | None = N
     n, dim = vecs[0].shape
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=vecs[0].device)
-    _check(lib().diffattn_lambda(*(v.data_ptr() for v in vecs), n, dim, int(layer), out.data_ptr(),
+    _check(lib().diffattn_lambda(*(_dp(v) for v in vecs), n, dim, int(layer), _dp(out),
                                  _stream(out.device)))
     return out
 
@@ -179,7 +187,7 @@ def diffattn_fwd(q1, q2, k1, k2, v, lam: torch.Tensor, causal: bool = True, epil
     if out is None:
         out = torch.empty((B, Nq, H, dv), dtype=q1.dtype, device=q1.device)
     _check(lib().diffattn_fwd(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1), _t4(k2), _t4(v), B, H, Nq, Nk,
-                              d, dv, lam.data_ptr(), float(lambda_init_value), int(bool(causal)),
+                              d, dv, _dp(lam), float(lambda_init_value), int(bool(causal)),
                               EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
                               float(scale), _t4(out), _stream(q1.device)))
     return out
@@ -209,10 +217,10 @@ def diffattn_decode(q1, q2, k1c, k2c, vc, lam: torch.Tensor, cache_lens: torch.T
     if cache_lens is not None and cache_lens.dtype != torch.int32:
         raise ValueError("cache_lens must be int32")
     _check(lib().diffattn_decode(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1c), _t4(k2c), _t4(vc),
-                                 _ptr(cache_lens), B, H, L, d, dv, lam.data_ptr(),
+                                 _ptr(cache_lens), B, H, L, d, dv, _dp(lam),
                                  float(lambda_init_value),
                                  EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
-                                 float(scale), _t4(out), workspace.data_ptr(), workspace.numel(),
+                                 float(scale), _t4(out), _dp(workspace), workspace.numel(),
                                  _stream(q1.device)))
     return out.squeeze(1)
 
@@ -231,7 +239,7 @@ def diffattn_v2_fwd(q, k, v, lam: torch.Tensor, causal: bool = True, scale: floa
         raise ValueError("lam must be a contiguous float32 [B, N, h] tensor")
     if out is None:
         out = torch.empty((B, N, h, d), dtype=q.dtype, device=q.device)
-    _check(lib().diffattn_v2_fwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), lam.data_ptr(), int(bool(lam_logits)), B, N,
+    _check(lib().diffattn_v2_fwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), _dp(lam), int(bool(lam_logits)), B, N,
                                  h, hkv,
                                  d, int(bool(causal)), float(scale), _t4(out), _stream(q.device)))
     return out
@@ -248,9 +256,9 @@ def diffattn_fwd_train(q1, q2, k1, k2, v, lam: torch.Tensor, causal: bool = True
     lse = torch.empty((B, H, Nq, 2), dtype=torch.float32, device=q1.device)
     maps = torch.empty((B, Nq, H, 2, dv), dtype=torch.float32, device=q1.device)
     _check(lib().diffattn_fwd_train(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1), _t4(k2), _t4(v), B, H, Nq, Nk, d,
-                                    dv, lam.data_ptr(), float(lambda_init_value), int(bool(causal)),
+                                    dv, _dp(lam), float(lambda_init_value), int(bool(causal)),
                                     EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
-                                    float(scale), _t4(out), lse.data_ptr(), maps.data_ptr(), _stream(q1.device)))
+                                    float(scale), _t4(out), _dp(lse), _dp(maps), _stream(q1.device)))
     return out, lse, maps
 
 
@@ -267,8 +275,8 @@ def diffattn_fwd_lambda(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer: int, causa
     if lam_out is None:
         lam_out = torch.empty((H,), dtype=torch.float32, device=q1.device)
     _check(lib().diffattn_fwd_lambda(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1), _t4(k2), _t4(v), B, H, Nq, Nk, d,
-                                     dv, *(x.data_ptr() for x in vecs), vecs[0].shape[1], int(layer),
-                                     lam_out.data_ptr(), int(bool(causal)),
+                                     dv, *(_dp(x) for x in vecs), vecs[0].shape[1], int(layer),
+                                     _dp(lam_out), int(bool(causal)),
                                      EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
                                      float(scale), _t4(out), _stream(q1.device)))
     return out, lam_out
@@ -284,7 +292,7 @@ def diffattn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None):
         out = torch.empty((B, N, H, dim), dtype=torch.float8_e4m3fn, device=x.device)
     scales = torch.empty((B, H), dtype=torch.float32, device=x.device)
     amax = torch.empty((B, H), dtype=torch.float32, device=x.device)
-    _check(lib().diffattn_quantize_fp8(_t4(x), B, N, H, dim, _t4(out), scales.data_ptr(), amax.data_ptr(),
+    _check(lib().diffattn_quantize_fp8(_t4(x), B, N, H, dim, _t4(out), _dp(scales), _dp(amax),
                                        _stream(x.device)))
     return out, scales, amax
 
@@ -298,8 +306,8 @@ def diffattn_fwd_fp8(q1, q2, k1, k2, sq1, sq2, sk1, sk2, v, lam: torch.Tensor, c
     Nk, dv = k1.shape[1], v.shape[3]
     if out is None:
         out = torch.empty((B, Nq, H, dv), dtype=torch.bfloat16, device=v.device)
-    _check(lib().diffattn_fwd_fp8(_t4(q1), _t4(q2), _t4(k1), _t4(k2), sq1.data_ptr(), sq2.data_ptr(),
-                                  sk1.data_ptr(), sk2.data_ptr(), _t4(v), B, H, Nq, Nk, d, dv, lam.data_ptr(),
+    _check(lib().diffattn_fwd_fp8(_t4(q1), _t4(q2), _t4(k1), _t4(k2), _dp(sq1), _dp(sq2),
+                                  _dp(sk1), _dp(sk2), _t4(v), B, H, Nq, Nk, d, dv, _dp(lam),
                                   float(lambda_init_value), int(bool(causal)),
                                   EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps), float(scale),
                                   _t4(out), _stream(v.device)))
@@ -321,9 +329,9 @@ def diffattn_v2_fwd_train(q, k, v, lam: torch.Tensor, causal: bool = True, scale
         out = torch.empty((B, N, h, d), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, h, N, 2), dtype=torch.float32, device=q.device)
     maps = torch.empty((B, N, h, 2, d), dtype=torch.float32, device=q.device)
-    _check(lib().diffattn_v2_fwd_train(_dtype_code(q), _t4(q), _t4(k), _t4(v), lam.data_ptr(), int(bool(lam_logits)),
-                                       B, N, h, hkv, d, int(bool(causal)), float(scale), _t4(out), lse.data_ptr(),
-                                       maps.data_ptr(), _stream(q.device)))
+    _check(lib().diffattn_v2_fwd_train(_dtype_code(q), _t4(q), _t4(k), _t4(v), _dp(lam), int(bool(lam_logits)),
+                                       B, N, h, hkv, d, int(bool(causal)), float(scale), _t4(out), _dp(lse),
+                                       _dp(maps), _stream(q.device)))
     return out, lse, maps
 
 
@@ -343,10 +351,10 @@ def diffattn_v2_bwd(q, k, v, dout, lam: torch.Tensor, lse: torch.Tensor, maps: t
     need = diffattn_v2_bwd_workspace_size(B, h, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check(lib().diffattn_v2_bwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), _t4(dout), lam.data_ptr(),
+    _check(lib().diffattn_v2_bwd(_dtype_code(q), _t4(q), _t4(k), _t4(v), _t4(dout), _dp(lam),
                                  int(bool(lam_logits)), B, N, h, hkv, d, int(bool(causal)), float(scale),
-                                 lse.data_ptr(), maps.data_ptr(), _t4(g["dq"]), _t4(g["dk"]), _t4(g["dv"]),
-                                 dlam.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+                                 _dp(lse), _dp(maps), _t4(g["dq"]), _t4(g["dk"]), _t4(g["dv"]),
+                                 _dp(dlam), _dp(workspace), workspace.numel(), _stream(q.device)))
     g["dlam"] = dlam
     return g
 
@@ -370,10 +378,10 @@ def diffattn_bwd(q1, q2, k1, k2, v, dout, lam: torch.Tensor, lse: torch.Tensor, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q1.device)
     _check(lib().diffattn_bwd(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1), _t4(k2), _t4(v), _t4(dout), B, H, Nq,
-                              Nk, d, dv, lam.data_ptr(), float(lambda_init_value), int(bool(causal)),
+                              Nk, d, dv, _dp(lam), float(lambda_init_value), int(bool(causal)),
                               EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps), float(scale),
-                              lse.data_ptr(), maps.data_ptr(), _t4(g["dq1"]), _t4(g["dq2"]), _t4(g["dk1"]),
-                              _t4(g["dk2"]), _t4(g["dv"]), dlam.data_ptr(), _ptr(dnw), workspace.data_ptr(),
+                              _dp(lse), _dp(maps), _t4(g["dq1"]), _t4(g["dq2"]), _t4(g["dk1"]),
+                              _t4(g["dk2"]), _t4(g["dv"]), _dp(dlam), _ptr(dnw), _dp(workspace),
                               workspace.numel(), _stream(q1.device)))
     g["dlam"] = dlam
     g["dnorm_w"] = dnw
@@ -386,8 +394,8 @@ def diffattn_lambda_bwd(lq1, lk1, lq2, lk2, dlam) -> dict:
     n, dim = vecs[0].shape
     outs = [torch.empty_like(x) for x in vecs]
     dl = dlam.reshape(-1).contiguous()
-    _check(lib().diffattn_lambda_bwd(*(x.data_ptr() for x in vecs), dl.data_ptr(), n, dim,
-                                     *(x.data_ptr() for x in outs), _stream(vecs[0].device)))
+    _check(lib().diffattn_lambda_bwd(*(_dp(x) for x in vecs), _dp(dl), n, dim,
+                                     *(_dp(x) for x in outs), _stream(vecs[0].device)))
     return dict(dlq1=outs[0], dlk1=outs[1], dlq2=outs[2], dlk2=outs[3])
 
 
@@ -419,8 +427,8 @@ def diffattn_v2_decode(q, kc, vc, lam: torch.Tensor, cache_lens: torch.Tensor | 
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if cache_lens is not None and cache_lens.dtype != torch.int32:
         raise ValueError("cache_lens must be int32")
-    _check(lib().diffattn_v2_decode(_dtype_code(q), _t4(q), _t4(kc), _t4(vc), _ptr(cache_lens), lam.data_ptr(),
-                                    int(bool(lam_logits)), B, h, hkv, L, d, float(scale), _t4(out), workspace.data_ptr(),
+    _check(lib().diffattn_v2_decode(_dtype_code(q), _t4(q), _t4(kc), _t4(vc), _ptr(cache_lens), _dp(lam),
+                                    int(bool(lam_logits)), B, h, hkv, L, d, float(scale), _t4(out), _dp(workspace),
                                     workspace.numel(), _stream(q.device)))
     return out.squeeze(1)
 
@@ -455,10 +463,10 @@ def diffattn_decode_paged(q1, q2, k1_pages, k2_pages, v_pages, block_table: torc
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q1.device)
     _check(lib().diffattn_decode_paged(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1_pages), _t4(k2_pages),
-                                       _t4(v_pages), block_table.data_ptr(), block_table.stride(0), P, page,
-                                       _ptr(cache_lens), B, H, L, d, dv, lam.data_ptr(), float(lambda_init_value),
+                                       _t4(v_pages), _dp(block_table), block_table.stride(0), P, page,
+                                       _ptr(cache_lens), B, H, L, d, dv, _dp(lam), float(lambda_init_value),
                                        EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
-                                       float(scale), _t4(out), workspace.data_ptr(), workspace.numel(),
+                                       float(scale), _t4(out), _dp(workspace), workspace.numel(),
                                        _stream(q1.device)))
     return out.squeeze(1)
 
@@ -489,10 +497,10 @@ def diffattn_v2_decode_paged(q, k_pages, v_pages, block_table: torch.Tensor, lam
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().diffattn_v2_decode_paged(_dtype_code(q), _t4(q), _t4(k_pages), _t4(v_pages),
-                                          block_table.data_ptr(), block_table.stride(0), P, page,
-                                          _ptr(cache_lens), lam.data_ptr(), int(bool(lam_logits)), B, h, hkv, L, d,
+                                          _dp(block_table), block_table.stride(0), P, page,
+                                          _ptr(cache_lens), _dp(lam), int(bool(lam_logits)), B, h, hkv, L, d,
                                           float(scale), _t4(out),
-                                          workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+                                          _dp(workspace), workspace.numel(), _stream(q.device)))
     return out.squeeze(1)
 
 
@@ -500,7 +508,7 @@ def diffattn_probe_mfma_peak(blocks: int = 4096, iters: int = 2000, device="cuda
     """Launch the dense bf16 MFMA rate probe once; returns (output tensor, flop of the launch)."""
     out = torch.empty((blocks * 256,), dtype=torch.float32, device=device)
     flop = ctypes.c_double(0.0)
-    _check(lib().diffattn_probe_mfma_peak(out.data_ptr(), int(blocks), int(iters), ctypes.byref(flop),
+    _check(lib().diffattn_probe_mfma_peak(_dp(out), int(blocks), int(iters), ctypes.byref(flop),
                                           _stream(out.device)))
     return out, flop.value
 

@@ -259,3 +259,16 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         da.lib()
     with pytest.raises(RuntimeError, match="not built"):
         da.diffattn_bwd_workspace_size(1, 1, 1)
+
+
+def test_host_tensors_refused():
+    import torch
+    # every pointer the library receives is dereferenced on the GPU: a host tensor must be
+    # refused by the binding before any launch
+    q = torch.zeros((1, 8, 4, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16)
+    lam = torch.zeros((1, 8, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="on the GPU"):
+        da.diffattn_v2_fwd(q, k, k.clone(), lam, causal=True)
+    with pytest.raises(ValueError, match="on the GPU"):
+        da._dp(lam)
