@@ -33,14 +33,18 @@ constexpr unsigned kVmcnt[16] = {0x0F70, 0x0F71, 0x0F72, 0x0F73, 0x0F74, 0x0F75,
 // does not track it as an LDS store: its generic tracking would otherwise wait for the next
 // tile's prefetch before every read of the current tile. Completion is ordered explicitly:
 // s_waitcnt vmcnt and a barrier before a stage is read. The LDS base travels in M0, which the
-// asm takes as an input operand so that the compiler knows the register is written.
+// asm takes as an input operand so that the compiler knows the register is written. The compiler
+// does not see the memory instruction inside the asm either, so it does not insert the five wait
+// states that a vector memory read of an SGPR needs after a VALU instruction (such as the
+// v_readfirstlane below) wrote it: the asm carries them itself (s_nop 4). Without them a schedule
+// that puts the readfirstlane right before the load reads a stale base address.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
     // the tile base is wave-uniform: pin it to SGPRs (readfirstlane returns int, so each word is
     // widened through uint32_t and the low word is not sign-extended)
     const uint64_t p = (uint64_t)(uintptr_t)sbase;
     const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32) |
                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-    asm volatile("global_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                  : : "v"(voff), "s"((const void*)(uintptr_t)u), "{m0}"(lds_wave_base) : "memory");
 }
 
@@ -49,7 +53,7 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
     const uint64_t p = (uint64_t)(uintptr_t)sbase;
     const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) << 32) |
                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-    asm volatile("global_load_lds_dword %0, %1"
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1"
                  : : "v"(voff), "s"((const void*)(uintptr_t)u), "{m0}"(lds_wave_base) : "memory");
 }
 
