@@ -22,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -74,26 +75,94 @@ def load_traffic(name, files):
     return t.get("hbm_bytes_per_launch")
 
 
-def time_launches(fn, reps, torch):
-    """Average device time per call of fn, from events around each call on the current stream."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+def warm_until_stable(fn, floor, torch, min_s=0.5, max_s=5.0, batch=20, tol=0.02):
+    """Launch fn at least `floor` times, then in batches of `batch` until at least `min_s` seconds
+    have passed and two consecutive batches agree within `tol` (or `max_s` passed), so that the
+    timed launches that follow run on a GPU at its steady clock. Returns the launch count."""
+    for _ in range(floor):
+        fn()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    prev, n = None, floor
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(batch):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        n += batch
+        avg = e0.elapsed_time(e1) / batch
+        elapsed = time.perf_counter() - t_start
+        if elapsed >= max_s or (elapsed >= min_s and prev is not None and abs(avg - prev) <= tol * prev):
+            return n
+        prev = avg
+
+
+def time_launches(fn, torch, samples=50, per=1):
+    """Device time per call of fn on the current stream: `samples` samples, each the mean of `per`
+    back-to-back calls between two HIP events (so the events' own cost is spread over `per`
+    calls). Returns the mean, median and min over the samples, in ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
     for a, b in evs:
         a.record()
-        fn()
+        for _ in range(per):
+            fn()
         b.record()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return sum(ms) / len(ms), min(ms)
+    ms = sorted(a.elapsed_time(b) / per for a, b in evs)
+    return {"mean": statistics.fmean(ms), "median": statistics.median(ms), "min": ms[0]}
+
+
+def measure(fn, torch, samples=50, target_ms=2.0, floor=3, min_s=0.2):
+    """Warm fn up until its time is steady, then time it with `per` chosen so a sample lasts about
+    target_ms."""
+    warm_until_stable(fn, floor, torch, min_s=min_s, max_s=3.0, batch=4)
+    t = time_launches(fn, torch, samples=3, per=1)
+    per = max(1, min(50, int(round(target_ms / max(t["median"], 1e-3)))))
+    r = time_launches(fn, torch, samples=samples, per=per)
+    r["per"] = per
+    r["samples"] = samples
+    return r
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def head_major_f64(t):
+    """A [B, N, H, dim] tensor as a float64 host array of the same shape whose (b, :, h) slices are
+    contiguous, so the oracle reads each head without a copy (layout only; no arithmetic)."""
+    import torch
+    return t.permute(0, 2, 1, 3).contiguous().to(torch.float64).cpu().numpy().transpose(0, 2, 1, 3)
+
+
+def sample_rows(n, rng, extra=48):
+    """Row sample of a causal prefill: the last row (it sees every key), the rows at 32-, 64- and
+    128-row tile boundaries near the start and the middle, and `extra` seeded random rows."""
+    fixed = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, n // 2 - 1, n // 2, n - 2, n - 1}
+    rows = sorted(r for r in fixed if 0 <= r < n)
+    rows += sorted(int(x) for x in rng.choice(n, size=extra, replace=False))
+    return rows
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="minimum warm-up launches; warm-up then continues until the launch time is steady")
     ap.add_argument("--secondary", default="32k,decode,v2,v2decode,bwd,v2bwd,fp8",
                     help="comma list of extra workloads to time (32k, decode, v2, v2decode, bwd, v2bwd, fp8) or 'none'")
-    ap.add_argument("--secondary-reps", type=int, default=10)
+    ap.add_argument("--secondary-samples", type=int, default=50,
+                    help="timing samples per secondary workload (median and min reported)")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the fp64 oracle on a sample (1) or not (0)")
     ap.add_argument("--copy-calibration", type=int, default=1,
                     help="run a 1 GiB device copy (reference kernel for HBM counter calibration)")
@@ -133,9 +202,10 @@ def main():
     def fwd_step():
         da._check(L.diffattn_fwd_lambda(*step_args))
 
-    for _ in range(args.warmup):
-        fwd_step()
-    torch.cuda.synchronize()
+    # warm-up: at least --warmup launches, then until the launch time is steady (two 20-launch
+    # batches within 2 %, at least 0.5 s), so the timed steps do not run on a cold GPU
+    n_warm = warm_until_stable(fwd_step, args.warmup, torch)
+    log(f"[bench] warm-up: {n_warm} launches")
 
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -145,28 +215,14 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # per-step events, in a separate untimed pass (event records on the stream cost time)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
-        a.record()
-        fwd_step()
-        b.record()
-    torch.cuda.synchronize()
-    fwd_ms = [a.elapsed_time(b) for a, b in evs]
-    # the fused kernel alone: the same number of launches back to back between two events on its
-    # stream, so per-event overhead is spread over the batch
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        fwd_step()
-    e1.record()
-    torch.cuda.synchronize()
-    fwd_avg_ms = e0.elapsed_time(e1) / args.steps
+    # the fused kernel alone, after the timed steps: 50 samples of 10 back-to-back launches, each
+    # sample between two HIP events on the launch stream; median and min over the samples
+    kt = time_launches(fwd_step, torch, samples=50, per=10)
     flops = FLOP_PER_PAIR_V1 * cfg.B * cfg.H * causal_pairs(cfg.N)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (fwd_avg_ms * 1e-3) / 1e12
-    log(f"[bench] step {ms_per_step * 1e3:.1f} us, fused forward kernel {fwd_avg_ms * 1e3:.1f} us "
-        f"(min {min(fwd_ms) * 1e3:.1f}) -> {achieved:.1f} TFLOP/s")
+    achieved = flops / (kt["median"] * 1e-3) / 1e12
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us; fused forward kernel median {kt['median'] * 1e3:.1f} us, "
+        f"min {kt['min'] * 1e3:.1f} us, mean {kt['mean'] * 1e3:.1f} us -> {achieved:.1f} TFLOP/s")
     traffic = load_traffic("v1_prefill_2k", ["fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"])
 
     result = {
@@ -191,10 +247,12 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "fwd_mfma_kernel<64,V1,causal,epilogue,lambda in-kernel>",
-                     "kernel_avg_us": round(fwd_avg_ms * 1e3, 2),
-                     "kernel_timing": f"{args.steps} back-to-back launches between two HIP events on the launch "
-                                      "stream, after the timed steps",
-                     "kernel_avg_us_step_events": round(sum(fwd_ms) / len(fwd_ms) * 1e3, 2)},
+                     "kernel_median_us": round(kt["median"] * 1e3, 2),
+                     "kernel_min_us": round(kt["min"] * 1e3, 2),
+                     "kernel_avg_us": round(kt["mean"] * 1e3, 2),
+                     "kernel_timing": "50 samples, each 10 back-to-back launches between two HIP events on "
+                                      "the launch stream, after the timed steps; achieved = flop / median",
+                     "warmup_launches": n_warm},
     }
     del x
 
@@ -211,10 +269,11 @@ def main():
                                      epilogue=True, lambda_init_value=da.lambda_init(c3.layer), out=o3)
         f3()
         torch.cuda.synchronize()
-        avg, mn = time_launches(f3, args.secondary_reps, torch)
+        _r = measure(f3, torch, samples=args.secondary_samples)
+        avg, mn = _r["median"], _r["min"]
         fl3 = FLOP_PER_PAIR_V1 * c3.B * c3.H * causal_pairs(c3.N)
         tf = fl3 / (avg * 1e-3) / 1e12
-        secondary["v1_prefill_32k"] = {"workload": c3.name, "kernel_avg_ms": round(avg, 4),
+        secondary["v1_prefill_32k"] = {"workload": c3.name, "kernel_median_ms": round(avg, 4),
                                        "kernel_min_ms": round(mn, 4), "flop": fl3, "TFLOP/s": round(tf, 2),
                                        "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s")
@@ -227,10 +286,11 @@ def main():
         f5 = lambda: da.diffattn_v2_fwd(x5["q"], x5["k"], x5["v"], x5["lam"], causal=True, out=o5)
         f5()
         torch.cuda.synchronize()
-        avg, mn = time_launches(f5, args.secondary_reps, torch)
+        _r = measure(f5, torch, samples=args.secondary_samples)
+        avg, mn = _r["median"], _r["min"]
         fl5 = FLOP_PER_PAIR_V2 * c5.B * c5.hq * causal_pairs(c5.N)
         tf = fl5 / (avg * 1e-3) / 1e12
-        secondary["v2_gqa_8k"] = {"workload": c5.name, "kernel_avg_ms": round(avg, 4), "kernel_min_ms": round(mn, 4),
+        secondary["v2_gqa_8k"] = {"workload": c5.name, "kernel_median_ms": round(avg, 4), "kernel_min_ms": round(mn, 4),
                                   "flop": fl5, "TFLOP/s": round(tf, 2),
                                   "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                                   "traffic": load_traffic("v2_gqa_8k", ["fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"])}
@@ -240,9 +300,10 @@ def main():
         fz = lambda: da.diffattn_v2_fwd(x5["q"], x5["k"], x5["v"], z5, causal=True, out=o5, lam_logits=True)
         fz()
         torch.cuda.synchronize()
-        avg, mn = time_launches(fz, args.secondary_reps, torch)
+        _r = measure(fz, torch, samples=args.secondary_samples)
+        avg, mn = _r["median"], _r["min"]
         tf = fl5 / (avg * 1e-3) / 1e12
-        secondary["v2_gqa_8k"]["lam_logits_kernel_avg_ms"] = round(avg, 4)
+        secondary["v2_gqa_8k"]["lam_logits_kernel_median_ms"] = round(avg, 4)
         secondary["v2_gqa_8k"]["lam_logits_TFLOP/s"] = round(tf, 2)
         log(f"[bench]   lambda logits: {avg:.3f} ms -> {tf:.1f} TFLOP/s")
         del x5, o5, z5
@@ -257,10 +318,11 @@ def main():
                                         lambda_init_value=c4.lambda_init, workspace=ws, out=o4)
         f4()
         torch.cuda.synchronize()
-        avg, mn = time_launches(f4, args.secondary_reps, torch)
+        _r = measure(f4, torch, samples=args.secondary_samples)
+        avg, mn = _r["median"], _r["min"]
         nbytes = DECODE_BYTES_PER_TOKEN * c4.B * c4.H * c4.L
         gbs = nbytes / (avg * 1e-3) / 1e9
-        secondary["v1_decode_64k"] = {"workload": c4.name, "split_plus_reduce_avg_ms": round(avg, 4),
+        secondary["v1_decode_64k"] = {"workload": c4.name, "split_plus_reduce_median_ms": round(avg, 4),
                                       "min_ms": round(mn, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
                                       "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                                       "traffic": load_traffic("v1_decode_64k", ["decode.hip", "common.hpp"])}
@@ -272,10 +334,11 @@ def main():
                                               epilogue=True, lambda_init_value=c4.lambda_init, workspace=ws, out=o4)
         fp()
         torch.cuda.synchronize()
-        avg, mn = time_launches(fp, args.secondary_reps, torch)
+        _r = measure(fp, torch, samples=args.secondary_samples)
+        avg, mn = _r["median"], _r["min"]
         gbs = nbytes / (avg * 1e-3) / 1e9
         secondary["v1_decode_64k_paged"] = {"workload": c4.name + f", {PAGE_SIZE}-token pages",
-                                            "split_plus_reduce_avg_ms": round(avg, 4), "min_ms": round(mn, 4),
+                                            "split_plus_reduce_median_ms": round(avg, 4), "min_ms": round(mn, 4),
                                             "bytes": nbytes, "GB/s": round(gbs, 1),
                                             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"[bench]   paged: {avg:.3f} ms -> {gbs:.0f} GB/s")
@@ -297,12 +360,14 @@ def main():
                                      lambda_init_value=li7, workspace=ws7)
         fb()
         torch.cuda.synchronize()
-        avg_f, mn_f = time_launches(ft, args.secondary_reps, torch)
-        avg_b, mn_b = time_launches(fb, args.secondary_reps, torch)
+        _r = measure(ft, torch, samples=args.secondary_samples)
+        avg_f, mn_f = _r["median"], _r["min"]
+        _r = measure(fb, torch, samples=args.secondary_samples)
+        avg_b, mn_b = _r["median"], _r["min"]
         pairs7 = c7.B * c7.H * causal_pairs(c7.N)
         fl_b = FLOP_PER_PAIR_V1_BWD * pairs7
-        secondary["v1_backward_2k"] = {"workload": c7.name, "train_forward_avg_ms": round(avg_f, 4),
-                                       "backward_avg_ms": round(avg_b, 4), "backward_min_ms": round(mn_b, 4),
+        secondary["v1_backward_2k"] = {"workload": c7.name, "train_forward_median_ms": round(avg_f, 4),
+                                       "backward_median_ms": round(avg_b, 4), "backward_min_ms": round(mn_b, 4),
                                        "flop": fl_b, "flop_per_visible_pair": FLOP_PER_PAIR_V1_BWD,
                                        "TFLOP/s": round(fl_b / (avg_b * 1e-3) / 1e12, 2),
                                        "frac_of_bf16_peak": round(fl_b / (avg_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -324,14 +389,16 @@ def main():
         fq9()
         ff9()
         torch.cuda.synchronize()
-        avg_q, _ = time_launches(fq9, args.secondary_reps, torch)
-        avg, mn = time_launches(ff9, args.secondary_reps, torch)
+        _r = measure(fq9, torch, samples=args.secondary_samples)
+        avg_q, _ = _r["median"], _r["min"]
+        _r = measure(ff9, torch, samples=args.secondary_samples)
+        avg, mn = _r["median"], _r["min"]
         fl9 = FLOP_PER_PAIR_V1 * c9.B * c9.H * causal_pairs(c9.N)
         tf = fl9 / (avg * 1e-3) / 1e12
         secondary["v1_prefill_2k_fp8_logits"] = {
-            "workload": c9.name + ", Q1 Q2 K1 K2 in fp8 e4m3", "kernel_avg_ms": round(avg, 4),
+            "workload": c9.name + ", Q1 Q2 K1 K2 in fp8 e4m3", "kernel_median_ms": round(avg, 4),
             "kernel_min_ms": round(mn, 4), "flop": fl9, "TFLOP/s": round(tf, 2),
-            "quantize_four_operands_avg_ms": round(avg_q, 4)}
+            "quantize_four_operands_median_ms": round(avg_q, 4)}
         log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s (quantising Q1, Q2, K1, K2: {avg_q:.3f} ms)")
         del x9, o9, qs9
     if "v2bwd" in which:
@@ -348,11 +415,13 @@ def main():
                                          workspace=ws8)
         fb8()
         torch.cuda.synchronize()
-        avg_f, _ = time_launches(ft8, args.secondary_reps, torch)
-        avg_b, mn_b = time_launches(fb8, args.secondary_reps, torch)
+        _r = measure(ft8, torch, samples=args.secondary_samples)
+        avg_f, _ = _r["median"], _r["min"]
+        _r = measure(fb8, torch, samples=args.secondary_samples)
+        avg_b, mn_b = _r["median"], _r["min"]
         fl8 = FLOP_PER_PAIR_V2_BWD * c8.B * c8.hq * causal_pairs(c8.N)
-        secondary["v2_backward_8k"] = {"workload": c8.name, "train_forward_avg_ms": round(avg_f, 4),
-                                       "backward_avg_ms": round(avg_b, 4), "backward_min_ms": round(mn_b, 4),
+        secondary["v2_backward_8k"] = {"workload": c8.name, "train_forward_median_ms": round(avg_f, 4),
+                                       "backward_median_ms": round(avg_b, 4), "backward_min_ms": round(mn_b, 4),
                                        "flop": fl8, "flop_per_visible_pair_and_query_head": FLOP_PER_PAIR_V2_BWD,
                                        "TFLOP/s": round(fl8 / (avg_b * 1e-3) / 1e12, 2),
                                        "frac_of_bf16_peak": round(fl8 / (avg_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
@@ -370,10 +439,11 @@ def main():
         f6 = lambda: da.diffattn_v2_decode(x6["q"], x6["k"], x6["v"], lam6, workspace=ws6, out=o6)
         f6()
         torch.cuda.synchronize()
-        avg, mn = time_launches(f6, args.secondary_reps, torch)
+        _r = measure(f6, torch, samples=args.secondary_samples)
+        avg, mn = _r["median"], _r["min"]
         nbytes = 2 * c6.d * 2 * c6.B * c6.hkv * c6.L     # K and V rows read once per KV head
         gbs = nbytes / (avg * 1e-3) / 1e9
-        secondary["v2_decode_64k"] = {"workload": c6.name, "split_plus_reduce_avg_ms": round(avg, 4),
+        secondary["v2_decode_64k"] = {"workload": c6.name, "split_plus_reduce_median_ms": round(avg, 4),
                                       "min_ms": round(mn, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
                                       "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                                       "traffic": load_traffic("v2_decode_64k", ["decode_v2.hip", "mfma_tile.hpp",
@@ -385,10 +455,11 @@ def main():
                                                   out=o6)
         fp6()
         torch.cuda.synchronize()
-        avg, mn = time_launches(fp6, args.secondary_reps, torch)
+        _r = measure(fp6, torch, samples=args.secondary_samples)
+        avg, mn = _r["median"], _r["min"]
         gbs = nbytes / (avg * 1e-3) / 1e9
         secondary["v2_decode_64k_paged"] = {"workload": c6.name + f", {PAGE_SIZE}-token pages",
-                                            "split_plus_reduce_avg_ms": round(avg, 4), "min_ms": round(mn, 4),
+                                            "split_plus_reduce_median_ms": round(avg, 4), "min_ms": round(mn, 4),
                                             "bytes": nbytes, "GB/s": round(gbs, 1),
                                             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"[bench]   paged: {avg:.3f} ms -> {gbs:.0f} GB/s")
@@ -404,11 +475,11 @@ def main():
         torch.cuda.synchronize()
         # measured peaks beside the published ones: the copy's rate (bytes read + written) and
         # the dense bf16 MFMA probe of the library
-        avg_c, _ = time_launches(lambda: dst.copy_(src), 10, torch)
+        avg_c = time_launches(lambda: dst.copy_(src), torch, samples=10)["median"]
         copy_gbs = 2 * (1 << 30) / (avg_c * 1e-3) / 1e9
         del src, dst
         probe_out, probe_flop = da.diffattn_probe_mfma_peak(4096, 2000, device=dev)
-        avg_p, _ = time_launches(lambda: da.diffattn_probe_mfma_peak(4096, 2000, device=dev), 5, torch)
+        avg_p = time_launches(lambda: da.diffattn_probe_mfma_peak(4096, 2000, device=dev), torch, samples=5)["median"]
         mfma_tflops = probe_flop / (avg_p * 1e-3) / 1e12
         result["measured_peaks"] = {
             "hbm_torch_copy_GB/s": round(copy_gbs, 1), "mfma_bf16_TFLOP/s": round(mfma_tflops, 1),
@@ -423,7 +494,7 @@ def main():
     if args.cpu_baseline:
         import oracle
         x = W.v1_inputs(cfg, device="cpu")
-        host = {k: x[k].float().numpy() for k in ("q1", "q2", "k1", "k2", "v")}
+        host = {k: head_major_f64(x[k]) for k in ("q1", "q2", "k1", "k2", "v")}
         lam_ref = oracle.lam(*(x[k].double().numpy() for k in ("lq1", "lk1", "lq2", "lk2")), cfg.layer)
         units_done, t_cpu, pairs = 0, 0.0, 0
         for b in range(cfg.B):
@@ -441,13 +512,55 @@ def main():
             if t_cpu > 20.0:
                 break
         cpu_tf = FLOP_PER_PAIR_V1 * pairs / t_cpu / 1e12
-        result["cpu_baseline"] = {"value": round(cpu_tf, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-                                  "kind": "oracle",
+        del x, host
+        cores = oracle.num_threads()
+        result["cpu_baseline"] = {"value": round(cpu_tf, 6), "unit": "TFLOP/s", "cores": cores,
+                                  "kind": "oracle", "cpu_model": cpu_model(),
                                   "sample": f"{units_done} of {cfg.B * cfg.H} (batch, head) units of the main "
                                             f"workload, every row ({pairs} visible pairs), fp64, "
                                             f"{t_cpu:.1f} s (capped at 20 s)"}
         log(f"[bench] oracle: {units_done} units in {t_cpu:.1f} s -> {cpu_tf * 1e3:.3f} GFLOP/s "
-            f"on {oracle.num_threads()} threads")
+            f"on {cores} threads ({cpu_model()})")
+        # the long-context and V2 workloads: a seeded row sample per head (or pair), timed, and the
+        # full-size oracle time extrapolated linearly in visible pairs (labelled as such)
+        others = {}
+        rng = np.random.default_rng(12345)
+        c3 = W.V1_PREFILL_32K
+        x3 = W.v1_inputs(c3, device=dev)          # the inputs the GPU leg timed, copied to the host
+        h3 = {k: head_major_f64(x3[k]) for k in ("q1", "q2", "k1", "k2", "v")}
+        lam3 = oracle.lam(*(x3[k].double().numpy() for k in ("lq1", "lk1", "lq2", "lk2")), c3.layer)
+        rows3 = sample_rows(c3.N, rng)
+        sel = np.array([(0, h, i) for h in range(c3.H) for i in rows3])
+        s = time.perf_counter()
+        oracle.v1_forward(h3["q1"], h3["q2"], h3["k1"], h3["k2"], h3["v"], lam3, causal=True, epilogue=True,
+                          lambda_init_value=oracle.lambda_init(c3.layer), rows=sel)
+        t3 = time.perf_counter() - s
+        p3 = c3.H * sum(i + 1 for i in rows3)
+        full3 = c3.B * c3.H * causal_pairs(c3.N)
+        others["v1_prefill_32k"] = {"workload": c3.name, "sample": f"{len(rows3)} rows per head x {c3.H} heads "
+                                    f"(last row, tile-boundary rows, 48 seeded random rows; {p3} visible pairs)",
+                                    "sample_s": round(t3, 3), "TFLOP/s": round(FLOP_PER_PAIR_V1 * p3 / t3 / 1e12, 6),
+                                    "full_size_s_extrapolated": round(t3 * full3 / p3, 1)}
+        del x3, h3
+        c5 = W.V2_GQA_8K
+        x5 = W.v2_inputs(c5, device=dev)
+        h5 = {k: head_major_f64(x5[k]) for k in ("q", "k", "v")}
+        rows5 = sample_rows(c5.N, rng)
+        sel = np.array([(b, p, i) for b in range(c5.B) for p in range(c5.hq // 2) for i in rows5])
+        s = time.perf_counter()
+        oracle.v2_forward(h5["q"], h5["k"], h5["v"], x5["lam"].double().cpu().numpy(), causal=True, rows=sel)
+        t5 = time.perf_counter() - s
+        p5 = c5.B * (c5.hq // 2) * sum(i + 1 for i in rows5)       # visible pairs per pair of query heads
+        full5 = c5.B * (c5.hq // 2) * causal_pairs(c5.N)
+        others["v2_gqa_8k"] = {"workload": c5.name, "sample": f"{len(rows5)} rows per (batch, pair) x "
+                               f"{c5.B * c5.hq // 2} (both query heads of each pair; {p5} visible pairs)",
+                               "sample_s": round(t5, 3),
+                               "TFLOP/s": round(2 * FLOP_PER_PAIR_V2 * p5 / t5 / 1e12, 6),
+                               "full_size_s_extrapolated": round(t5 * full5 / p5, 1)}
+        del x5, h5
+        result["cpu_baseline"]["other_workloads"] = others
+        log(f"[bench] oracle samples: 32K {t3:.2f} s (full size ~{t3 * full3 / p3:.0f} s extrapolated), "
+            f"V2 8K {t5:.2f} s (~{t5 * full5 / p5:.0f} s)")
 
     print(json.dumps(result), flush=True)
 
