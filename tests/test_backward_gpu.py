@@ -7,11 +7,10 @@ import torch
 import differential_softmax_attention_amd as da
 import oracle
 import workloads as W
+from tolerances import grad_excess
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-TOL_REL = 2e-2    # bf16 gradients: max error within 2% of the tensor's largest reference value,
-TOL_ABS = 1e-4    # plus bf16 rounding noise where the exact gradient is 0 (a single visible key)
 
 
 def note(msg):
@@ -27,11 +26,11 @@ def f64(x):
     return x.double().cpu().numpy() if isinstance(x, torch.Tensor) else x
 
 
-def relerr(got, ref):
-    """max |got - ref| beyond the absolute floor, relative to the tensor's largest reference value"""
-    got, ref = f64(got), np.asarray(ref)
-    err = max(float(np.max(np.abs(got - ref))) - TOL_ABS, 0.0)
-    return err / max(float(np.max(np.abs(ref))), 1e-30)
+
+def close(got, ref, name):
+    e = grad_excess(got, ref)
+    note(f"{name}: worst error / bound = {e:.3f}")
+    assert e <= 1.0, (name, e)
 
 
 def case(B, Nq, Nk, H, seed, causal=True, epilogue=True, norm=False, qscale=1.0):
@@ -79,24 +78,24 @@ def test_train_stats(N, causal):
 def test_bwd_causal_epilogue(N):
     out, lse, maps, g, ref = run(case(2, N, N, 2, 3100 + N, causal=True, epilogue=True, norm=True))
     for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
-        assert relerr(g[k], ref[k]) <= TOL_REL, k
-    assert relerr(g["dlam"], ref["dlam"]) <= TOL_REL
-    assert relerr(g["dnorm_w"], ref["dg"]) <= TOL_REL
+        close(g[k], ref[k], k)
+    close(g["dlam"], ref["dlam"], "dlam")
+    close(g["dnorm_w"], ref["dg"], "dnorm_w")
 
 
 @pytest.mark.parametrize("Nq,Nk,causal", [(64, 64, False), (70, 130, True), (40, 200, False), (300, 260, False), (200, 330, True)])
 def test_bwd_noepi_and_rect(Nq, Nk, causal):
     out, lse, maps, g, ref = run(case(1, Nq, Nk, 3, 3200 + Nq + Nk, causal=causal, epilogue=False))
     for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
-        assert relerr(g[k], ref[k]) <= TOL_REL, k
-    assert relerr(g["dlam"], ref["dlam"]) <= TOL_REL
+        close(g[k], ref[k], k)
+    close(g["dlam"], ref["dlam"], "dlam")
     assert g["dnorm_w"] is None
 
 
 def test_bwd_large_logits():
     out, lse, maps, g, ref = run(case(1, 160, 160, 2, 3300, causal=True, epilogue=True, qscale=6.0))
     for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
-        assert relerr(g[k], ref[k]) <= TOL_REL, k
+        close(g[k], ref[k], k)
 
 
 def test_bwd_deterministic():
@@ -137,5 +136,5 @@ def test_full_v1_prefill_2k_backward_sampled():
     ref = oracle.v1_backward(*(f64(t) for t in (q1, q2, k1, k2, v)), lam.cpu().numpy(), f64(dy), causal=True,
                              epilogue=True, lambda_init_value=li)
     for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
-        assert relerr(g[k], ref[k]) <= TOL_REL, k
-    assert relerr(g["dlam"], ref["dlam"]) <= TOL_REL
+        close(g[k], ref[k], k)
+    close(g["dlam"], ref["dlam"], "dlam")

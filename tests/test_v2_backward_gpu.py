@@ -7,11 +7,10 @@ import torch
 import differential_softmax_attention_amd as da
 import oracle
 import workloads as W
+from tolerances import grad_excess
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-TOL_REL = 2e-2    # bf16 gradients: max error within 2% of the tensor's largest reference value,
-TOL_ABS = 1e-4    # plus bf16 rounding noise where the exact gradient is 0
 
 
 def note(msg):
@@ -26,11 +25,6 @@ def rand(shape, seed, scale=1.0):
 def f64(x):
     return x.double().cpu().numpy() if isinstance(x, torch.Tensor) else x
 
-
-def relerr(got, ref):
-    got, ref = f64(got), np.asarray(ref)
-    err = max(float(np.max(np.abs(got - ref))) - TOL_ABS, 0.0)
-    return err / max(float(np.max(np.abs(ref))), 1e-30)
 
 
 def case(B, N, hq, hkv, seed, causal=True, logits=False, qscale=1.0):
@@ -59,8 +53,9 @@ def run(c):
 
 def check(g, ref):
     for k in ("dq", "dk", "dv", "dlam"):
-        e = relerr(g[k], ref[k])
-        assert e <= TOL_REL, (k, e)
+        e = grad_excess(g[k], ref[k])
+        note(f"{k}: worst error / bound = {e:.3f}")
+        assert e <= 1.0, (k, e)
 
 
 @pytest.mark.parametrize("N,causal", [(1, True), (31, True), (33, False), (200, True)])
@@ -141,15 +136,27 @@ def test_full_v2_bwd_8k_sampled():
     ref = oracle.v2_backward(f64(x["q"][b:b + 1, :M, 2 * p:2 * p + 2]), f64(x["k"][b:b + 1, :M, gk:gk + 1]),
                              f64(x["v"][b:b + 1, :M, gk:gk + 1]), lam[b:b + 1, :M, p:p + 1].cpu().numpy(),
                              f64(dy[b:b + 1, :M, p:p + 1]), causal=True)
-    assert relerr(g["dq"][b:b + 1, :M, 2 * p:2 * p + 2], ref["dq"]) <= TOL_REL
-    assert relerr(g["dlam"][b:b + 1, :M, p:p + 1], ref["dlam"]) <= TOL_REL
+    e = grad_excess(g["dq"][b:b + 1, :M, 2 * p:2 * p + 2], ref["dq"])
+    note(f"worst error / bound = {e:.3f}")
+    assert e <= 1.0
+    e = grad_excess(g["dlam"][b:b + 1, :M, p:p + 1], ref["dlam"])
+    note(f"worst error / bound = {e:.3f}")
+    assert e <= 1.0
     M = 64
     b, gk = cfg.B - 1, cfg.hkv - 1
     hs, ps = slice(gk * group, (gk + 1) * group), slice(gk * group // 2, (gk + 1) * group // 2)
     ref = oracle.v2_backward(f64(x["q"][b:b + 1, -M:, hs]), f64(x["k"][b:b + 1, :, gk:gk + 1]),
                              f64(x["v"][b:b + 1, :, gk:gk + 1]), lam[b:b + 1, -M:, ps].cpu().numpy(),
                              f64(dy[b:b + 1, -M:, ps]), causal=True)
-    assert relerr(g["dq"][b:b + 1, -M:, hs], ref["dq"]) <= TOL_REL
-    assert relerr(g["dlam"][b:b + 1, -M:, ps], ref["dlam"]) <= TOL_REL
-    assert relerr(g["dk"][b:b + 1, -M:, gk:gk + 1], ref["dk"][:, -M:]) <= TOL_REL
-    assert relerr(g["dv"][b:b + 1, -M:, gk:gk + 1], ref["dv"][:, -M:]) <= TOL_REL
+    e = grad_excess(g["dq"][b:b + 1, -M:, hs], ref["dq"])
+    note(f"worst error / bound = {e:.3f}")
+    assert e <= 1.0
+    e = grad_excess(g["dlam"][b:b + 1, -M:, ps], ref["dlam"])
+    note(f"worst error / bound = {e:.3f}")
+    assert e <= 1.0
+    e = grad_excess(g["dk"][b:b + 1, -M:, gk:gk + 1], ref["dk"][:, -M:])
+    note(f"worst error / bound = {e:.3f}")
+    assert e <= 1.0
+    e = grad_excess(g["dv"][b:b + 1, -M:, gk:gk + 1], ref["dv"][:, -M:])
+    note(f"worst error / bound = {e:.3f}")
+    assert e <= 1.0
