@@ -67,6 +67,16 @@ __device__ __forceinline__ void agpr_drain(f32x16& x0, f32x16& x1, f32x16& x2, f
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3));
 }
 
+// The end of a loop iteration whose asm MFMAs accumulate into these eight tiles: the compiler may
+// copy or move accumulators at the top of the next iteration (out of sight of the asm, so with no
+// wait states of its own), so the iteration ends with the 18 wait states an MFMA result needs
+// before any other instruction touches it (8 + 8 + 4 here).
+__device__ __forceinline__ void agpr_fence(f32x16& x0, f32x16& x1, f32x16& x2, f32x16& x3, f32x16& x4, f32x16& x5,
+                                           f32x16& x6, f32x16& x7) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "+a"(x4), "+a"(x5), "+a"(x6), "+a"(x7));
+}
+
 template <int V> struct IC { static constexpr int value = V; };
 
 // f(IC<0>), f(IC<1>), ..., f(IC<N - 1>): a loop whose index is a compile-time constant

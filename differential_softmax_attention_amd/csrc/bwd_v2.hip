@@ -602,17 +602,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // outstanding loads of its own and adds no waits on the query-tile DMA
     __builtin_amdgcn_s_waitcnt(kVmcnt[0]);
     int it = 0;
+    auto fence = [&]() __attribute__((always_inline)) { agpr_fence(dk[0], dk[1], dk[2], dk[3], dv[0], dv[1], dv[2], dv[3]); };
     for (; it < is; it += 4) {
         pair(std::false_type{}, it, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
         if (it + 2 < nit) pair(std::false_type{}, it + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
+        fence();
     }
     for (; it < ie; it += 4) {
         pair(std::true_type{}, it, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
         pair(std::true_type{}, it + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
+        fence();
     }
     for (; it < nit; it += 4) {
         pair(std::false_type{}, it, IC<0>{}, IC<1>{}, IC<2>{}, IC<3>{});
         if (it + 2 < nit) pair(std::false_type{}, it + 2, IC<2>{}, IC<3>{}, IC<0>{}, IC<1>{});
+        fence();
     }
     agpr_drain(dk[0], dk[1], dk[2], dk[3]);
     agpr_drain(dv[0], dv[1], dv[2], dv[3]);

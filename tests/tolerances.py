@@ -20,19 +20,21 @@ Gradients (the backward passes), element by element:
   these terms cancel, and an element can be far smaller than its terms. A bound relative to
   |ref| alone would fail on such elements; a bound relative to the tensor's largest value would
   hardly test the small ones. The typical size of the terms of an element is the tensor's RMS
-  scale. With per-element errors of standard deviation about 2u times that scale, the largest
-  of 10^4 - 10^5 elements lies about 4.5 standard deviations out, 4.5 * 2u = 1.8e-2 of the RMS
-  (measured on MI355X: up to 2.0e-2 over the backward tests). So each element may deviate by
-  GRAD_ATOL_RMS = 3e-2 of the tensor's RMS plus GRAD_RTOL = 2e-2 of its own magnitude, and by
-  GRAD_ATOL = 1e-4 where the exact gradient is identically zero (a row with one visible key: its
-  softmax has zero gradient, and the kernel's dP - D is then pure rounding noise).
+  scale. Measured on MI355X over the backward tests: the RMS of the error is 0.3-0.4% of the
+  tensor's RMS (about 2u, as the analysis says), but not evenly spread: the first keys and the
+  first query rows of a causal map, where short rows give the largest weights and so the largest
+  terms, carry about three times that, and their worst elements reach 3.6% of the RMS. So each
+  element may deviate by GRAD_ATOL_RMS = 5e-2 of the tensor's RMS plus GRAD_RTOL = 2e-2 of its
+  own magnitude, and by GRAD_ATOL = 1e-4 where the exact gradient is identically zero (a row with
+  one visible key: its softmax has zero gradient, and the kernel's dP - D is then pure rounding
+  noise).
 """
 import numpy as np
 
 FWD_F32_ABS = 1e-5
 FWD_BF16_ABS = 2e-2
 GRAD_RTOL = 2e-2
-GRAD_ATOL_RMS = 3e-2
+GRAD_ATOL_RMS = 5e-2
 GRAD_ATOL = 1e-4
 
 
