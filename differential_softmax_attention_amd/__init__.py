@@ -38,7 +38,9 @@ EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "
             "diffattn_v2_decode_workspace_size", "diffattn_v2_decode", "diffattn_fwd_train",
             "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd", "diffattn_decode_paged",
             "diffattn_v2_decode_paged", "diffattn_v2_fwd_train", "diffattn_v2_bwd_workspace_size", "diffattn_v2_bwd",
-            "diffattn_quantize_fp8", "diffattn_fwd_fp8", "diffattn_fwd_lambda", "diffattn_probe_mfma_peak")
+            "diffattn_quantize_fp8", "diffattn_fwd_fp8", "diffattn_fwd_lambda", "diffattn_probe_mfma_peak",
+            "diffattn_decode_noalloc")
+DECODE_NOALLOC_MAX_BYTES = 32 << 20
 
 
 class DiffAttnError(RuntimeError):
@@ -95,6 +97,8 @@ def lib():
         L.diffattn_v2_decode.restype = i
         L.diffattn_v2_decode.argtypes = [i, T, T, T, vp, vp, i, i, i, i, i, i, f, T, vp, sz, vp]
         i64 = ctypes.c_int64
+        L.diffattn_decode_noalloc.restype = i
+        L.diffattn_decode_noalloc.argtypes = [i, T, T, T, T, T, vp, i, i, i, i, i, vp, f, i, vp, f, f, T, vp]
         L.diffattn_decode_paged.restype = i
         L.diffattn_decode_paged.argtypes = [i, T, T, T, T, T, vp, i64, i, i, vp, i, i, i, i, i, vp, f, i, vp, f,
                                             f, T, vp, sz, vp]
@@ -283,12 +287,8 @@ def diffattn_decode_workspace_size(batch: int, heads: int, cache_len: int, dv: i
     return int(lib().diffattn_decode_workspace_size(batch, heads, cache_len, dv))
 
 
-def diffattn_decode(q1, q2, k1c, k2c, vc, lam: torch.Tensor, cache_lens: torch.Tensor | None = None,
-                    epilogue: bool = True, lambda_init_value: float = 0.8,
-                    norm_w: torch.Tensor | None = None, eps: float = 1e-5, scale: float = 0.0,
-                    workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
-    """DIFF V1 decode. q1, q2: [B, H, d] (or [B, 1, H, d]); caches [B, L, H, d|dv];
-    cache_lens: int32 [B] on the device or None. Returns [B, H, dv]."""
+def _decode_operands(q1, q2, k1c, k2c, vc, lam, cache_lens, norm_w, out):
+    """Shapes of a V1 decode call; returns (q1, q2, out) as 4-d views and (B, H, L, d, dv)."""
     if q1.dim() == 3:
         q1, q2 = q1.unsqueeze(1), q2.unsqueeze(1)
     if out is not None and out.dim() == 3:
@@ -307,6 +307,16 @@ def diffattn_decode(q1, q2, k1c, k2c, vc, lam: torch.Tensor, cache_lens: torch.T
     _flat("lam", lam, H, torch.float32, q1)
     _flat("norm_w", norm_w, dv, torch.float32, q1, optional=True)
     _flat("cache_lens", cache_lens, B, torch.int32, q1, optional=True)
+    return q1, q2, out, (B, H, L, d, dv)
+
+
+def diffattn_decode(q1, q2, k1c, k2c, vc, lam: torch.Tensor, cache_lens: torch.Tensor | None = None,
+                    epilogue: bool = True, lambda_init_value: float = 0.8,
+                    norm_w: torch.Tensor | None = None, eps: float = 1e-5, scale: float = 0.0,
+                    workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """DIFF V1 decode. q1, q2: [B, H, d] (or [B, 1, H, d]); caches [B, L, H, d|dv];
+    cache_lens: int32 [B] on the device or None. Returns [B, H, dv]."""
+    q1, q2, out, (B, H, L, d, dv) = _decode_operands(q1, q2, k1c, k2c, vc, lam, cache_lens, norm_w, out)
     _workspace(workspace, q1)
     if out is None:
         out = torch.empty((B, 1, H, dv), dtype=q1.dtype, device=q1.device)
@@ -320,6 +330,23 @@ def diffattn_decode(q1, q2, k1c, k2c, vc, lam: torch.Tensor, cache_lens: torch.T
                                  float(scale), _t4(out), _dp(workspace), workspace.numel(),
                                  _stream(q1.device)))
     return out.squeeze(1)
+
+
+def diffattn_decode_noalloc(q1, q2, k1c, k2c, vc, lam: torch.Tensor, out: torch.Tensor,
+                            cache_lens: torch.Tensor | None = None, epilogue: bool = True,
+                            lambda_init_value: float = 0.8, norm_w: torch.Tensor | None = None, eps: float = 1e-5,
+                            scale: float = 0.0) -> torch.Tensor:
+    """diffattn_decode with the library's own per-GPU scratch instead of a workspace: the library
+    allocates nothing, and neither does this binding (out is the caller's). Calls that overlap on
+    one GPU race on that scratch. Returns out viewed as [B, H, dv]."""
+    if out is None:
+        raise ValueError("out is required: diffattn_decode_noalloc allocates nothing")
+    q1, q2, out4, (B, H, L, d, dv) = _decode_operands(q1, q2, k1c, k2c, vc, lam, cache_lens, norm_w, out)
+    _check(lib().diffattn_decode_noalloc(_dtype_code(q1), _t4(q1), _t4(q2), _t4(k1c), _t4(k2c), _t4(vc),
+                                         _ptr(cache_lens), B, H, L, d, dv, _dp(lam), float(lambda_init_value),
+                                         EPI_RMSNORM_SCALE if epilogue else EPI_NONE, _ptr(norm_w), float(eps),
+                                         float(scale), _t4(out4), _stream(q1.device)))
+    return out4.squeeze(1)
 
 
 def diffattn_v2_fwd(q, k, v, lam: torch.Tensor, causal: bool = True, scale: float = 0.0,

@@ -16,6 +16,8 @@
 // rescaling), forms O1/l1 - lambda O2/l2 and applies the RMSNorm * w * (1 - lambda_init)
 // epilogue ("Noise-Canceling Attention by Subtraction", section "Making lambda learnable and
 // stable"). No atomics: the result is bitwise reproducible.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -267,6 +269,32 @@ size_t decode_workspace_bytes(int batch, int heads, int cache_len, int dv) {
     (void)dv;
     const int s = decode_num_splits(batch, heads, cache_len);
     return (size_t)batch * heads * s * kPartial * sizeof(float);
+}
+
+// ---- the workspace of the allocation-free entry point
+// The split partials of diffattn_decode_noalloc live in this file-scope array instead of a
+// caller's workspace: one copy per GPU the library runs on (the code object's device globals are
+// created when it is loaded on that GPU and live until the process ends), kNoallocScratchBytes in
+// all. Host code never uses the array's name as an address (on the host it is a stand-in
+// symbol): its device address is looked up once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+hipError_t decode_noalloc_scratch(int device, float** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float* ptrs[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[device]) {
+        // the caller has made `device` current: the lookup returns that device's copy
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptrs[device] = (float*)p;
+    }
+    *out = ptrs[device];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a0, hipStream_t stream) {

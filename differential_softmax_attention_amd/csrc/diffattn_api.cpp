@@ -204,8 +204,8 @@ static diffattn_status decode_impl(diffattn_dtype dtype, diffattn_tensor q1, dif
                                    int heads, int cache_len, int d, int dv, const float* lambda, float lambda_init,
                                    diffattn_epilogue epi, const float* norm_w, float eps, float scale,
                                    diffattn_tensor out, void* workspace, size_t workspace_bytes, void* stream,
-                                   const diffattn::PagedCache& pc) {
-    const char* fn_name = pc.block_table ? "diffattn_decode_paged" : "diffattn_decode";
+                                   const diffattn::PagedCache& pc, bool noalloc = false) {
+    const char* fn_name = pc.block_table ? "diffattn_decode_paged" : noalloc ? "diffattn_decode_noalloc" : "diffattn_decode";
     if (!valid_dtype(dtype)) return fail(DIFFATTN_ERR_ARG, "diffattn_decode: unknown dtype %d", (int)dtype);
     const diffattn_tensor* ts[6] = {&q1, &q2, &k1c, &k2c, &vc, &out};
     const char* names[6] = {"q1", "q2", "k1c", "k2c", "vc", "out"};
@@ -224,10 +224,19 @@ static diffattn_status decode_impl(diffattn_dtype dtype, diffattn_tensor q1, dif
     if (d > 256 || dv > 512)
         return fail(DIFFATTN_ERR_UNSUPPORTED, "diffattn_decode: d=%d dv=%d exceed the supported d <= 256, dv <= 512", d, dv);
     const size_t need = diffattn_decode_workspace_size(batch, heads, cache_len, dv);
-    if (workspace_bytes < need)
-        return fail(DIFFATTN_ERR_WORKSPACE, "diffattn_decode: workspace of %zu bytes < required %zu", workspace_bytes, need);
-    if (need > 0 && (!workspace || ((uintptr_t)workspace) % 256 != 0))
-        return fail(DIFFATTN_ERR_ARG, "diffattn_decode: workspace must be non-null and 256-byte aligned");
+    if (noalloc) {
+        if (need > diffattn::kNoallocScratchBytes)
+            return fail(DIFFATTN_ERR_WORKSPACE,
+                        "%s: these sizes need %zu bytes of workspace, more than the %zu bytes the library holds per "
+                        "GPU; call diffattn_decode with a workspace instead", fn_name, need,
+                        diffattn::kNoallocScratchBytes);
+    } else {
+        if (workspace_bytes < need)
+            return fail(DIFFATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes < required %zu", fn_name, workspace_bytes,
+                        need);
+        if (need > 0 && (!workspace || ((uintptr_t)workspace) % 256 != 0))
+            return fail(DIFFATTN_ERR_ARG, "%s: workspace must be non-null and 256-byte aligned", fn_name);
+    }
     const float sc = resolve_scale(scale, d);
     hipStream_t st = (hipStream_t)stream;
 
@@ -246,6 +255,22 @@ static diffattn_status decode_impl(diffattn_dtype dtype, diffattn_tensor q1, dif
         a.lam = lambda;
         a.norm_w = norm_w;
         a.ws = (float*)workspace;
+        if (noalloc) {
+            // every argument is valid: the launch's device (the current one, which the stream must
+            // belong to) and that device's copy of the library's scratch array
+            int dev = 0;
+            if (hipError_t e = hipGetDevice(&dev)) return hip_status(e, "diffattn_decode_noalloc: hipGetDevice");
+            if (st) {
+                hipDevice_t sdev = 0;
+                if (hipError_t e = hipStreamGetDevice(st, &sdev))
+                    return hip_status(e, "diffattn_decode_noalloc: hipStreamGetDevice");
+                if ((int)sdev != dev)
+                    return fail(DIFFATTN_ERR_ARG, "diffattn_decode_noalloc: the stream belongs to device %d but device "
+                                "%d is current", (int)sdev, dev);
+            }
+            if (hipError_t e = diffattn::decode_noalloc_scratch(dev, &a.ws))
+                return hip_status(e, "diffattn_decode_noalloc: scratch address");
+        }
         a.batch = batch; a.heads = heads; a.cache_len = cache_len;
         a.epi = epi == DIFFATTN_EPI_RMSNORM_SCALE;
         a.eps = eps; a.lambda_init = lambda_init;
@@ -274,6 +299,18 @@ diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffat
                                 diffattn_tensor out, void* workspace, size_t workspace_bytes, void* stream) {
     return decode_impl(dtype, q1, q2, k1c, k2c, vc, cache_lens, batch, heads, cache_len, d, dv, lambda, lambda_init,
                        epi, norm_w, eps, scale, out, workspace, workspace_bytes, stream, diffattn::PagedCache{});
+}
+
+static_assert(DIFFATTN_DECODE_NOALLOC_MAX_BYTES == diffattn::kNoallocScratchBytes,
+              "the header's limit is the size of the scratch array");
+
+diffattn_status diffattn_decode_noalloc(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1c,
+                                        diffattn_tensor k2c, diffattn_tensor vc, const int32_t* cache_lens, int batch,
+                                        int heads, int cache_len, int d, int dv, const float* lambda,
+                                        float lambda_init, diffattn_epilogue epi, const float* norm_w, float eps,
+                                        float scale, diffattn_tensor out, void* stream) {
+    return decode_impl(dtype, q1, q2, k1c, k2c, vc, cache_lens, batch, heads, cache_len, d, dv, lambda, lambda_init,
+                       epi, norm_w, eps, scale, out, nullptr, 0, stream, diffattn::PagedCache{}, true);
 }
 
 diffattn_status diffattn_decode_paged(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,

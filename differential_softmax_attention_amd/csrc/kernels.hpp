@@ -97,6 +97,10 @@ struct DecodeArgs {
 int decode_num_splits(int batch, int heads, int cache_len);
 size_t decode_workspace_bytes(int batch, int heads, int cache_len, int dv);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Size of the device array that serves as diffattn_decode_noalloc's workspace, and its address
+// on `device` (which must be the current device on the first call for it).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+hipError_t decode_noalloc_scratch(int device, float** out);
 
 // V2 split-K decode (bf16, d = 128, 2 <= group <= 32): q [batch, 1, 2h, d], caches
 // [batch, L, h_kv, d], lambda [batch, h] at lam[b * lam_bs + p], out [batch, 1, h, d].

@@ -216,6 +216,34 @@ diffattn_status diffattn_decode(diffattn_dtype dtype, diffattn_tensor q1, diffat
                                 void* stream);
 
 /*
+ * diffattn_decode without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, serving loops that keep allocation out of the step, and harnesses
+ * that forbid hipMalloc. Same operation, arguments, kernels and results as diffattn_decode (the
+ * outputs are bit-identical); the split partials go to a device array that the library holds,
+ * one per GPU it runs on, created when the library's code is loaded on that GPU and kept until
+ * the process ends. This call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.
+ *  Limit: the sizes must need at most DIFFATTN_DECODE_NOALLOC_MAX_BYTES of workspace
+ *  (diffattn_decode_workspace_size(batch, heads, cache_len, dv) <= 32 MiB, 1056 bytes per split
+ *  of each (batch, head); that covers every batch * heads up to 31,775 at any cache length);
+ *  larger sizes return ERR_WORKSPACE before any HIP call.
+ *  stream: must belong to the current device (ERR_ARG otherwise); NULL is the current device's
+ *  null stream.
+ *  Concurrency: every call on one GPU uses that GPU's one array, so calls that overlap in time on
+ *  one GPU (other streams, other threads) race on it and their results are undefined; calls on
+ *  one stream are ordered and safe. Nothing in the array needs clearing between calls (every
+ *  partial is written before it is read).
+ *  Errors: as diffattn_decode, without ERR_WORKSPACE for a short workspace.
+ */
+#define DIFFATTN_DECODE_NOALLOC_MAX_BYTES (32u << 20)
+diffattn_status diffattn_decode_noalloc(diffattn_dtype dtype, diffattn_tensor q1, diffattn_tensor q2,
+                                        diffattn_tensor k1c, diffattn_tensor k2c, diffattn_tensor vc,
+                                        const int32_t* cache_lens, int batch, int heads, int cache_len,
+                                        int d, int dv, const float* lambda, float lambda_init,
+                                        diffattn_epilogue epi, const float* norm_w, float eps, float scale,
+                                        diffattn_tensor out, void* stream);
+
+/*
  * DIFF V1 decode against a paged KV cache: the same operation as diffattn_decode, with the cache
  * of each sequence held in fixed-size pages of shared pools, listed by a block table.
  *  k1_pages, k2_pages: [num_pages, page_size, heads, d];  v_pages: [num_pages, page_size, heads, dv]

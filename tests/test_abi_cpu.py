@@ -119,6 +119,33 @@ def test_decode_workspace_size(L):
     assert 0 < small < big < 64 << 20      # partials only: a few MB even for a 17 GB cache
 
 
+def _decode_noalloc(L, B=2, H=2, Lc=100, d=64, dv=128, epi=1, lens=None, lam=FAKE, dtype=1):
+    ts = [_t(FAKE, 4096, 512, 64) for _ in range(6)]
+    return L.diffattn_decode_noalloc(dtype, ts[0], ts[1], ts[2], ts[3], ts[4], lens, B, H, Lc, d, dv, lam, 0.8, epi,
+                                     None, 1e-5, 0.0, ts[5], None)
+
+
+def test_decode_noalloc_rejects_before_any_hip_call(L):
+    assert _decode_noalloc(L, Lc=0) == da.DIFFATTN_ERR_ARG
+    assert _decode_noalloc(L, lam=None) == da.DIFFATTN_ERR_ARG
+    assert _decode_noalloc(L, dtype=9) == da.DIFFATTN_ERR_ARG
+    assert _decode_noalloc(L, d=512) == da.DIFFATTN_ERR_UNSUPPORTED
+    # beyond the library's scratch: a clear ERR_WORKSPACE that names the limit
+    assert _decode_noalloc(L, B=64, H=512, Lc=4096) == da.DIFFATTN_ERR_WORKSPACE
+    msg = L.diffattn_last_error().decode()
+    assert "diffattn_decode_noalloc" in msg and str(da.DECODE_NOALLOC_MAX_BYTES) in msg
+
+
+def test_decode_noalloc_limit_covers_what_the_header_states(L):
+    # every batch * heads up to 31,775 fits at any cache length; one more does not (at one split)
+    lim = da.DECODE_NOALLOC_MAX_BYTES
+    for bh in (1, 7, 100, 4095, 4097, 5000, 8000, 8191, 8192, 8193, 16384, 31775):
+        for lc in (1, 255, 256, 257, 4096, 65536, 1 << 20):
+            assert L.diffattn_decode_workspace_size(1, bh, lc, 128) <= lim, (bh, lc)
+    assert L.diffattn_decode_workspace_size(1, 31776, 1 << 20, 128) > lim
+    assert L.diffattn_decode_workspace_size(32, 16, 65536, 128) <= lim     # the 64K decode workload
+
+
 def _v2(L, B=1, N=8, h=4, hkv=2, d=128, lam=FAKE, causal=1, dtype=1, scale=0.0, mode=0):
     ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(4)]
     return L.diffattn_v2_fwd(dtype, ts[0], ts[1], ts[2], lam, mode, B, N, h, hkv, d, causal, scale, ts[3], None)
