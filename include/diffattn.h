@@ -101,7 +101,13 @@ diffattn_status diffattn_lambda(const float* lq1, const float* lk1, const float*
                                 void* stream);
 
 /*
- * DIFF V1 forward (prefill), one output row per query token and head.
+ * DIFF V1 forward (prefill), one output row per query token and head: the two softmax maps over the
+ * same visible keys, their difference with lambda, times V ("Differential Transformer:
+ * Noise-Canceling Attention by Subtraction", section "The mechanism"; "softmax can't say zero, so
+ * it subtracts", section "The mechanism, exactly"), then optionally the per-head RMSNorm and the
+ * (1 - lambda_init) multiply ("Noise-Canceling Attention by Subtraction", section "Making lambda
+ * learnable and stable", items 1-2; "softmax can't say zero", section "The row no longer sums to
+ * one").
  *  q1, q2: [batch, seq_q, heads, d];  k1, k2: [batch, seq_k, heads, d];  v: [batch, seq_k, heads, dv]
  *  out:    [batch, seq_q, heads, dv], same dtype as the inputs.
  *  lambda: DEVICE fp32 [heads] (per-layer lambda: pass equal entries). Any real value is accepted.
@@ -192,7 +198,9 @@ size_t diffattn_decode_workspace_size(int batch, int heads, int cache_len, int d
 
 /*
  * DIFF V1 decode: one new query per (batch, head) against a KV cache; the query's own key and
- * value are expected to be in the cache already, so it attends to cache entries 0..len-1.
+ * value are expected to be in the cache already, so it attends to cache entries 0..len-1. The
+ * operation is diffattn_fwd's for one query row over every cached key; the value cache is read
+ * once for both maps ("Differential Transformer V2": unfused V1 decoding reads it twice).
  *  q1, q2: [batch, 1, heads, d] (the token stride is unused);
  *  k1c, k2c: [batch, cache_len, heads, d];  vc: [batch, cache_len, heads, dv]
  *  cache_lens: DEVICE int32 [batch] with 1 <= len <= cache_len, or NULL (every len = cache_len).
@@ -277,7 +285,9 @@ diffattn_status diffattn_decode_paged(diffattn_dtype dtype, diffattn_tensor q1, 
 /*
  * DIFF V2 forward: out[b, i, p] = O_{2p} - lam[b, i, p] * O_{2p+1}, where O_j is ordinary softmax
  * attention of query head j over KV head j / (2h / h_kv) (the heads of one GQA group are
- * contiguous, and a differenced pair sits in one group). No norm, no rescale.
+ * contiguous, and a differenced pair sits in one group). No norm, no rescale ("softmax can't say
+ * zero, so it subtracts", section "DIFF V2: what the authors changed"; "Differential Transformer
+ * V2").
  *  q: [batch, seq, 2h, d];  k, v: [batch, seq, h_kv, d];  out: [batch, seq, h, d]
  *  lam: DEVICE fp32 [batch, seq, h] contiguous: lambda itself (lam_mode DIFFATTN_LAMBDA_VALUE) or
  *       the projected logits W_lambda x, whose sigmoid the kernel takes per row
