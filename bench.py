@@ -382,25 +382,37 @@ def main():
         lam9 = da.diffattn_lambda(*(x9[k].to(dev) for k in ("lq1", "lk1", "lq2", "lk2")), c9.layer)
         li9 = da.lambda_init(c9.layer)
         o9 = torch.empty((c9.B, c9.N, c9.H, c9.dv), dtype=torch.bfloat16, device=dev)
-        qs9 = [da.diffattn_quantize_fp8(x9[k]) for k in ("q1", "q2", "k1", "k2")]
-        fq9 = lambda: [da.diffattn_quantize_fp8(x9[k], out=q[0]) for k, q in zip(("q1", "q2", "k1", "k2"), qs9)]
-        ff9 = lambda: da.diffattn_fwd_fp8(*(q[0] for q in qs9), *(q[1] for q in qs9), x9["v"], lam9, causal=True,
+        codes9, sc9, _ = da.diffattn_quantize_fp8_qk(x9["q1"], x9["q2"], x9["k1"], x9["k2"])
+        fq9 = lambda: da.diffattn_quantize_fp8_qk(x9["q1"], x9["q2"], x9["k1"], x9["k2"], out=codes9)
+        ff9 = lambda: da.diffattn_fwd_fp8(*codes9, sc9[0], sc9[1], sc9[2], sc9[3], x9["v"], lam9, causal=True,
                                           epilogue=True, lambda_init_value=li9, out=o9)
+        o9b = torch.empty_like(o9)
+        fb9 = lambda: da.diffattn_fwd(x9["q1"], x9["q2"], x9["k1"], x9["k2"], x9["v"], lam9, causal=True,
+                                      epilogue=True, lambda_init_value=li9, out=o9b)
+
+        def fs9():
+            fq9()
+            ff9()
         fq9()
         ff9()
         torch.cuda.synchronize()
         _r = measure(fq9, torch, samples=args.secondary_samples)
-        avg_q, _ = _r["median"], _r["min"]
+        avg_q = _r["median"]
         _r = measure(ff9, torch, samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
+        avg_s = measure(fs9, torch, samples=args.secondary_samples)["median"]
+        avg_b = measure(fb9, torch, samples=args.secondary_samples)["median"]
         fl9 = FLOP_PER_PAIR_V1 * c9.B * c9.H * causal_pairs(c9.N)
         tf = fl9 / (avg * 1e-3) / 1e12
         secondary["v1_prefill_2k_fp8_logits"] = {
             "workload": c9.name + ", Q1 Q2 K1 K2 in fp8 e4m3", "kernel_median_ms": round(avg, 4),
             "kernel_min_ms": round(mn, 4), "flop": fl9, "TFLOP/s": round(tf, 2),
-            "quantize_four_operands_median_ms": round(avg_q, 4)}
-        log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s (quantising Q1, Q2, K1, K2: {avg_q:.3f} ms)")
-        del x9, o9, qs9
+            "quantize_four_operands_median_ms": round(avg_q, 4),
+            "quantize_plus_forward_median_ms": round(avg_s, 4),
+            "bf16_forward_median_ms": round(avg_b, 4)}
+        log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s (quantising Q1, Q2, K1, K2: {avg_q:.3f} ms; "
+            f"quantise + fp8 forward {avg_s:.3f} ms against bf16 forward {avg_b:.3f} ms)")
+        del x9, o9, o9b, codes9, sc9
     if "v2bwd" in which:
         # training step of the V2 prefill workload: the V2 training forward and the V2 backward
         c8 = W.V2_GQA_8K

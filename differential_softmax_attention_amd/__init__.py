@@ -39,7 +39,7 @@ EXPORTED = ("diffattn_last_error", "diffattn_version", "diffattn_lambda_init", "
             "diffattn_bwd_workspace_size", "diffattn_bwd", "diffattn_lambda_bwd", "diffattn_decode_paged",
             "diffattn_v2_decode_paged", "diffattn_v2_fwd_train", "diffattn_v2_bwd_workspace_size", "diffattn_v2_bwd",
             "diffattn_quantize_fp8", "diffattn_fwd_fp8", "diffattn_fwd_lambda", "diffattn_probe_mfma_peak",
-            "diffattn_decode_noalloc")
+            "diffattn_decode_noalloc", "diffattn_quantize_fp8_qk")
 DECODE_NOALLOC_MAX_BYTES = 32 << 20
 
 
@@ -115,6 +115,8 @@ def lib():
                                           T, vp]
         L.diffattn_quantize_fp8.restype = i
         L.diffattn_quantize_fp8.argtypes = [T, i, i, i, i, T, vp, vp, vp]
+        L.diffattn_quantize_fp8_qk.restype = i
+        L.diffattn_quantize_fp8_qk.argtypes = [T, T, T, T, i, i, i, i, i, T, T, T, T, vp, vp, vp]
         L.diffattn_fwd_fp8.restype = i
         L.diffattn_fwd_fp8.argtypes = [T, T, T, T, vp, vp, vp, vp, T, i, i, i, i, i, i, vp, f, i, i, vp, f, f, T, vp]
         L.diffattn_v2_decode_paged.restype = i
@@ -419,6 +421,28 @@ def diffattn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None):
     amax = torch.empty((B, H), dtype=torch.float32, device=x.device)
     _check(lib().diffattn_quantize_fp8(_t4(x), B, N, H, dim, _t4(out), _dp(scales), _dp(amax),
                                        _stream(x.device)))
+    return out, scales, amax
+
+
+def diffattn_quantize_fp8_qk(q1, q2, k1, k2, out=None):
+    """The four score operands quantised in one call: q1, q2 bf16 [B, Nq, H, dim], k1, k2 bf16
+    [B, Nk, H, dim]. Returns (codes (cq1, cq2, ck1, ck2) float8_e4m3fn, scales fp32 [4, B, H],
+    amax fp32 [4, B, H]); scales[i] is the i-th operand's, in the order q1, q2, k1, k2."""
+    _shape("q1", q1, (None, None, None, None), torch.bfloat16)
+    B, Nq, H, dim = q1.shape
+    _shape("q2", q2, (B, Nq, H, dim), torch.bfloat16, q1)
+    _shape("k1", k1, (B, None, H, dim), torch.bfloat16, q1)
+    Nk = k1.shape[1]
+    _shape("k2", k2, (B, Nk, H, dim), torch.bfloat16, q1)
+    f8 = torch.float8_e4m3fn
+    if out is None:
+        out = tuple(torch.empty(t.shape, dtype=f8, device=q1.device) for t in (q1, q2, k1, k2))
+    for name, o, x in zip(("oq1", "oq2", "ok1", "ok2"), out, (q1, q2, k1, k2)):
+        _shape(name, o, tuple(x.shape), f8, q1)
+    scales = torch.empty((4, B, H), dtype=torch.float32, device=q1.device)
+    amax = torch.empty((4, B, H), dtype=torch.float32, device=q1.device)
+    _check(lib().diffattn_quantize_fp8_qk(_t4(q1), _t4(q2), _t4(k1), _t4(k2), B, Nq, Nk, H, dim,
+                                          *(_t4(o) for o in out), _dp(scales), _dp(amax), _stream(q1.device)))
     return out, scales, amax
 
 

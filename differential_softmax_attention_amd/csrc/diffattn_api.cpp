@@ -681,6 +681,46 @@ diffattn_status diffattn_quantize_fp8(diffattn_tensor x, int batch, int tokens, 
     return hip_status(diffattn::launch_quantize_fp8(a, (hipStream_t)stream), "diffattn_quantize_fp8 launch");
 }
 
+diffattn_status diffattn_quantize_fp8_qk(diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1, diffattn_tensor k2,
+                                         int batch, int seq_q, int seq_k, int heads, int dim, diffattn_tensor oq1,
+                                         diffattn_tensor oq2, diffattn_tensor ok1, diffattn_tensor ok2, float* scales,
+                                         float* amax, void* stream) {
+    const diffattn_tensor* xs[4] = {&q1, &q2, &k1, &k2};
+    const diffattn_tensor* os[4] = {&oq1, &oq2, &ok1, &ok2};
+    const char* xn[4] = {"q1", "q2", "k1", "k2"};
+    const char* on[4] = {"oq1", "oq2", "ok1", "ok2"};
+    for (int i = 0; i < 4; ++i) {
+        if (diffattn_status st = check_tensor(*xs[i], xn[i], DIFFATTN_BF16)) return st;
+        if (!os[i]->ptr) return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8_qk: %s is null", on[i]);
+        if (os[i]->s_batch < 0 || os[i]->s_seq < 0 || os[i]->s_head < 0)
+            return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8_qk: negative stride in %s", on[i]);
+        if (((uintptr_t)os[i]->ptr) % 2 != 0 || os[i]->s_batch % 2 != 0 || os[i]->s_seq % 2 != 0 ||
+            os[i]->s_head % 2 != 0)
+            return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8_qk: %s base and strides must be even", on[i]);
+    }
+    if (!scales || !amax) return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8_qk: scales and amax must be non-null");
+    if (batch < 1 || seq_q < 1 || seq_k < 1 || heads < 1 || dim < 2 || dim % 2 != 0)
+        return fail(DIFFATTN_ERR_ARG,
+                    "diffattn_quantize_fp8_qk: sizes must be >= 1 and dim even (batch=%d seq_q=%d seq_k=%d heads=%d dim=%d)",
+                    batch, seq_q, seq_k, heads, dim);
+    if (batch > 65535 || heads > 65535)
+        return fail(DIFFATTN_ERR_ARG, "diffattn_quantize_fp8_qk: batch and heads must be <= 65535");
+    diffattn::Fp8QuantManyArgs a{};
+    const int64_t bh = (int64_t)batch * heads;
+    for (int i = 0; i < 4; ++i) {
+        a.x[i] = xs[i]->ptr;
+        a.out[i] = os[i]->ptr;
+        copy_strides(a.xs[i], *xs[i]);
+        copy_strides(a.os[i], *os[i]);
+        a.scales[i] = scales + i * bh;
+        a.amax[i] = amax + i * bh;
+        a.tokens[i] = i < 2 ? seq_q : seq_k;
+    }
+    a.n = 4;
+    a.batch = batch; a.heads = heads; a.dim = dim;
+    return hip_status(diffattn::launch_quantize_fp8_many(a, (hipStream_t)stream), "diffattn_quantize_fp8_qk launch");
+}
+
 diffattn_status diffattn_fwd_fp8(diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1, diffattn_tensor k2,
                                  const float* sq1, const float* sq2, const float* sk1, const float* sk2,
                                  diffattn_tensor v, int batch, int heads, int seq_q, int seq_k, int d, int dv,

@@ -193,6 +193,19 @@ struct Fp8QuantArgs {
 
 hipError_t launch_quantize_fp8(const Fp8QuantArgs& a, hipStream_t stream);
 
+// Up to four score operands quantised together (diffattn_quantize_fp8_qk): operand i has its own
+// tensor, codes, token count, scales and amax; batch, heads and dim are shared.
+struct Fp8QuantManyArgs {
+    const void* x[4];
+    void* out[4];
+    int64_t xs[4][3], os[4][3];
+    float* scales[4];
+    float* amax[4];
+    int tokens[4];
+    int n, batch, heads, dim;
+};
+hipError_t launch_quantize_fp8_many(const Fp8QuantManyArgs& a, hipStream_t stream);
+
 // Dense bf16 MFMA rate probe: `blocks` blocks of 4 waves, each wave 8 x iters MFMAs of 32x32x16
 // (32768 flop each); out receives blocks * 256 floats.
 hipError_t launch_mfma_peak(float* out, int blocks, int iters, hipStream_t stream);

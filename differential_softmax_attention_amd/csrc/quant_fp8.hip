@@ -9,7 +9,9 @@
 // With at least 256 slices of up to 4096 x 128 elements, one kernel, a block per slice (amax, then
 // the codes). Otherwise three: zero the amax buffer, per-block maxima merged with an atomic max on the
 // fp32 bit pattern (exact, so the result does not depend on the order), then the conversion,
-// which also writes s.
+// which also writes s. The four operands of one forward (Q1, Q2, K1, K2) go through one launch
+// when every slice fits in the registers of a 1024-thread block (16 x 16 bytes per thread): read
+// once, amax, codes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -168,12 +170,92 @@ __global__ __launch_bounds__(1024) void fp8_slice_kernel(Fp8QuantArgs a) {
     }
 }
 
+// Several operands in one launch, one block per (head, batch, operand) slice of up to
+// 1024 x kRegChunks 16-byte chunks, held in registers between its two steps: the slice is read
+// once from memory, its amax taken (wave and block reductions, no atomics), then its codes written
+// from the registers.
+constexpr int kRegChunks = 16;
+__global__ __launch_bounds__(1024) void fp8_slices_reg_kernel(Fp8QuantManyArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, op = blockIdx.z;
+    const int tid = threadIdx.x;
+    const bf16* xb = (const bf16*)a.x[op] + b * a.xs[op][0] + (int64_t)h * a.xs[op][2];
+    unsigned char* ob = (unsigned char*)a.out[op] + b * a.os[op][0] + (int64_t)h * a.os[op][2];
+    const int64_t xt = a.xs[op][1], ot = a.os[op][1];
+    const int cpr = a.dim / 8;
+    const int n = a.tokens[op] * cpr;
+    bf16x8 v[kRegChunks];
+    float m = 0.f;
+#pragma unroll
+    for (int u = 0; u < kRegChunks; ++u) {
+        const int e = min(tid + u * 1024, n - 1);   // past the end: the last chunk again
+        v[u] = *(const bf16x8*)(xb + (int64_t)(e / cpr) * xt + 8 * (e % cpr));
+    }
+#pragma unroll
+    for (int u = 0; u < kRegChunks; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)v[u][j]));
+    m = wave_max(m);
+    __shared__ float red[16];
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    float am = red[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) am = fmaxf(am, red[w]);
+    const float s = am > 0.f ? am / 448.f : 1.f;
+    const float r = am > 0.f ? 448.f / am : 1.f;
+    if (tid == 0) {
+        a.amax[op][(int64_t)b * a.heads + h] = am;
+        a.scales[op][(int64_t)b * a.heads + h] = s;
+    }
+#pragma unroll
+    for (int u = 0; u < kRegChunks; ++u) {
+        const int e = tid + u * 1024;
+        if (e < n) {
+            const int t = e / cpr, c = 8 * (e % cpr);
+            unsigned w[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int lo = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[u][4 * j] * r, (float)v[u][4 * j + 1] * r, 0, false);
+                w[j] = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32((float)v[u][4 * j + 2] * r, (float)v[u][4 * j + 3] * r,
+                                                                 lo, true);
+            }
+            *(uint2*)(ob + (int64_t)t * ot + c) = make_uint2(w[0], w[1]);
+        }
+    }
+}
+
+bool fp8_vec_ok(const void* x, const int64_t* xs, const void* out, const int64_t* os, int dim) {
+    return dim % 8 == 0 && ((uintptr_t)x) % 16 == 0 && xs[0] % 8 == 0 && xs[1] % 8 == 0 && xs[2] % 8 == 0 &&
+           ((uintptr_t)out) % 8 == 0 && os[0] % 8 == 0 && os[1] % 8 == 0 && os[2] % 8 == 0;
+}
+
 }  // namespace
 
+hipError_t launch_quantize_fp8_many(const Fp8QuantManyArgs& a, hipStream_t stream) {
+    bool one = true;
+    for (int i = 0; i < a.n; ++i)
+        one = one && fp8_vec_ok(a.x[i], a.xs[i], a.out[i], a.os[i], a.dim) &&
+              (int64_t)a.tokens[i] * (a.dim / 8) <= (int64_t)1024 * kRegChunks;
+    if (one) {
+        hipLaunchKernelGGL(fp8_slices_reg_kernel, dim3(a.heads, a.batch, a.n), dim3(1024), 0, stream, a);
+        return hipGetLastError();
+    }
+    // longer slices: each operand on its own
+    for (int i = 0; i < a.n; ++i) {
+        Fp8QuantArgs s{};
+        s.x = a.x[i];
+        s.out = a.out[i];
+        for (int k = 0; k < 3; ++k) { s.xs[k] = a.xs[i][k]; s.os[k] = a.os[i][k]; }
+        s.scales = a.scales[i];
+        s.amax = a.amax[i];
+        s.batch = a.batch; s.tokens = a.tokens[i]; s.heads = a.heads; s.dim = a.dim;
+        if (hipError_t e = launch_quantize_fp8(s, stream)) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_quantize_fp8(const Fp8QuantArgs& a, hipStream_t stream) {
-    const bool vec = a.dim % 8 == 0 && ((uintptr_t)a.x) % 16 == 0 && a.xs[0] % 8 == 0 && a.xs[1] % 8 == 0 &&
-                     a.xs[2] % 8 == 0 && ((uintptr_t)a.out) % 8 == 0 && a.os[0] % 8 == 0 && a.os[1] % 8 == 0 &&
-                     a.os[2] % 8 == 0;
+    const bool vec = fp8_vec_ok(a.x, a.xs, a.out, a.os, a.dim);
     if (vec && (int64_t)a.tokens * a.dim <= (int64_t)4096 * 128 && a.batch * a.heads >= 256) {
         hipLaunchKernelGGL(fp8_slice_kernel, dim3(a.heads, a.batch), dim3(1024), 0, stream, a);
         return hipGetLastError();

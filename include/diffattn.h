@@ -170,6 +170,23 @@ diffattn_status diffattn_quantize_fp8(diffattn_tensor x, int batch, int tokens, 
                                       diffattn_tensor out, float* scales, float* amax, void* stream);
 
 /*
+ * The four score operands of one fp8 forward quantised in one call: diffattn_quantize_fp8 of
+ * q1, q2 (seq_q tokens) and k1, k2 (seq_k tokens), same arithmetic and bit-identical codes.
+ *  q1, q2, k1, k2: bf16 views as in diffattn_quantize_fp8;  oq1, oq2, ok1, ok2: their code views.
+ *  scales, amax: DEVICE fp32 [4, batch, heads] contiguous, operand order q1, q2, k1, k2 (so
+ *  scales, scales + batch * heads, ... are the sq1, sq2, sk1, sk2 of diffattn_fwd_fp8).
+ *  Kernels: one launch for all four when every slice fits in the registers of a 1024-thread block
+ *  (tokens * dim <= 131072, 16-byte aligned views): each slice read once, its amax taken, its codes
+ *  written; else diffattn_quantize_fp8's kernels operand by operand.
+ *  Errors: as diffattn_quantize_fp8.
+ */
+diffattn_status diffattn_quantize_fp8_qk(diffattn_tensor q1, diffattn_tensor q2, diffattn_tensor k1,
+                                         diffattn_tensor k2, int batch, int seq_q, int seq_k, int heads,
+                                         int dim, diffattn_tensor oq1, diffattn_tensor oq2,
+                                         diffattn_tensor ok1, diffattn_tensor ok2, float* scales,
+                                         float* amax, void* stream);
+
+/*
  * DIFF V1 forward with the attention logits taken on the fp8 matrix cores: S_k = Q_k K_k^T with
  * e4m3 operands (one v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 tile and map), each product scaled
  * back by sq_k[b, h] * sk_k[b, h] in fp32; the softmaxes, the difference, the products with V

@@ -121,3 +121,24 @@ def test_full_fp8_prefill_2k():
         ref = oracle.v1_forward(*deq, sl(x["v"]).astype(np.float64), lam_np[h:h + 1], causal=True, epilogue=True,
                                 lambda_init_value=li, rows=np.array([(0, 0, r) for r in rows]))
         assert maxerr(got[b, rows, h], ref) <= TOL_BF16, (b, h)
+
+
+@pytest.mark.parametrize("B,Nq,Nk,H", [(2, 100, 100, 3), (1, 40, 300, 2), (4, 2048, 2048, 16), (1, 5000, 5000, 2)])
+def test_quantize_qk_equals_per_operand(B, Nq, Nk, H):
+    # one call for the four operands (one launch when the slices fit in registers: the 2K
+    # workload's shape; operand by operand otherwise) against diffattn_quantize_fp8 and the oracle
+    g = torch.Generator(device=DEV).manual_seed(7000 + Nq + Nk)
+    xs = [torch.randn((B, n, H, 64), generator=g, device=DEV).mul_(s).to(torch.bfloat16)
+          for n, s in ((Nq, 1.0), (Nq, 3.0), (Nk, 0.5), (Nk, 20.0))]
+    xs[1][0, :, 0] = 0.0                                       # an all-zero slice
+    codes, scales, amax = da.diffattn_quantize_fp8_qk(*xs)
+    torch.cuda.synchronize()
+    for i, x in enumerate(xs):
+        c1, s1, a1 = da.diffattn_quantize_fp8(x)
+        torch.cuda.synchronize()
+        assert torch.equal(codes[i].view(torch.uint8), c1.view(torch.uint8)), i
+        assert torch.equal(scales[i], s1) and torch.equal(amax[i], a1), i
+        if B * x.shape[1] <= 4 * 2048:
+            rc, rs = oracle.quantize_fp8(x.float().cpu().numpy())
+            assert np.array_equal(codes[i].view(torch.uint8).cpu().numpy(), rc), i
+            assert np.array_equal(scales[i].cpu().numpy(), rs), i
