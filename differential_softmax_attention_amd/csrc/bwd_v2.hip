@@ -90,9 +90,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __align__(16) unsigned char smem[4 * kKStage];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, h2 = lane >> 5;
-    // the last query tiles see the most keys under causal masking: they go first
-    const int qt = gridDim.y - 1 - blockIdx.y, p = blockIdx.x % a.h, b = blockIdx.x / a.h;
-    const int g = (2 * p) / a.group;
+    // the last query tiles see the most keys under causal masking: they go first. Within a query
+    // tile, (batch, KV head) varies fastest: blocks are dealt round-robin over the 8 XCDs in order
+    // of linear block index, so when h_kv * batch is a multiple of 8 the pairs of one (batch, KV
+    // head) run on one XCD and share its L2 copy of their K and V tiles.
+    const int units = a.h_kv * a.batch, unit = blockIdx.x % units;
+    const int g = unit % a.h_kv, b = unit / a.h_kv, p = g * (a.group / 2) + blockIdx.x / units;
+    const int qt = gridDim.y - 1 - blockIdx.y;
     const int q0 = qt * 128, qw0 = q0 + wave * 32, qrow = qw0 + n;
     const bool qok = qrow < a.seq;
     const int qr = qok ? qrow : 0;
@@ -335,15 +339,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ------------------------------------------------------------------------------------------------
-// dK, dV: a block of 4 waves owns 128 keys of one KV head, 32 per wave, and walks the query tiles
-// of every pair of the group. Each lane holds its key's K and V rows as MFMA B operands; dK^T and
-// dV^T of the wave's 32 keys (128 registers) sit in AGPRs. One wave per SIMD.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_v2_dkdv_kernel(V2BwdArgs a) {
-    __shared__ __align__(16) unsigned char sq[kDkdvLds];
+// dK, dV of one key tile: the block's 4 waves own 128 keys of KV head g, 32 per wave, and walk the
+// query tiles of every pair of the group, from the last tile down (down) or from the first tile the
+// keys see up. Each lane holds its key's K and V rows as MFMA B operands; dK^T and dV^T of the
+// wave's 32 keys (128 registers) sit in AGPRs. One wave per SIMD. Ends with the LDS ring still in
+// use by other waves: a second call needs a block barrier first.
+__device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdArgs& a, unsigned char* sq, int kt,
+                                                                    int g, int b, bool down) {
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = tid & 63;
     const int n = lane & 31, h2 = lane >> 5;
-    // the first key tiles see the most queries under causal masking: they go first
-    const int kt = blockIdx.y, g = blockIdx.x % a.h_kv, b = blockIdx.x / a.h_kv;
     const int k0 = kt * 128, kw0 = k0 + wave * 32, key = kw0 + n;
     const int npair = a.group / 2;        // pairs of this KV group: g * npair .. + npair - 1
     const float c = a.scale_log2;
@@ -367,10 +371,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int t = 0; t < 4; ++t) { dk[t] = f32x16{}; dv[t] = f32x16{}; }
 
-    // work items: (query tile, pair of the group), query tile outermost
+    // work items: (query tile, pair of the group), query tile outermost; item it reads query tile
+    // qbase + qstep * (it / npair)
     const int nqt = (a.seq + kBN - 1) / kBN;
     const int qt0 = a.causal ? k0 / kBN : 0;
     const int nit = (nqt - qt0) * npair;
+    const int qbase = down ? nqt - 1 : qt0, qstep = down ? -1 : 1;
 
     // stage DMA: thread tid fills Q_{2p}, Q_{2p+1} and go_p slots tid and tid + 256; wave 0 also
     // fetches the rows' log-sum-exp and D (64 floats each) and lambda (32 floats). Rows past the
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int r0 = slot_row<kD>(tid), r1 = r0 + 16;
     const int c0 = slot_chunk<kD>(tid), c1 = slot_chunk<kD>(tid + 256);
     auto issue = [&](int it, int stage) __attribute__((always_inline)) {
-        const int qt = qt0 + it / npair, p = g * npair + it % npair;
+        const int qt = qbase + qstep * (it / npair), p = g * npair + it % npair;
         const int i0 = qt * kBN;
         const int last = min(kBN, a.seq - i0) - 1;
         const uint32_t st = lds_sq + stage * kTile + wave * 1024;
@@ -497,7 +503,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < 24; ++i) mfma_g(i, rd_g(slot, i), b1[i / 12], b2[i / 12], bp[i / 12]);
     };
-    auto item_i0 = [&](int it) { return (qt0 + it / npair) * kBN; };
+    auto item_i0 = [&](int it) { return (qbase + qstep * (it / npair)) * kBN; };
     auto item_full = [&](int i0) { return i0 + kBN <= a.seq && kw0 + kBN <= a.seq && (!a.causal || kw0 + kBN - 1 <= i0); };
     auto item_skip = [&](int i0) { return !wave_active || (a.causal && i0 + kBN - 1 < kw0); };
     // two items per block barrier; slots S0, S1 hold them, N0, N1 take the pair after next.
@@ -593,7 +599,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (k0 + 128 <= a.seq) {
         const int qf = a.causal ? (k0 + 127 + kBN - 1) / kBN : 0;   // first tile unmasked for all waves
         const int qe = a.seq / kBN;                                    // tiles below hold no row past the end
-        const int i_f = (max(qf, qt0) - qt0) * npair, i_e = (qe - qt0) * npair;
+        // the unmasked tiles [max(qf, qt0), qe) as a range of items in the walk's order
+        const int i_f = (down ? nqt - qe : max(qf, qt0) - qt0) * npair;
+        const int i_e = (down ? nqt - max(qf, qt0) : qe - qt0) * npair;
         const int i4 = (i_f + 3) / 4 * 4;
         if (i4 + 4 <= i_e) { is = i4; ie = i4 + (i_e - i4) / 4 * 4; }
     }
@@ -639,6 +647,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+// Block y of KV head g owns key tiles y and nkt - 1 - y, one after the other. Under causal
+// masking the pair sees a fixed number of query tiles (nqt + 4) whatever y is, so every block does
+// the same work. The first tile is walked from the last query tile down, the second from its first
+// query tile up: blocks that start together then read the same query tile at the same time (each
+// block's second walk is at tile t - 4 after t tiles of work). Blocks are dealt round-robin over
+// the 8 XCDs in order of linear block index, so when h_kv * batch is a multiple of 8 all blocks of
+// one (batch, KV head) run on one XCD, whose L2 then serves a query tile to all of them from one
+// fetch instead of each block fetching it again. The loop is kept rolled: one copy of the body.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_v2_dkdv_kernel(V2BwdArgs a) {
+    __shared__ __align__(16) unsigned char sq[kDkdvLds];
+    const int g = blockIdx.x % a.h_kv, b = blockIdx.x / a.h_kv, y = blockIdx.y;
+    const int nkt = (a.seq + 127) / 128;
+#pragma clang loop unroll(disable)
+    for (int s = 0; s < 2; ++s) {
+        const int kt = s ? nkt - 1 - y : y;
+        if (s) {
+            if (kt <= y) break;   // an odd tile count leaves the middle tile unpaired
+            __syncthreads();      // every wave is done with the LDS ring of the first tile
+        }
+        dkdv_key_tile(a, sq, kt, g, b, s == 0);
+    }
+}
+
 }  // namespace
 
 size_t v2_bwd_workspace_bytes(int batch, int h, int seq) {
@@ -663,7 +694,7 @@ hipError_t launch_v2_bwd(V2BwdArgs a, void* workspace, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_v2_dq_kernel, dim3(a.h * a.batch, (a.seq + 127) / 128), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_v2_dkdv_kernel, dim3(a.h_kv * a.batch, (a.seq + 127) / 128), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_v2_dkdv_kernel, dim3(a.h_kv * a.batch, ((a.seq + 127) / 128 + 1) / 2), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
