@@ -114,15 +114,17 @@ def time_launches(fn, torch, samples=50, per=1):
     return {"mean": statistics.fmean(ms), "median": statistics.median(ms), "min": ms[0]}
 
 
-def measure(fn, torch, samples=50, target_ms=2.0, floor=3, min_s=0.2):
+def measure(fn, torch, label, samples=50, target_ms=2.0, floor=3, min_s=0.2):
     """Warm fn up until its time is steady, then time it with `per` chosen so a sample lasts about
-    target_ms."""
-    warm_until_stable(fn, floor, torch, min_s=min_s, max_s=3.0, batch=4)
+    target_ms. Logs the call counts under `label`, so that a kernel trace of the run can be split
+    into untimed and timed launches."""
+    n_warm = warm_until_stable(fn, floor, torch, min_s=min_s, max_s=3.0, batch=4)
     t = time_launches(fn, torch, samples=3, per=1)
     per = max(1, min(50, int(round(target_ms / max(t["median"], 1e-3)))))
     r = time_launches(fn, torch, samples=samples, per=per)
     r["per"] = per
     r["samples"] = samples
+    log(f"[bench]   calls of {label}: {n_warm + 3} untimed, then {samples} x {per} timed")
     return r
 
 
@@ -269,13 +271,15 @@ def main():
                                      epilogue=True, lambda_init_value=da.lambda_init(c3.layer), out=o3)
         f3()
         torch.cuda.synchronize()
-        _r = measure(f3, torch, samples=args.secondary_samples)
+        _r = measure(f3, torch, "v1_prefill_32k", samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
         fl3 = FLOP_PER_PAIR_V1 * c3.B * c3.H * causal_pairs(c3.N)
         tf = fl3 / (avg * 1e-3) / 1e12
         secondary["v1_prefill_32k"] = {"workload": c3.name, "kernel_median_ms": round(avg, 4),
                                        "kernel_min_ms": round(mn, 4), "flop": fl3, "TFLOP/s": round(tf, 2),
-                                       "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                                       "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                       "traffic": load_traffic("v1_prefill_32k",
+                                                               ["fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"])}
         log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s")
         del x3, o3
     if "v2" in which:
@@ -286,7 +290,7 @@ def main():
         f5 = lambda: da.diffattn_v2_fwd(x5["q"], x5["k"], x5["v"], x5["lam"], causal=True, out=o5)
         f5()
         torch.cuda.synchronize()
-        _r = measure(f5, torch, samples=args.secondary_samples)
+        _r = measure(f5, torch, "v2_gqa_8k", samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
         fl5 = FLOP_PER_PAIR_V2 * c5.B * c5.hq * causal_pairs(c5.N)
         tf = fl5 / (avg * 1e-3) / 1e12
@@ -300,7 +304,7 @@ def main():
         fz = lambda: da.diffattn_v2_fwd(x5["q"], x5["k"], x5["v"], z5, causal=True, out=o5, lam_logits=True)
         fz()
         torch.cuda.synchronize()
-        _r = measure(fz, torch, samples=args.secondary_samples)
+        _r = measure(fz, torch, "v2_gqa_8k_logits", samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
         tf = fl5 / (avg * 1e-3) / 1e12
         secondary["v2_gqa_8k"]["lam_logits_kernel_median_ms"] = round(avg, 4)
@@ -318,7 +322,7 @@ def main():
                                         lambda_init_value=c4.lambda_init, workspace=ws, out=o4)
         f4()
         torch.cuda.synchronize()
-        _r = measure(f4, torch, samples=args.secondary_samples)
+        _r = measure(f4, torch, "v1_decode", samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
         nbytes = DECODE_BYTES_PER_TOKEN * c4.B * c4.H * c4.L
         gbs = nbytes / (avg * 1e-3) / 1e9
@@ -334,7 +338,7 @@ def main():
                                               epilogue=True, lambda_init_value=c4.lambda_init, workspace=ws, out=o4)
         fp()
         torch.cuda.synchronize()
-        _r = measure(fp, torch, samples=args.secondary_samples)
+        _r = measure(fp, torch, "v1_decode_paged", samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
         gbs = nbytes / (avg * 1e-3) / 1e9
         secondary["v1_decode_64k_paged"] = {"workload": c4.name + f", {PAGE_SIZE}-token pages",
@@ -360,9 +364,9 @@ def main():
                                      lambda_init_value=li7, workspace=ws7)
         fb()
         torch.cuda.synchronize()
-        _r = measure(ft, torch, samples=args.secondary_samples)
+        _r = measure(ft, torch, "v1_train_forward", samples=args.secondary_samples)
         avg_f, mn_f = _r["median"], _r["min"]
-        _r = measure(fb, torch, samples=args.secondary_samples)
+        _r = measure(fb, torch, "v1_backward", samples=args.secondary_samples)
         avg_b, mn_b = _r["median"], _r["min"]
         pairs7 = c7.B * c7.H * causal_pairs(c7.N)
         fl_b = FLOP_PER_PAIR_V1_BWD * pairs7
@@ -382,8 +386,12 @@ def main():
         lam9 = da.diffattn_lambda(*(x9[k].to(dev) for k in ("lq1", "lk1", "lq2", "lk2")), c9.layer)
         li9 = da.lambda_init(c9.layer)
         o9 = torch.empty((c9.B, c9.N, c9.H, c9.dv), dtype=torch.bfloat16, device=dev)
-        codes9, sc9, _ = da.diffattn_quantize_fp8_qk(x9["q1"], x9["q2"], x9["k1"], x9["k2"])
-        fq9 = lambda: da.diffattn_quantize_fp8_qk(x9["q1"], x9["q2"], x9["k1"], x9["k2"], out=codes9)
+        codes9, sc9, am9 = da.diffattn_quantize_fp8_qk(x9["q1"], x9["q2"], x9["k1"], x9["k2"])
+        # the quantiser's C-ABI arguments marshalled once (as for the main step): the kernel takes
+        # about 20 us, less than the Python binding's own argument checks
+        q_args = (*(da._t4(x9[k]) for k in ("q1", "q2", "k1", "k2")), c9.B, c9.N, c9.N, c9.H, c9.d,
+                  *(da._t4(o) for o in codes9), sc9.data_ptr(), am9.data_ptr(), stream)
+        fq9 = lambda: da._check(L.diffattn_quantize_fp8_qk(*q_args))
         ff9 = lambda: da.diffattn_fwd_fp8(*codes9, sc9[0], sc9[1], sc9[2], sc9[3], x9["v"], lam9, causal=True,
                                           epilogue=True, lambda_init_value=li9, out=o9)
         o9b = torch.empty_like(o9)
@@ -396,12 +404,12 @@ def main():
         fq9()
         ff9()
         torch.cuda.synchronize()
-        _r = measure(fq9, torch, samples=args.secondary_samples)
+        _r = measure(fq9, torch, "fp8_quantize", samples=args.secondary_samples)
         avg_q = _r["median"]
-        _r = measure(ff9, torch, samples=args.secondary_samples)
+        _r = measure(ff9, torch, "fp8_forward", samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
-        avg_s = measure(fs9, torch, samples=args.secondary_samples)["median"]
-        avg_b = measure(fb9, torch, samples=args.secondary_samples)["median"]
+        avg_s = measure(fs9, torch, "fp8_quantize_plus_forward", samples=args.secondary_samples)["median"]
+        avg_b = measure(fb9, torch, "bf16_forward", samples=args.secondary_samples)["median"]
         fl9 = FLOP_PER_PAIR_V1 * c9.B * c9.H * causal_pairs(c9.N)
         tf = fl9 / (avg * 1e-3) / 1e12
         secondary["v1_prefill_2k_fp8_logits"] = {
@@ -427,9 +435,9 @@ def main():
                                          workspace=ws8)
         fb8()
         torch.cuda.synchronize()
-        _r = measure(ft8, torch, samples=args.secondary_samples)
+        _r = measure(ft8, torch, "v2_train_forward", samples=args.secondary_samples)
         avg_f, _ = _r["median"], _r["min"]
-        _r = measure(fb8, torch, samples=args.secondary_samples)
+        _r = measure(fb8, torch, "v2_backward", samples=args.secondary_samples)
         avg_b, mn_b = _r["median"], _r["min"]
         fl8 = FLOP_PER_PAIR_V2_BWD * c8.B * c8.hq * causal_pairs(c8.N)
         secondary["v2_backward_8k"] = {"workload": c8.name, "train_forward_median_ms": round(avg_f, 4),
@@ -451,7 +459,7 @@ def main():
         f6 = lambda: da.diffattn_v2_decode(x6["q"], x6["k"], x6["v"], lam6, workspace=ws6, out=o6)
         f6()
         torch.cuda.synchronize()
-        _r = measure(f6, torch, samples=args.secondary_samples)
+        _r = measure(f6, torch, "v2_decode", samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
         nbytes = 2 * c6.d * 2 * c6.B * c6.hkv * c6.L     # K and V rows read once per KV head
         gbs = nbytes / (avg * 1e-3) / 1e9
@@ -467,7 +475,7 @@ def main():
                                                   out=o6)
         fp6()
         torch.cuda.synchronize()
-        _r = measure(fp6, torch, samples=args.secondary_samples)
+        _r = measure(fp6, torch, "v2_decode_paged", samples=args.secondary_samples)
         avg, mn = _r["median"], _r["min"]
         gbs = nbytes / (avg * 1e-3) / 1e9
         secondary["v2_decode_64k_paged"] = {"workload": c6.name + f", {PAGE_SIZE}-token pages",
