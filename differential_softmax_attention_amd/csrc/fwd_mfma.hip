@@ -98,7 +98,10 @@ template <int D, bool V2, bool CAUSAL, bool EPI, bool F8 = false, bool LAMF = fa
 __global__ __launch_bounds__(V2 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(V2 ? 1 : 2, 2)))
 void fwd_mfma_kernel(MfmaFwdArgs a) {
     using C = Cfg<D, V2, F8>;
-    extern __shared__ __align__(16) unsigned char smem[];
+    // a static allocation: its address is a compile-time constant, so each LDS operand address is a
+    // lane offset plus an immediate (an extern array's base is a link-time symbol, added to every
+    // address with a VALU instruction)
+    __shared__ __align__(16) unsigned char smem[C::NSTAGE * C::STAGE_BYTES + C::Q2_BYTES];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -615,7 +618,7 @@ hipError_t launch_fwd(const MfmaFwdArgs& a, hipStream_t stream) {
     const int n_units = V2 ? a.batch * (a.heads * 2 / a.kv_group) : a.batch * a.heads;
     const int nqt = (a.seq_q + BM - 1) / BM;
     const dim3 grid((unsigned)(nqt * n_units));
-    const size_t smem = C::NSTAGE * C::STAGE_BYTES + C::Q2_BYTES;
+    const size_t smem = 0;   // the kernel's LDS is static
     if (!V2 && !F8 && a.lq1) {   // lambda from its vectors inside the kernel
         if (a.causal) {
             if (a.epi) hipLaunchKernelGGL((fwd_mfma_kernel<D, V2, true, true, F8, true>), grid, dim3(C::NT), smem, stream, a);
