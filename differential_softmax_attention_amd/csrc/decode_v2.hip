@@ -80,26 +80,31 @@ __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
     // 64 w + i of the slice), so that a tile's lookup is a lane read rather than a memory load
     // with its latency in front of the tile's DMA
     const int first_slot = paged ? ks / a.pc.page_size : 0;
+    const int last_slot = paged ? (ke - 1) / a.pc.page_size : 0;
     int win = -1, pvec = 0;
-    auto page_of = [&](int t0) __attribute__((always_inline)) -> int64_t {
-        const int slot = t0 / a.pc.page_size - first_slot;
-        if ((slot >> 6) != win) {
-            win = slot >> 6;
-            const int sl = first_slot + win * 64 + lane;
-            const int p = sl <= (ke - 1) / a.pc.page_size ? a.pc.block_table[(int64_t)b * a.pc.bt_stride + sl] : 0;
-            pvec = min(max(p, 0), a.pc.num_pages - 1);
-        }
-        return (int64_t)__builtin_amdgcn_readlane(pvec, slot & 63);
-    };
+    // tiles are issued in order, so the next tile's page slot (relative to first_slot) and first
+    // row within the page advance by one tile at a time: no division per tile (the page size and
+    // the slice start are multiples of the 32-key tile)
+    int next_slot = 0, next_in = paged ? ks - first_slot * a.pc.page_size : 0;
     auto issue_tile = [&](int t) __attribute__((always_inline)) {
         const uint32_t st = lds0 + (t % kStages) * kStageBytes;
         const int last = min(kBN, ke - ks - t * kBN) - 1;   // last valid row of this tile
         const bf16 *kb, *vb;
         if (paged) {
-            const int t0 = ks + t * kBN;
-            const int64_t pg = page_of(t0), in = t0 % a.pc.page_size;
+            if ((next_slot >> 6) != win) {
+                win = next_slot >> 6;
+                const int sl = first_slot + win * 64 + lane;
+                const int p = sl <= last_slot ? a.pc.block_table[(int64_t)b * a.pc.bt_stride + sl] : 0;
+                pvec = min(max(p, 0), a.pc.num_pages - 1);
+            }
+            const int64_t pg = __builtin_amdgcn_readlane(pvec, next_slot & 63), in = next_in;
             kb = kbase + pg * a.kcs[0] + in * a.kcs[1];
             vb = vbase + pg * a.vcs[0] + in * a.vcs[1];
+            next_in += kBN;
+            if (next_in == a.pc.page_size) {
+                next_in = 0;
+                ++next_slot;
+            }
         } else {
             kb = kbase + (int64_t)t * kBN * a.kcs[1];
             vb = vbase + (int64_t)t * kBN * a.vcs[1];
