@@ -246,32 +246,39 @@ __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
 __global__ __launch_bounds__(128) void v2_decode_reduce_kernel(V2DecodeArgs a) {
     const int p = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
     const int G = a.group;
-    float res[2];
+    // the two heads of pair p, merged over the splits in split order in one pass (running maximum,
+    // sum and channel value rescaled when the maximum rises), so that the loads of eight splits of
+    // both heads are in flight together
+    const float* w[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int j = 2 * p + k;   // query head
-        const float* w = a.ws + (((int64_t)b * a.h_kv + j / G) * a.n_splits * G + (j % G)) * kPart;
-        const int64_t stride = (int64_t)G * kPart;   // next split of the same head
-        // an empty slice stored shift -inf, sum 0 and zeros, so it drops out without a branch and
-        // the loads of successive slices are independent
-        float M = -INFINITY;
+        w[k] = a.ws + (((int64_t)b * a.h_kv + j / G) * a.n_splits * G + (j % G)) * kPart;
+    }
+    const int64_t stride = (int64_t)G * kPart;   // next split of the same head
+    float M[2] = {-INFINITY, -INFINITY}, L[2] = {0.f, 0.f}, O[2] = {0.f, 0.f};
 #pragma unroll 8
-        for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, w[s * stride]);
-        float L = 0.f, O = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < a.n_splits; ++s) {
-            const float* ws = w + s * stride;
-            const float f = fast_exp2(ws[0] - M);
-            L = fmaf(ws[1], f, L);
-            O = fmaf(ws[4 + c], f, O);
+    for (int s = 0; s < a.n_splits; ++s) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const float* ws = w[k] + s * stride;
+            const float ms = ws[0], ls = ws[1], os = ws[4 + c];
+            // an empty slice stored shift -inf, sum 0 and zeros: it changes nothing (selected, not
+            // branched, so the loads stay ahead; before the first non-empty slice both shifts are
+            // -inf and their difference NaN, which the selects discard)
+            const bool empty = ms == -INFINITY;
+            const float mn = fmaxf(M[k], ms);
+            const float fo = empty ? 1.f : fast_exp2(M[k] - mn), fs = empty ? 0.f : fast_exp2(ms - mn);
+            L[k] = fmaf(ls, fs, L[k] * fo);
+            O[k] = fmaf(os, fs, O[k] * fo);
+            M[k] = empty ? M[k] : mn;
         }
-        res[k] = O / L;
     }
     const float lam = a.lam_sigmoid ? sigmoid_f32(a.lam[(int64_t)b * a.lam_bs + p]) : a.lam[(int64_t)b * a.lam_bs + p];
     float x;
     {
 #pragma clang fp contract(off)
-        x = res[0] - lam * res[1];
+        x = O[0] / L[0] - lam * (O[1] / L[1]);
     }
     bf16* op = (bf16*)a.out + b * a.os[0] + (int64_t)p * a.os[2];
     op[c] = (bf16)x;
