@@ -513,10 +513,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     const bf16x8* bp = m < 48 ? bpA : bpB;
                     const int kb = i >> 3, jj = i & 7;
                     if (jj < 4) {
-                        if (jj & 1) mfma_agpr(dk2[jj >> 1], op[m], b2[kb]);
-                        else mfma_agpr(dk1[jj >> 1], op[m], b1[kb]);
+                        if (jj & 1) mfma_agpr_ready(dk2[jj >> 1], op[m], b2[kb]);
+                        else mfma_agpr_ready(dk1[jj >> 1], op[m], b1[kb]);
                     } else {
-                        mfma_agpr(dv[jj - 4], op[m], bp[kb]);
+                        mfma_agpr_ready(dv[jj - 4], op[m], bp[kb]);
                     }
                 }
             };

@@ -61,6 +61,13 @@ __device__ __forceinline__ bf16x8 c_to_b(const f32x16& x, int kb) {
 __device__ __forceinline__ void mfma_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// The same without the two wait states, for the fixed-order pair loops, where each B operand is
+// packed by the vector work of an earlier step, many instructions ahead of its first MFMA; the
+// wait-state check of the product's gfx950 assembly covers every such site (and fails the build's
+// CPU tests if a schedule ever puts the writing instruction closer).
+__device__ __forceinline__ void mfma_agpr_ready(f32x16& acc, bf16x8 a, bf16x8 b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
 // Wait states between the last such MFMA and VALU reads of its accumulator (more than the 18 the
 // longest MFMA needs).
 __device__ __forceinline__ void agpr_drain(f32x16& x0, f32x16& x1, f32x16& x2, f32x16& x3) {

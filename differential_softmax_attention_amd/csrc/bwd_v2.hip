@@ -248,8 +248,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     }
                 } else {
                     const int i = m < 64 ? m - 48 : m - 64, kb = i >> 3, mt = (i >> 1) & 3;
-                    if (i & 1) mfma_agpr(dq2[mt], o, m < 64 ? b2A[kb] : b2B[kb]);
-                    else mfma_agpr(dq1[mt], o, m < 64 ? b1A[kb] : b1B[kb]);
+                    if (i & 1) mfma_agpr_ready(dq2[mt], o, m < 64 ? b2A[kb] : b2B[kb]);
+                    else mfma_agpr_ready(dq1[mt], o, m < 64 ? b1A[kb] : b1B[kb]);
                 }
             };
             // row r of a tile (its 16 registers hold keys k0 + 8 (r / 4) + 4 h2 + r % 4)
@@ -444,10 +444,16 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
         else if (!(i & 1)) s1 = mfma32x32x16(o, kr[(i - 8) >> 1], s1);
         else s2 = mfma32x32x16(o, kr[(i - 8) >> 1], s2);
     };
-    auto mfma_g = [&](int i, bf16x8 o, bf16x8 b1, bf16x8 b2, bf16x8 bp) __attribute__((always_inline)) {
+    // READY: the fixed-order pair loop, whose operands were packed many instructions earlier
+    auto mfma_g = [&](int i, bf16x8 o, bf16x8 b1, bf16x8 b2, bf16x8 bp, auto READY) __attribute__((always_inline)) {
         const int jj = i % 12;
-        if (jj < 8) mfma_agpr(dk[jj >> 1], o, (jj & 1) ? b2 : b1);
-        else mfma_agpr(dv[jj - 8], o, bp);
+        if constexpr (decltype(READY)::value) {
+            if (jj < 8) mfma_agpr_ready(dk[jj >> 1], o, (jj & 1) ? b2 : b1);
+            else mfma_agpr_ready(dv[jj - 8], o, bp);
+        } else {
+            if (jj < 8) mfma_agpr(dk[jj >> 1], o, (jj & 1) ? b2 : b1);
+            else mfma_agpr(dv[jj - 8], o, bp);
+        }
     };
     // statistics of register row r (query 8 (r / 4) + 4 h2 + r % 4) of a slot's tile
     auto st_lse = [&](int slot, int r) __attribute__((always_inline)) {
@@ -501,7 +507,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
             bp[r >> 3][r & 7] = (bf16)fmaf(nl, p2[r], p1[r]);
         }
 #pragma unroll
-        for (int i = 0; i < 24; ++i) mfma_g(i, rd_g(slot, i), b1[i / 12], b2[i / 12], bp[i / 12]);
+        for (int i = 0; i < 24; ++i) mfma_g(i, rd_g(slot, i), b1[i / 12], b2[i / 12], bp[i / 12], std::false_type{});
     };
     auto item_i0 = [&](int it) { return (qbase + qstep * (it / npair)) * kBN; };
     auto item_full = [&](int i0) { return i0 + kBN <= a.seq && kw0 + kBN <= a.seq && (!a.causal || kw0 + kBN - 1 <= i0); };
@@ -523,8 +529,9 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
             float ds1A[16], ds2A[16], pcA[16], ds1B[16], ds2B[16], pcB[16];
             bf16x8 b1A[2], b2A[2], bpA[2], b1B[2], b2B[2], bpB[2];
             bf16x8 op[96];
-            f32x2 sl[32], sd[32];
-            float sm[32];
+            // statistics of row group g (rows 4 g .. 4 g + 3 of tile A for g < 4, of B after): lse
+            // and D as (map 1, map 2) pairs, two rows per 16-byte read, and lambda of the four rows
+            f32x4 gl[8][2], gd[8][2], gm[8];
             // MFMA m: [0,24) scores of A, [24,48) scores of B, [48,72) gradients of A, [72,96) of B
             auto read_op = [&](int m) __attribute__((always_inline)) {
                 if (m < 24) op[m] = rd_s(sa, m);
@@ -535,19 +542,27 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
             auto issue_mfma = [&](int m) __attribute__((always_inline)) {
                 if (m < 24) mfma_s(m, op[m], dpA, s1A, s2A);
                 else if (m < 48) mfma_s(m - 24, op[m], dpB, s1B, s2B);
-                else if (m < 72) { const int kb = (m - 48) / 12; mfma_g(m - 48, op[m], b1A[kb], b2A[kb], bpA[kb]); }
-                else { const int kb = (m - 72) / 12; mfma_g(m - 72, op[m], b1B[kb], b2B[kb], bpB[kb]); }
+                else if (m < 72) { const int kb = (m - 48) / 12; mfma_g(m - 48, op[m], b1A[kb], b2A[kb], bpA[kb], std::true_type{}); }
+                else { const int kb = (m - 72) / 12; mfma_g(m - 72, op[m], b1B[kb], b2B[kb], bpB[kb], std::true_type{}); }
             };
             // row job j: [0,16) rows of A (beside B's scores), [16,32) rows of B (beside A's
             // gradients); job j follows MFMA 24 + (3 j) / 2; its statistics are read two jobs ahead
-            auto read_row = [&](int j) __attribute__((always_inline)) {
-                const int slot = j < 16 ? sa : sb, r = j & 15;
-                sl[j] = st_lse(slot, r); sd[j] = st_dd(slot, r); sm[j] = st_lam(slot, r);
+            auto read_group = [&](int g) __attribute__((always_inline)) {
+                const int slot = g < 4 ? sa : sb, rg = g & 3;
+                const unsigned char* pl = sq + sto + slot * kStSlot + 64 * rg;
+                gl[g][0] = *(const f32x4*)pl;
+                gl[g][1] = *(const f32x4*)(pl + 16);
+                gd[g][0] = *(const f32x4*)(pl + 256);
+                gd[g][1] = *(const f32x4*)(pl + 256 + 16);
+                gm[g] = *(const f32x4*)(sq + stm + slot * kStSlot + 32 * rg);
             };
             auto job = [&](int j) __attribute__((always_inline)) {
-                const int r = j & 15;
+                const int r = j & 15, g = j >> 2, w = j & 3;
+                const f32x2 lj = {gl[g][w >> 1][2 * (w & 1)], gl[g][w >> 1][2 * (w & 1) + 1]};
+                const f32x2 dj = {gd[g][w >> 1][2 * (w & 1)], gd[g][w >> 1][2 * (w & 1) + 1]};
+                const float mj = gm[g][w];
                 if (j < 16) {
-                    row_math(dpA[r], s1A[r], s2A[r], sl[j], sd[j], sm[j], ds1A[r], ds2A[r], pcA[r]);
+                    row_math(dpA[r], s1A[r], s2A[r], lj, dj, mj, ds1A[r], ds2A[r], pcA[r]);
                     if ((r & 7) == 7) {
                         const int kb = r >> 3;
                         for (int t = 0; t < 8; ++t) {
@@ -555,7 +570,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
                         }
                     }
                 } else {
-                    row_math(dpB[r], s1B[r], s2B[r], sl[j], sd[j], sm[j], ds1B[r], ds2B[r], pcB[r]);
+                    row_math(dpB[r], s1B[r], s2B[r], lj, dj, mj, ds1B[r], ds2B[r], pcB[r]);
                     if ((r & 7) == 7) {
                         const int kb = r >> 3;
                         for (int t = 0; t < 8; ++t) {
@@ -571,12 +586,12 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
                 if (m + kLead < 96) read_op(m + kLead);
                 issue_mfma(m);
                 // jobs after MFMA 24 + floor(3 j / 2): j = 0 at 24, 1 at 25, 2 at 27, 3 at 28, ...
-                if (m == 22) { read_row(0); read_row(1); }
+                if (m == 20) read_group(0);
                 if (m >= 24 && m < 72) {
                     const int u = m - 24;   // u = floor(3 j / 2) has a solution j iff u % 3 != 2
                     if (u % 3 != 2) {
                         const int j = (2 * u + 2) / 3;
-                        if (j + 2 < 32) read_row(j + 2);
+                        if ((j & 3) == 0 && (j >> 2) + 1 < 8) read_group((j >> 2) + 1);
                         job(j);
                     }
                 }
