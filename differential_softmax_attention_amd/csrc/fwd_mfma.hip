@@ -104,7 +104,7 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     __shared__ __align__(16) unsigned char smem[C::NSTAGE * C::STAGE_BYTES + C::Q2_BYTES];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: the tile guards are scalar
     const int lane = tid & 63;
     const int n = lane & 31;   // query column within the wave's 32 rows
     const int h2 = lane >> 5;  // which half of the MFMA k-dimension this lane feeds
@@ -316,6 +316,9 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
         c2a *= a.sq1[sh] * a.sk1[sh];
         c2b *= a.sq2[sh] * a.sk2[sh];
     }
+    // rescale thresholds in raw score units, (m + 8) / c (c > 0); -inf until the first tile
+    const float ic2a = 1.f / c2a, ic2b = 1.f / c2b;
+    float th1 = -INFINITY, th2 = -INFINITY;
 
     if (V2) {
         // this wave's 32 rows of Q_{2p+1} into its LDS region (rows of 16 chunks, swizzled like K;
@@ -408,15 +411,18 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
             t[5] = x[15];
             return fmax_nc(fmax_nc(fmax_nc(t[0], t[1]), t[2]), fmax_nc(fmax_nc(t[3], t[4]), t[5]));
         };
-        float mx1 = tile_max(s1), mx2 = tile_max(s2);
-        mx1 = max_halves(mx1) * c2a;
-        mx2 = max_halves(mx2) * c2b;
-        const bool need = (mx1 > m1 + kRescaleThreshold) || (mx2 > m2 + kRescaleThreshold);
+        // compared in raw score units against the thresholds (m + 8) / c, which change only on a
+        // rescale: no scaling of the maxima on the common path
+        const float rx1 = max_halves(tile_max(s1)), rx2 = max_halves(tile_max(s2));
+        const bool need = (rx1 > th1) || (rx2 > th2);
         if (__builtin_amdgcn_ballot_w64(need)) {
+            const float mx1 = rx1 * c2a, mx2 = rx2 * c2b;
             const float mn1 = fmax_nc(m1, mx1), mn2 = fmax_nc(m2, mx2);
             const float al1 = fast_exp2(m1 - mn1), al2 = fast_exp2(m2 - mn2);
             m1 = mn1;
             m2 = mn2;
+            th1 = (m1 + kRescaleThreshold) * ic2a;
+            th2 = (m2 + kRescaleThreshold) * ic2b;
             la1 *= al1;
             lb1 *= al1;
             la2 *= al2;
