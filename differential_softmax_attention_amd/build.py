@@ -24,8 +24,10 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
           "-I", os.path.join(ROOT, "include")]
 # Per-source additions. The dK/dV backward kernel runs one wave per SIMD with ~320 live
 # registers; left to itself the compiler gives its MFMA accumulators the AGPR form and then
-# copies them to VGPRs around every element-wise step. The VGPR form keeps them in place.
-SOURCE_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "bwd_v2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# copies them to VGPRs around every element-wise step. The VGPR form keeps them in place. The V2
+# decode's output accumulators are scaled by VALU on its rare shift path, which in the AGPR form
+# costs 64 AGPR-to-VGPR copies on every tile.
+SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for src in ("bwd.hip", "bwd_v2.hip", "decode_v2.hip")}
 
 
 def _compile(src: str) -> str:

@@ -9,11 +9,15 @@
 //
 // Split-K: the cache of each (batch, KV head) is cut into n_splits slices; one 64-lane wave
 // streams one slice in 32-key tiles through a private 3-stage LDS ring (global_load_lds, no
-// block barrier). Per tile, S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 head columns,
-// G of them used, k = 128 in eight steps), scaled by scale * log2(e) in fp32, base-2 weights, and
-// O^T += V^T P^T with V^T read by the transposing LDS read. The slice's partial (shift, sum, 128-wide accumulator per head) goes to
-// the workspace; v2_decode_reduce merges the slices of each head in split order (log-sum-exp)
-// and forms O_{2p} - lambda_p O_{2p+1}. No atomics: the result is bitwise reproducible.
+// block barrier). Per tile, S = Q K^T on v_mfma_f32_32x32x16_bf16 (32 head rows, G of them used,
+// x 32 keys, k = 128 in eight steps). The heads are the M dimension so that the 8-row blocks
+// holding no head fall on registers the kernel never touches: a lane carries 4 ceil(G/8) scores
+// (4 for G <= 8), not 16. Scores are scaled by scale * log2(e) in fp32, base-2 weights are rounded
+// to bf16 and staged through a small LDS tile, read back by the transposing LDS read as the A
+// operand of O = P V, whose B operand V comes from the same read of the V tile. The slice's
+// partial (shift, sum, 128-wide accumulator per head) goes to the workspace; v2_decode_reduce
+// merges the slices of each head in split order (log-sum-exp) and forms O_{2p} - lambda_p O_{2p+1}.
+// No atomics: the result is bitwise reproducible.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
@@ -30,14 +34,22 @@ constexpr int kStageBytes = kKBytes + kVBytes;
 constexpr int kStages = 3;
 constexpr int kLoadsK = kKBytes / (64 * 16);  // DMA instructions per lane per K tile (8)
 constexpr int kLoadsV = kVBytes / (64 * 16);
+static_assert(kStages == 3 && kLoadsK + kLoadsV == 16, "the ring's vmcnt waits count 16 loads per tile, 3 stages");
 constexpr int kPart = 4 + kD;                 // shift, sum, two pad words, o[128]
-constexpr int kMaxGroup = 32;                 // heads per group that fit the MFMA's N = 32
+constexpr int kMaxGroup = 32;                 // heads per group that fit the MFMA's M = 32
+constexpr int kPRow = 72;                     // bytes per key row of the P staging tile: 32 heads + 8 pad
+constexpr int kPBytes = kBN * kPRow;
+template <int V>
+struct StageC { static constexpr int value = V; };
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kMaxSum = 18446744073709551616.0f;  // 2^64: bound on a lane's 16 weights, unshifted
-constexpr float kMaxSumShifted = 32768.0f;          // 2^15: the same bound in shifted mode
-constexpr float kMinSum = 8.673617379884035e-19f;   // 2^-60: a column below this has no weight yet
+constexpr float kMaxLog2 = 64.0f;                   // unshifted weights stay below 2^64
+constexpr float kMaxLog2Shifted = 15.0f;            // shifted weights below 2^15
+constexpr float kMinSum = 8.673617379884035e-19f;   // 2^-60: a head whose lane sums are all below this has no weight yet
 constexpr float kUnshiftedRange = 60.0f;            // first-tile maxima within +-60 (base 2)
 
+// RB = ceil(G / 8): the 8-row blocks of the 32-row MFMA tiles that hold the group's heads
+template <int RB>
 __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -52,7 +64,7 @@ __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
     const int ke = min(ks + a.split_len, len);
     const int ntiles = ke > ks ? (ke - ks + kBN - 1) / kBN : 0;
 
-    // ---- Q fragments (B operand of S^T = K Q^T): lane (n, h2) holds q[head n][16kk + 8h2 .. +7]
+    // ---- Q fragments (A operand of S = Q K^T): lane (n, h2) holds q[head n][16kk + 8h2 .. +7]
     //      as given, zero for columns past the group; the scale is applied to the fp32 scores.
     bf16x8 bq[kD / 16];
     {
@@ -86,8 +98,21 @@ __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
     // row within the page advance by one tile at a time: no division per tile (the page size and
     // the slice start are multiples of the 32-key tile)
     int next_slot = 0, next_in = paged ? ks - first_slot * a.pc.page_size : 0;
-    auto issue_tile = [&](int t) __attribute__((always_inline)) {
-        const uint32_t st = lds0 + (t % kStages) * kStageBytes;
+    // lane i fills K and V slots i + 64j of a stage (row (i + 64j) / 16, swizzled chunk): byte
+    // offsets within a whole tile
+    uint32_t koffg[kLoadsK], voffg[kLoadsV];
+#pragma unroll
+    for (int j = 0; j < kLoadsK; ++j) {
+        const int s = lane + 64 * j, row = s >> 4;
+        koffg[j] = (uint32_t)(row * a.kcs[1] + ((s & 15) ^ k_swz<kD>(row)) * 8) * 2u;
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadsV; ++j) {
+        const int s = lane + 64 * j, row = s >> 4;
+        voffg[j] = (uint32_t)(row * a.vcs[1] + v_logical(row, s & 15) * 8) * 2u;
+    }
+    auto issue_tile = [&](int t, auto stage_c) __attribute__((always_inline)) {
+        const uint32_t st = lds0 + decltype(stage_c)::value * kStageBytes;
         const int last = min(kBN, ke - ks - t * kBN) - 1;   // last valid row of this tile
         const bf16 *kb, *vb;
         if (paged) {
@@ -109,135 +134,192 @@ __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
             kb = kbase + (int64_t)t * kBN * a.kcs[1];
             vb = vbase + (int64_t)t * kBN * a.vcs[1];
         }
+        if (last == kBN - 1) {
+            // a whole tile: the offsets computed once
 #pragma unroll
-        for (int j = 0; j < kLoadsK; ++j) {
-            const int s = lane + 64 * j;
-            const int row = s >> 4;
-            const int col = (s & 15) ^ k_swz<kD>(row);
-            dma16(kb, (uint32_t)(min(row, last) * a.kcs[1] + col * 8) * 2u, st + j * 1024);
-        }
+            for (int j = 0; j < kLoadsK; ++j) dma16(kb, koffg[j], st + j * 1024);
 #pragma unroll
-        for (int j = 0; j < kLoadsV; ++j) {
-            const int s = lane + 64 * j;
-            const int row = s >> 4;
-            const int col = v_logical(row, s & 15);
-            dma16(vb, (uint32_t)(min(row, last) * a.vcs[1] + col * 8) * 2u, st + kKBytes + j * 1024);
+            for (int j = 0; j < kLoadsV; ++j) dma16(vb, voffg[j], st + kKBytes + j * 1024);
+        } else {
+            // the slice's last tile: rows past its end read the last row
+#pragma unroll
+            for (int j = 0; j < kLoadsK; ++j) {
+                const int s = lane + 64 * j;
+                const int row = s >> 4;
+                const int col = (s & 15) ^ k_swz<kD>(row);
+                dma16(kb, (uint32_t)(min(row, last) * a.kcs[1] + col * 8) * 2u, st + j * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < kLoadsV; ++j) {
+                const int s = lane + 64 * j;
+                const int row = s >> 4;
+                const int col = v_logical(row, s & 15);
+                dma16(vb, (uint32_t)(min(row, last) * a.vcs[1] + col * 8) * 2u, st + kKBytes + j * 1024);
+            }
         }
     };
 
-    // per-lane LDS offsets of the MFMA operands (see the prefill kernels)
+    // per-lane LDS offsets of the MFMA operands: K (B operand of S = Q K^T) row n, chunk
+    // 2kk + h2; V (B operand of O = P V) through the transposing read, lane (n, h2) receiving
+    // channel 32 ct + n of keys 16kb + 4h2 .. +3 and 16kb + 8 + 4h2 .. +3; P (A operand of O) through
+    // the same read from the staging tile, lane (n, h2) receiving head n of those keys
     const int koff0 = n * (kD * 2) + ((h2 ^ k_swz<kD>(n)) * 16);
-    int voff0;
+    int voff0, pr_off;
     {
         const int Gq = lane >> 4, L = lane & 15;
         const int row = 4 * (Gq >> 1) + (L >> 2);
         const int c = (Gq & 1) * 2 + ((L >> 1) & 1);
         voff0 = row * (kD * 2) + v_phys(row, c) * 16 + (L & 1) * 8;
+        pr_off = row * kPRow + ((Gq & 1) * 16 + 4 * (L & 3)) * 2;
     }
+    // P staging tile: [key][head], rows of kPRow bytes; lane (n, h2) writes key n, heads
+    // 8rb + 4h2 .. +3 (8 bytes per row block). Zeroed once: heads past 8 RB are never written and
+    // feed only output rows that are not stored.
+    unsigned char* const ps = smem + kStages * kStageBytes;
+    const int pw_off = n * kPRow + 8 * h2;
+#pragma unroll
+    for (int i = 0; i < kPBytes / 256; ++i) *(uint32_t*)(ps + 4 * (lane + 64 * i)) = 0u;
 
+    // S = Q K^T: lane (n, h2) holds score register 4rb + j = head 8rb + 4h2 + j against key n,
+    // and O = P V the same heads against channel 32 ct + n, so each lane carries only the 4 RB
+    // registers that can hold heads of the group (the other rows of the 32-row tiles stay unused)
+    constexpr int NR = 4 * RB;
     f32x16 o[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) o[ct] = f32x16{};
-    float m = 0.f, l = 0.f;   // shift and this lane's running sum (column n)
+    float m[NR], l[NR];       // per head: shift (equal over the 32 lanes of a half), this lane's sum
+#pragma unroll
+    for (int r = 0; r < NR; ++r) { m[r] = 0.f; l[r] = 0.f; }
     bool shifted = false;
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    // the bf16 pairs {1, 0} and {0, 1} that pick one weight of a packed pair, held in VGPRs: as a
+    // constant, {1, 0} is folded into the inline operand 1.0, whose reading by v_dot2c_f32_bf16
+    // is not the pair the compiler meant
+    uint32_t e_lo_u = 0x00003f80u, e_hi_u = 0x3f800000u;
+    asm volatile("" : "+v"(e_lo_u), "+v"(e_hi_u));
+    const bf16x2 e_lo = __builtin_bit_cast(bf16x2, e_lo_u), e_hi = __builtin_bit_cast(bf16x2, e_hi_u);
+    // maximum over the 32 keys of a tile (the lanes of one half)
+    auto half_max = [&](float v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int msk = 1; msk < 32; msk <<= 1) v = fmax_nc(v, lane_xor(v, (lane ^ msk) << 2));
+        return v;
+    };
 
-    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_tile(t);
-    for (int t = 0; t < ntiles; ++t) {
-        // loads complete in order: tile t+1's loads may stay in flight
-        if (t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
-        else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
-        if (t + kStages - 1 < ntiles) issue_tile(t + kStages - 1);  // into the stage of tile t-1
-        const unsigned char* st = smem + (t % kStages) * kStageBytes;
+    if (0 < ntiles) issue_tile(0, StageC<0>{});
+    if (1 < ntiles) issue_tile(1, StageC<1>{});
+    // one tile in stage S (a constant: the loop is unrolled by the three stages, so every LDS
+    // address is a register plus an immediate)
+    auto tile_step = [&](int t, auto stage_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(stage_c)::value;
+        // tile t+2 goes into the stage of tile t-1, whose operand reads the previous iteration's
+        // MFMAs consumed: issued before the wait, so three tiles are in flight while this wave
+        // waits and two while it computes. Loads complete in order, so the wait for tile t leaves
+        // the later tiles' 16 loads each in flight.
+        if (t + kStages - 1 < ntiles) {
+            issue_tile(t + kStages - 1, StageC<(S + kStages - 1) % kStages>{});
+            __builtin_amdgcn_s_waitcnt(0x8F70);                   // vmcnt(32)
+        } else if (t + 1 < ntiles) {
+            __builtin_amdgcn_s_waitcnt(0x4F70);                   // vmcnt(16)
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+        }
+        const unsigned char* st = smem + S * kStageBytes;
 
         f32x16 s = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < kD / 16; ++kk) s = mfma32x32x16(lds16(st + (koff0 ^ (kk << 5))), bq[kk], s);
+        for (int kk = 0; kk < kD / 16; ++kk) s = mfma32x32x16(bq[kk], lds16(st + (koff0 ^ (kk << 5))), s);
+        float x[NR];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] *= a.scale_log2;   // scores in base-2 units, fp32
-        if (ks + (t + 1) * kBN > ke) {
-            // rows past the slice end were fetched from a clamped address: drop their keys
+        for (int r = 0; r < NR; ++r) x[r] = s[r] * a.scale_log2;   // base-2 units, fp32
+        // keys past the slice end were fetched from a clamped address: drop them
+        if (ks + (t + 1) * kBN > ke && ks + t * kBN + n >= ke) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (ks + t * kBN + (r >> 2) * 8 + h2 * 4 + (r & 3) >= ke) s[r] = -INFINITY;
+            for (int r = 0; r < NR; ++r) x[r] = -INFINITY;
         }
         auto move_shift = [&]() __attribute__((always_inline)) {
-            float mx = s[0];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmax_nc(mx, s[r]);
-            mx = max_halves(mx);
-            if (!(sum_halves(l) < kMinSum)) mx = fmax_nc(mx, 0.f);
-            const float al = fast_exp2(-mx);
-            l *= al;
+            for (int r = 0; r < NR; ++r) {
+                float mx = half_max(x[r]);
+                if (!(half_max(l[r]) < kMinSum)) mx = fmax_nc(mx, 0.f);   // a head with weight keeps its scale or raises it
+                const float al = fast_exp2(-mx);
+                l[r] *= al;
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) o[ct] *= al;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] -= mx;
-            m += mx;
+                for (int ct = 0; ct < 4; ++ct) o[ct][r] *= al;
+                x[r] -= mx;
+                m[r] += mx;
+            }
         };
         if (t == 0) {
-            float mx = s[0];
+            bool out = false;
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmax_nc(mx, s[r]);
-            if (__builtin_amdgcn_ballot_w64(!(fabsf(mx) <= kUnshiftedRange))) {
+            for (int r = 0; r < NR; ++r) out |= !(fabsf(half_max(x[r])) <= kUnshiftedRange);
+            if (__builtin_amdgcn_ballot_w64(out)) {
                 move_shift();
                 shifted = true;
             }
         } else if (shifted) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] -= m;
+            for (int r = 0; r < NR; ++r) x[r] -= m[r];
         }
-        bf16x8 p[2];
-        float ls;
-        auto weights = [&]() __attribute__((always_inline)) {
-            float acc = 0.f;
+        // a weight above the mode's bound moves the shifts first (exact: the shift travels with
+        // the partial)
+        float xm = x[0];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                bf16x2 pp[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = kb * 8 + 2 * j;
-                    pp[j] = bf16x2{(bf16)fast_exp2(s[r]), (bf16)fast_exp2(s[r + 1])};
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, acc, false);
-                }
-                p[kb] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
-                                                __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-            ls = acc;
-        };
-        weights();
-        if (__builtin_amdgcn_ballot_w64(!(ls <= (shifted ? kMaxSumShifted : kMaxSum)))) {
+        for (int r = 1; r < NR; ++r) xm = fmax_nc(xm, x[r]);
+        if (__builtin_amdgcn_ballot_w64(!(xm <= (shifted ? kMaxLog2Shifted : kMaxLog2)))) {
             shifted = true;
             move_shift();
-            weights();
         }
-        l += ls;
+        // weights rounded to bf16, their sums taken from the same bf16 values, staged as P
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            bf16x2 w2[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 4 * rb + 2 * i;
+                w2[i] = bf16x2{(bf16)fast_exp2(x[r]), (bf16)fast_exp2(x[r + 1])};
+                l[r] = __builtin_amdgcn_fdot2_f32_bf16(w2[i], e_lo, l[r], false);
+                l[r + 1] = __builtin_amdgcn_fdot2_f32_bf16(w2[i], e_hi, l[r + 1], false);
+            }
+            *(u32x2*)(ps + pw_off + 16 * rb) = u32x2{__builtin_bit_cast(uint32_t, w2[0]), __builtin_bit_cast(uint32_t, w2[1])};
+        }
+        // O += P V over the tile's two 16-key halves
         const unsigned char* Vs = st + kKBytes;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            const i16x4 plo = lds_read_tr16((const bf16*)(ps + pr_off + kb * 16 * kPRow));
+            const i16x4 phi = lds_read_tr16((const bf16*)(ps + pr_off + (kb * 16 + 8) * kPRow));
+            const bf16x8 pa = __builtin_bit_cast(bf16x8, __builtin_shufflevector(plo, phi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 const bf16* vp = (const bf16*)(Vs + (voff0 ^ (ct << 6)) + kb * 16 * (kD * 2));
                 const i16x4 lo = lds_read_tr16(vp);
                 const i16x4 hi = lds_read_tr16(vp + 8 * kD);
-                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[ct] = mfma32x32x16(va, p[kb], o[ct]);
+                const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[ct] = mfma32x32x16(pa, vb, o[ct]);
             }
         }
+    };
+    for (int t = 0; t < ntiles; t += kStages) {
+        tile_step(t, StageC<0>{});
+        if (t + 1 < ntiles) tile_step(t + 1, StageC<1>{});
+        if (t + 2 < ntiles) tile_step(t + 2, StageC<2>{});
     }
 
     // ---- partial of this slice for each head of the group (an empty slice has no weight)
-    l = sum_halves(l);
-    if (n < G) {
-        float* w = a.ws + ((((int64_t)b * a.h_kv + g) * a.n_splits + split) * G + n) * kPart;
-        if (h2 == 0) {
-            w[0] = ntiles > 0 ? m : -INFINITY;
-            w[1] = l;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int msk = 1; msk < 32; msk <<= 1) l[r] += lane_xor(l[r], (lane ^ msk) << 2);
+        const int head = 8 * (r >> 2) + 4 * h2 + (r & 3);
+        if (head < G) {
+            float* w = a.ws + ((((int64_t)b * a.h_kv + g) * a.n_splits + split) * G + head) * kPart;
+            if (n == 0) {
+                w[0] = ntiles > 0 ? m[r] : -INFINITY;
+                w[1] = l[r];
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) w[4 + ct * 32 + n] = o[ct][r];
         }
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) w[4 + ct * 32 + (r >> 2) * 8 + h2 * 4 + (r & 3)] = o[ct][r];
     }
 }
 
@@ -311,8 +393,15 @@ bool v2_decode_group_ok(int group) { return group >= 2 && group <= kMaxGroup; }
 hipError_t launch_v2_decode(V2DecodeArgs a, hipStream_t stream) {
     a.n_splits = v2_decode_num_splits(a.batch, a.h_kv, a.cache_len);
     a.split_len = v2_decode_split_len(a.cache_len, a.n_splits);
-    hipLaunchKernelGGL(v2_decode_split_kernel, dim3(a.n_splits, a.h_kv, a.batch), dim3(64),
-                       (size_t)kStages * kStageBytes, stream, a);
+    const dim3 grid(a.n_splits, a.h_kv, a.batch);
+    const size_t lds = (size_t)kStages * kStageBytes + kPBytes;
+    switch ((a.group + 7) / 8) {
+        case 1: hipLaunchKernelGGL(v2_decode_split_kernel<1>, grid, dim3(64), lds, stream, a); break;
+        case 2: hipLaunchKernelGGL(v2_decode_split_kernel<2>, grid, dim3(64), lds, stream, a); break;
+        case 3: hipLaunchKernelGGL(v2_decode_split_kernel<3>, grid, dim3(64), lds, stream, a); break;
+        case 4: hipLaunchKernelGGL(v2_decode_split_kernel<4>, grid, dim3(64), lds, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(v2_decode_reduce_kernel, dim3(a.h, a.batch), dim3(kD), 0, stream, a);

@@ -127,3 +127,19 @@ def test_checker_mfma_rules():
     assert H.check(_fn([*asm_mfma, "s_nop 7", "s_nop 7", "s_nop 1", "v_accvgpr_read_b32 v0, a3"]))[0] == []
     # back-to-back accumulation into the same registers needs no wait
     assert H.check(_fn([*asm_mfma, *asm_mfma, "s_nop 7", "s_nop 7", "s_nop 7"]))[0] == []
+
+
+def test_no_inline_float_constant_in_bf16_dot_operands(assembly):
+    """v_dot2c_f32_bf16 reads an inline float constant as that float's 32-bit pattern (1.0 gives the
+    bf16 pair {0, 1}), while the compiler folds the pair {1, 0} into the inline operand 1.0: the
+    selector then picks the other weight of the pair. Packed bf16 operands stay in registers or
+    literals."""
+    bad = []
+    for (src, sched), text in assembly.items():
+        for line in text.splitlines():
+            t = line.strip()
+            if t.startswith(("v_dot2c_f32_bf16", "v_dot2_f32_bf16")):
+                ops = [o.strip() for o in t.split(None, 1)[1].split(",")]
+                if any(re.fullmatch(r"-?\d+\.\d+", o) for o in ops[1:3]):
+                    bad.append(f"[{src}, {sched}] {t}")
+    assert not bad, "\n".join(bad[:10])

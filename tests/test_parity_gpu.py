@@ -291,9 +291,13 @@ def test_v2_generic_fallback():
 # V2 decode
 # ------------------------------------------------------------------------------------------------
 
-def v2_decode_case(B, L, hq, hkv, d, seed, lens=None, dtype=torch.bfloat16, qscale=1.0):
+def v2_decode_case(B, L, hq, hkv, d, seed, lens=None, dtype=torch.bfloat16, qscale=1.0, kramp=None):
     q = rand((B, hq, d), seed, dtype, scale=qscale)
     k = rand((B, L, hkv, d), seed + 1, dtype)
+    if kramp is not None:
+        # key norms growing along the cache by the factor kramp
+        ramp = torch.linspace(1.0, kramp, L, device=k.device).view(1, L, 1, 1)
+        k = (k.float() * ramp).to(dtype)
     v = rand((B, L, hkv, d), seed + 2, dtype)
     g = torch.Generator().manual_seed(seed + 3)
     lam = torch.rand((B, hq // 2), generator=g)
@@ -311,7 +315,7 @@ def test_v2_decode_shapes(L):
     assert maxerr(out, ref) <= TOL_BF16
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (32, 1), (64, 8), (64, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (12, 2), (32, 2), (48, 2), (32, 1), (64, 8), (64, 2)])
 def test_v2_decode_groupings(hq, hkv):
     out, ref = v2_decode_case(2, 700, hq, hkv, 128, 1400 + hq + hkv)
     assert maxerr(out, ref) <= TOL_BF16
@@ -325,6 +329,19 @@ def test_v2_decode_ragged_lengths():
 def test_v2_decode_large_logits():
     # logits far outside +-60 (base 2) put the waves in shifted mode
     out, ref = v2_decode_case(2, 900, 8, 2, 128, 1550, qscale=12.0)
+    assert maxerr(out, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (48, 2)])
+def test_v2_decode_logits_grow_along_the_cache(hq, hkv):
+    # the first tiles' maxima lie within +-60 (base 2), later keys push the weights past the
+    # unshifted bound, so the shifts move in the middle of a slice
+    out, ref = v2_decode_case(2, 4000, hq, hkv, 128, 1570 + hq, kramp=40.0)
+    assert maxerr(out, ref) <= TOL_BF16
+
+
+def test_v2_decode_large_logits_wide_group():
+    out, ref = v2_decode_case(2, 900, 48, 2, 128, 1560, qscale=12.0)
     assert maxerr(out, ref) <= TOL_BF16
 
 
