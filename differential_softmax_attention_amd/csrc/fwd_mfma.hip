@@ -119,11 +119,24 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     int unit, qt;
     {
         const int bid = blockIdx.x;
+        // blocks resident at once on one XCD (32 CUs; two V1 blocks or one V2 block per CU)
+        constexpr int kConc = 32 * (V2 ? 1 : 2);
         if ((n_units & 7) == 0) {
             const int per = n_units >> 3;
             const int slot = bid >> 3;
-            unit = (bid & 7) * per + slot % per;
-            qt = slot / per;
+            if (nqt >= 2 * kConc) {
+                // many query tiles per unit: chunks of kConc consecutive tiles of one unit, the
+                // units' first chunks first, so the blocks resident together on an XCD mostly
+                // stream the same unit's K and V (L2 reuse) while the heavy causal tiles still go
+                // first
+                const int c = slot / (kConc * per), within = slot % (kConc * per);
+                const int cc = min(kConc, nqt - c * kConc);
+                unit = (bid & 7) * per + within / cc;
+                qt = c * kConc + within % cc;
+            } else {
+                unit = (bid & 7) * per + slot % per;
+                qt = slot / per;
+            }
         } else {
             unit = bid % n_units;
             qt = bid / n_units;
