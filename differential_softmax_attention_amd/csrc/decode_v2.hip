@@ -18,6 +18,9 @@
 // partial (shift, sum, 128-wide accumulator per head) goes to the workspace; v2_decode_reduce
 // merges the slices of each head in split order (log-sum-exp) and forms O_{2p} - lambda_p O_{2p+1}.
 // No atomics: the result is bitwise reproducible.
+#include <algorithm>
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_tile.hpp"
@@ -368,12 +371,52 @@ __global__ __launch_bounds__(128) void v2_decode_reduce_kernel(V2DecodeArgs a) {
 
 }  // namespace
 
-int v2_decode_num_splits(int batch, int h_kv, int cache_len) {
-    const int units = batch * h_kv;
-    const int max_splits = (cache_len + 255) / 256;   // at least 256 keys (8 tiles) per slice
-    int splits = (8192 + units - 1) / units;
-    splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
-    int split_len = (cache_len + splits - 1) / splits;
+// Blocks of the split kernel resident at once on the current device (three per CU: the LDS
+// ring), cached per device and row-block count.
+static int v2_decode_capacity(int rb) {
+    static std::atomic<int> cache[64][5];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int c = cache[dev][rb].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const size_t lds = (size_t)kStages * kStageBytes + kPBytes;
+    hipError_t e = hipErrorInvalidValue;
+    switch (rb) {
+        case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v2_decode_split_kernel<1>, 64, lds); break;
+        case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v2_decode_split_kernel<2>, 64, lds); break;
+        case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v2_decode_split_kernel<3>, 64, lds); break;
+        default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v2_decode_split_kernel<4>, 64, lds); break;
+    }
+    if (e != hipSuccess || per_cu <= 0) per_cu = 3;
+    c = cus * per_cu;
+    cache[dev][rb].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+// Slices per (batch, KV head). A block ends with its partial's stores, and its slot takes about
+// one loaded memory round trip (a few tiles' time) to free, so short slices cost; too few blocks
+// leave resident slots idle in the last round. The count minimises rounds x (tiles per slice +
+// kSplitOverheadTiles), with at least 8 tiles per slice.
+constexpr int kSplitOverheadTiles = 4;
+
+int v2_decode_num_splits(int batch, int h_kv, int group, int cache_len) {
+    const int64_t units = (int64_t)batch * h_kv;
+    const int64_t cap = v2_decode_capacity((group + 7) / 8);
+    const int max_splits = std::max(1, std::min((cache_len + 255) / 256, 4096));
+    const int64_t tiles = (cache_len + kBN - 1) / kBN;
+    int best = 1;
+    int64_t best_cost = -1;
+    for (int sp = 1; sp <= max_splits; ++sp) {
+        const int64_t rounds = (units * sp + cap - 1) / cap;
+        const int64_t cost = rounds * ((tiles + sp - 1) / sp + kSplitOverheadTiles);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = sp;
+        }
+    }
+    int split_len = (cache_len + best - 1) / best;
     split_len = (split_len + kBN - 1) / kBN * kBN;
     return (cache_len + split_len - 1) / split_len;
 }
@@ -385,13 +428,13 @@ static int v2_decode_split_len(int cache_len, int splits) {
 
 size_t v2_decode_workspace_bytes(int batch, int h, int h_kv, int cache_len) {
     const int G = 2 * h / h_kv;
-    return (size_t)batch * h_kv * v2_decode_num_splits(batch, h_kv, cache_len) * G * kPart * sizeof(float);
+    return (size_t)batch * h_kv * v2_decode_num_splits(batch, h_kv, G, cache_len) * G * kPart * sizeof(float);
 }
 
 bool v2_decode_group_ok(int group) { return group >= 2 && group <= kMaxGroup; }
 
 hipError_t launch_v2_decode(V2DecodeArgs a, hipStream_t stream) {
-    a.n_splits = v2_decode_num_splits(a.batch, a.h_kv, a.cache_len);
+    a.n_splits = v2_decode_num_splits(a.batch, a.h_kv, a.group, a.cache_len);
     a.split_len = v2_decode_split_len(a.cache_len, a.n_splits);
     const dim3 grid(a.n_splits, a.h_kv, a.batch);
     const size_t lds = (size_t)kStages * kStageBytes + kPBytes;

@@ -118,7 +118,7 @@ struct V2DecodeArgs {
     float scale_log2;
 };
 
-int v2_decode_num_splits(int batch, int h_kv, int cache_len);
+int v2_decode_num_splits(int batch, int h_kv, int group, int cache_len);
 size_t v2_decode_workspace_bytes(int batch, int h, int h_kv, int cache_len);
 bool v2_decode_group_ok(int group);
 hipError_t launch_v2_decode(V2DecodeArgs a, hipStream_t stream);
