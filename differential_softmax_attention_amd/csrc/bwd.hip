@@ -64,41 +64,54 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     float w0 = 1.f, w1 = 1.f;
     if (a.epi && a.norm_w) { w0 = a.norm_w[lane]; w1 = a.norm_w[lane + 64]; }
     float gw0 = 0.f, gw1 = 0.f, glam = 0.f;   // this wave's partial dL/dw (2 channels) and dlambda
-    for (int k = 0; k < kPreRows / 4; ++k) {
-        const int i = blk * kPreRows + wave * (kPreRows / 4) + k;
-        if (i >= a.seq_q) break;
+    // the wave's rows: every load issued first (rows past the end read row 0 and are not used),
+    // so the rows' memory latencies overlap and their reductions interleave
+    constexpr int R = kPreRows / 4;
+    float a1x[R], a1y[R], a2x[R], a2y[R], dy0[R], dy1[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int i = blk * kPreRows + wave * R + k;
+        const int ii = i < a.seq_q ? i : 0;
+        const float* mp = a.maps + (((int64_t)b * a.seq_q + ii) * a.heads + h) * 2 * kDV;
+        a1x[k] = mp[lane];
+        a1y[k] = mp[lane + 64];
+        a2x[k] = mp[kDV + lane];
+        a2y[k] = mp[kDV + lane + 64];
+        const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)ii * a.dos[1] + (int64_t)h * a.dos[2];
+        dy0[k] = (float)dyp[lane];
+        dy1[k] = (float)dyp[lane + 64];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int i = blk * kPreRows + wave * R + k;
+        if (i >= a.seq_q) continue;
         const int64_t row = ((int64_t)b * a.heads + h) * a.seq_q + i;
-        const float* mp = a.maps + (((int64_t)b * a.seq_q + i) * a.heads + h) * 2 * kDV;
-        const float a1x = mp[lane], a1y = mp[lane + 64];
-        const float a2x = mp[kDV + lane], a2y = mp[kDV + lane + 64];
-        const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)i * a.dos[1] + (int64_t)h * a.dos[2];
-        const float dy0 = (float)dyp[lane], dy1 = (float)dyp[lane + 64];
-        float g0 = dy0, g1 = dy1;
+        float g0 = dy0[k], g1 = dy1[k];
         if (a.epi) {
             float o0, o1;
             {
 #pragma clang fp contract(off)
-                o0 = a1x - lam * a2x;
-                o1 = a1y - lam * a2y;
+                o0 = a1x[k] - lam * a2x[k];
+                o1 = a1y[k] - lam * a2y[k];
             }
             const float ms = wave_sum(o0 * o0 + o1 * o1) * (1.f / kDV);
             const float inv = 1.f / sqrtf(ms + a.eps);
             const float u0 = o0 * inv, u1 = o1 * inv;
-            const float du0 = kappa * w0 * dy0, du1 = kappa * w1 * dy1;
+            const float du0 = kappa * w0 * dy0[k], du1 = kappa * w1 * dy1[k];
             const float t = wave_sum(du0 * u0 + du1 * u1) * (1.f / kDV);
             g0 = (du0 - u0 * t) * inv;
             g1 = (du1 - u1 * t) * inv;
-            gw0 += dy0 * kappa * u0;
-            gw1 += dy1 * kappa * u1;
+            gw0 += dy0[k] * kappa * u0;
+            gw1 += dy1[k] * kappa * u1;
         }
         // dlambda takes go in fp32; go enters the MFMA kernels rounded to bf16, and D_k takes the
         // same rounded values, so that each row of dS_k sums to zero as the softmax Jacobian's do
-        glam -= wave_sum(g0 * a2x + g1 * a2y);
+        glam -= wave_sum(g0 * a2x[k] + g1 * a2y[k]);
         const bf16 gb0 = (bf16)g0, gb1 = (bf16)g1;
         g0 = (float)gb0;
         g1 = (float)gb1;
-        const float D1 = wave_sum(g0 * a1x + g1 * a1y);
-        const float D2 = wave_sum(g0 * a2x + g1 * a2y);
+        const float D1 = wave_sum(g0 * a1x[k] + g1 * a1y[k]);
+        const float D2 = wave_sum(g0 * a2x[k] + g1 * a2y[k]);
         bf16* gp = a.go + row * kDV;
         gp[lane] = gb0;
         gp[lane + 64] = gb1;

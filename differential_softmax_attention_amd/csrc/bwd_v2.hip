@@ -56,22 +56,36 @@ constexpr int kDkdvLds = kStOff + kQRing * kStSlot;
 __global__ __launch_bounds__(256) void bwd_v2_pre_kernel(V2BwdArgs a) {
     const int blk = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int k = 0; k < kPreRows / 4; ++k) {
-        const int i = blk * kPreRows + wave * (kPreRows / 4) + k;
-        if (i >= a.seq) break;
+    // the wave's rows: every load issued first (rows past the end read row 0 and are not used)
+    constexpr int R = kPreRows / 4;
+    float a1x[R], a1y[R], a2x[R], a2y[R];
+    bf16 g0[R], g1[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int i = blk * kPreRows + wave * R + k;
+        const int ii = i < a.seq ? i : 0;
+        const int64_t tok = ((int64_t)b * a.seq + ii) * a.h + p;     // token-major (lam, maps)
+        const float* mp = a.maps + tok * 2 * kD;
+        a1x[k] = mp[lane];
+        a1y[k] = mp[lane + 64];
+        a2x[k] = mp[kD + lane];
+        a2y[k] = mp[kD + lane + 64];
+        const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)ii * a.dos[1] + (int64_t)p * a.dos[2];
+        g0[k] = dyp[lane];
+        g1[k] = dyp[lane + 64];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int i = blk * kPreRows + wave * R + k;
+        if (i >= a.seq) continue;
         const int64_t row = ((int64_t)b * a.h + p) * a.seq + i;      // head-major row
         const int64_t tok = ((int64_t)b * a.seq + i) * a.h + p;      // token-major (lam, maps)
-        const float* mp = a.maps + tok * 2 * kD;
-        const float a1x = mp[lane], a1y = mp[lane + 64];
-        const float a2x = mp[kD + lane], a2y = mp[kD + lane + 64];
-        const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)i * a.dos[1] + (int64_t)p * a.dos[2];
-        const bf16 g0 = dyp[lane], g1 = dyp[lane + 64];
-        const float y0 = (float)g0, y1 = (float)g1;
-        const float D1 = wave_sum(y0 * a1x + y1 * a1y);
-        const float D2 = wave_sum(y0 * a2x + y1 * a2y);
+        const float y0 = (float)g0[k], y1 = (float)g1[k];
+        const float D1 = wave_sum(y0 * a1x[k] + y1 * a1y[k]);
+        const float D2 = wave_sum(y0 * a2x[k] + y1 * a2y[k]);
         bf16* gp = a.go + row * kD;
-        gp[lane] = g0;
-        gp[lane + 64] = g1;
+        gp[lane] = g0[k];
+        gp[lane + 64] = g1[k];
         if (lane == 0) {
             const float z = a.lam[tok];
             const float lam = a.lam_sigmoid ? sigmoid_f32(z) : z;

@@ -29,18 +29,37 @@ __device__ __forceinline__ float lane_xor(float x, int addr) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
 }
 
-// Butterfly reductions over all 64 lanes of a wave.
+// x of a partner lane inside the lane's 16-lane row, by DPP (CTRL: 0xB1 lane ^ 1, 0x4E lane ^ 2,
+// 0x141 lane 7 - i within 8, 0x140 lane 15 - i within 16)
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// x combined with x of lane ^ 16 and with x of lane ^ 32 (the gfx950 row swaps)
+template <class F>
+__device__ __forceinline__ float combine_rows(float x, F op) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// Reductions over all 64 lanes of a wave: pairs, quads, the mirrored halves of 8 and of 16 lanes
+// by DPP, then across rows. Each step combines two lanes that are also combined with each other
+// (the operation commutes), so every lane ends with the same value.
 __device__ __forceinline__ float wave_max(float x) {
-    const int l = lane_id();
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, lane_xor(x, (l ^ m) << 2));
-    return x;
+    x = fmaxf(x, dpp_partner<0xB1>(x));
+    x = fmaxf(x, dpp_partner<0x4E>(x));
+    x = fmaxf(x, dpp_partner<0x141>(x));
+    x = fmaxf(x, dpp_partner<0x140>(x));
+    return combine_rows(x, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sum(float x) {
-    const int l = lane_id();
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += lane_xor(x, (l ^ m) << 2);
-    return x;
+    x += dpp_partner<0xB1>(x);
+    x += dpp_partner<0x4E>(x);
+    x += dpp_partner<0x141>(x);
+    x += dpp_partner<0x140>(x);
+    return combine_rows(x, [](float a, float b) { return a + b; });
 }
 
 // 1 / (1 + e^-z): DIFF V2's per-token lambda from its projected logit. Saturates to 0 and 1 for
