@@ -332,6 +332,7 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     // rescale thresholds in raw score units, (m + 8) / c (c > 0); -inf until the first tile
     const float ic2a = 1.f / c2a, ic2b = 1.f / c2b;
     float th1 = -INFINITY, th2 = -INFINITY;
+    bool started = false;   // a rescale has happened (wave-uniform)
 
     if (V2) {
         // this wave's 32 rows of Q_{2p+1} into its LDS region (rows of 16 chunks, swizzled like K;
@@ -440,8 +441,12 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
             lb1 *= al1;
             la2 *= al2;
             lb2 *= al2;
+            // the wave's first rescale finds the accumulators still zero
+            if (started) {
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) { o1[ct] *= al1; o2[ct] *= al2; }
+                for (int ct = 0; ct < 4; ++ct) { o1[ct] *= al1; o2[ct] *= al2; }
+            }
+            started = true;
         }
 
         // Per half of the tile's keys (kb): unnormalised weights exp2(s*c - m) rounded to bf16
@@ -604,14 +609,19 @@ void fwd_mfma_kernel(MfmaFwdArgs a) {
     if (EPI) {
         ss = sum_halves(ss);
         const float inv = (1.f / sqrtf(ss * (1.f / kDV) + a.eps)) * (1.f - a.lambda_init);
+        // the weight test is made once, not per channel
+        if (a.norm_w) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
+            for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = ct * 32 + (r >> 2) * 8 + h2 * 4 + (r & 3);
-                const float w = a.norm_w ? a.norm_w[c] : 1.f;
-                o1[ct][r] *= inv * w;
+                for (int r = 0; r < 16; ++r) {
+                    const int c = ct * 32 + (r >> 2) * 8 + h2 * 4 + (r & 3);
+                    o1[ct][r] *= inv * a.norm_w[c];
+                }
             }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) o1[ct] *= inv;
         }
     }
     if (qrow < a.seq_q) {
