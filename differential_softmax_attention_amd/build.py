@@ -13,8 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffattn.so")
 
-SOURCES = ["diffattn_api.cpp", "generic_kernel.hip", "fwd_mfma.hip", "decode.hip", "decode_v2.hip", "bwd.hip", "bwd_v2.hip", "quant_fp8.hip", "lambda_kernel.hip", "probe.hip"]
-HEADERS = ["common.hpp", "kernels.hpp", "mfma_tile.hpp", "bwd_tile.hpp"]
+SOURCES = ["diffattn_api.cpp", "generic_kernel.hip", "fwd_mfma.hip", "fwd_mfma_long.hip", "decode.hip", "decode_v2.hip", "bwd.hip", "bwd_v2.hip", "quant_fp8.hip", "lambda_kernel.hip", "probe.hip"]
+HEADERS = ["common.hpp", "kernels.hpp", "mfma_tile.hpp", "bwd_tile.hpp", "fwd_mfma_kernel.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -28,6 +28,8 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno
 # decode's output accumulators are scaled by VALU on its rare shift path, which in the AGPR form
 # costs 64 AGPR-to-VGPR copies on every tile.
 SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for src in ("bwd.hip", "bwd_v2.hip", "decode_v2.hip")}
+# The forward kernels a second time under the max-ilp schedule, which the launches use from 4096 keys.
+SOURCE_FLAGS["fwd_mfma_long.hip"] = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 
 
 def _compile(src: str) -> str:

@@ -63,6 +63,11 @@ struct MfmaFwdArgs {
 hipError_t launch_v1_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
 hipError_t launch_v2_fwd_mfma(const MfmaFwdArgs& a, hipStream_t stream);
 hipError_t launch_v1_fwd_fp8(const MfmaFwdArgs& a, hipStream_t stream);
+// the same kernels built under the max-ilp schedule, which the launches above use from kLongKeys keys
+constexpr int kLongKeys = 4096;
+hipError_t launch_v1_fwd_mfma_long(const MfmaFwdArgs& a, hipStream_t stream);
+hipError_t launch_v2_fwd_mfma_long(const MfmaFwdArgs& a, hipStream_t stream);
+hipError_t launch_v1_fwd_fp8_long(const MfmaFwdArgs& a, hipStream_t stream);
 
 // Split-K decode (bf16, d = 64, dv = 128).
 // Paged KV cache (block_table non-null): each cache tensor is a pool of pages whose batch stride

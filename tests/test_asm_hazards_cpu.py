@@ -1,6 +1,7 @@
 """The inline asm of the product meets the CDNA wait-state rules it relies on (tests/asm_hazards.py),
 checked on the gfx950 assembly of every source that contains inline asm, built with the library's
-own flags and again under a different instruction schedule (`-amdgpu-sched-strategy=max-ilp`):
+own flags and again under a different instruction schedule (`-amdgpu-sched-strategy=max-ilp`, or
+max-memory-clause for a source the library already builds under max-ilp):
 the guards must hold wherever the compiler places the surrounding instructions, not only in
 today's schedule. Runs on the CPU (hipcc cross-compiles for gfx950)."""
 import concurrent.futures as cf
@@ -40,13 +41,27 @@ def _asm_sources():
     return out
 
 
-SCHEDULES = {"default": [], "max-ilp": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+SCHEDULES = {"default": [], "other": None}
+
+
+def _schedule_flags(src, sched):
+    """The build's own schedule, or another one: max-ilp, or max-memory-clause for a source that the
+    build already compiles under max-ilp."""
+    if sched == "default":
+        return []
+    own = " ".join(_build_module().SOURCE_FLAGS.get(src, []))
+    strategy = "max-memory-clause" if "sched-strategy=max-ilp" in own else "max-ilp"
+    return ["-mllvm", f"-amdgpu-sched-strategy={strategy}"]
 
 
 def _assemble(src, sched, outdir):
     b = _build_module()
     out = os.path.join(outdir, f"{src}.{sched}.s")
-    cmd = [b.HIPCC, *b.CFLAGS, *b.SOURCE_FLAGS.get(src, []), *SCHEDULES[sched], "--cuda-device-only", "-S",
+    own = b.SOURCE_FLAGS.get(src, [])
+    if sched != "default" and any("sched-strategy" in f for f in own):
+        own = [f for f in own if f != "-mllvm" and "sched-strategy" not in f]
+        own = [x for f in own for x in ("-mllvm", f)]
+    cmd = [b.HIPCC, *b.CFLAGS, *own, *_schedule_flags(src, sched), "--cuda-device-only", "-S",
            os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

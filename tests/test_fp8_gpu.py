@@ -92,6 +92,12 @@ def test_fp8_forward(N, causal, epilogue):
     assert maxerr(out, ref) <= TOL_BF16
 
 
+def test_fp8_forward_long_keys():
+    # 4096 keys and more run the kernels' max-ilp build
+    out, ref = fp8_case(1, 4100, 4100, 1, 7300, True, True)
+    assert maxerr(out, ref) <= TOL_BF16
+
+
 def test_fp8_forward_rectangular_and_large_logits():
     out, ref = fp8_case(1, 70, 200, 3, 7100, True, True)
     assert maxerr(out, ref) <= TOL_BF16

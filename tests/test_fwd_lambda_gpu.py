@@ -33,6 +33,7 @@ def rand(shape, seed, dtype, scale=1.0):
     (129, 2, 64, 128, torch.bfloat16, 2e-2, 200),    # lam_dim past one wave's lanes
     (77, 2, 32, 48, torch.bfloat16, 2e-2, 32),       # generic kernel after the lambda kernel
     (40, 2, 8, 16, torch.float32, 1e-5, 8),
+    (4100, 1, 64, 128, torch.bfloat16, 2e-2, 64),    # 4096 keys and more: the max-ilp build of the kernels
 ])
 def test_fused_lambda_equals_separate_calls(N, H, d, dv, dtype, tol, lam_dim):
     B, layer = 2, 5
