@@ -63,6 +63,12 @@ def kernel_source_hash(files):
     return h.hexdigest()[:16]
 
 
+# the sources each forward build compiles (short keys: the default schedule; 4096 keys and more:
+# the max-ilp build of the same kernels)
+FWD_SOURCES = ["fwd_mfma_kernel.hpp", "fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"]
+FWD_LONG_SOURCES = ["fwd_mfma_kernel.hpp", "fwd_mfma_long.hip", "mfma_tile.hpp", "common.hpp"]
+
+
 def load_traffic(name, files):
     """HBM traffic per launch from committed rocprofv3 PMC summaries, if taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
@@ -225,7 +231,7 @@ def main():
     achieved = flops / (kt["median"] * 1e-3) / 1e12
     log(f"[bench] step {ms_per_step * 1e3:.1f} us; fused forward kernel median {kt['median'] * 1e3:.1f} us, "
         f"min {kt['min'] * 1e3:.1f} us, mean {kt['mean'] * 1e3:.1f} us -> {achieved:.1f} TFLOP/s")
-    traffic = load_traffic("v1_prefill_2k", ["fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"])
+    traffic = load_traffic("v1_prefill_2k", FWD_SOURCES)
 
     result = {
         "metric": METRIC,
@@ -278,8 +284,7 @@ def main():
         secondary["v1_prefill_32k"] = {"workload": c3.name, "kernel_median_ms": round(avg, 4),
                                        "kernel_min_ms": round(mn, 4), "flop": fl3, "TFLOP/s": round(tf, 2),
                                        "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                                       "traffic": load_traffic("v1_prefill_32k",
-                                                               ["fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"])}
+                                       "traffic": load_traffic("v1_prefill_32k", FWD_LONG_SOURCES)}
         log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s")
         del x3, o3
     if "v2" in which:
@@ -297,7 +302,7 @@ def main():
         secondary["v2_gqa_8k"] = {"workload": c5.name, "kernel_median_ms": round(avg, 4), "kernel_min_ms": round(mn, 4),
                                   "flop": fl5, "TFLOP/s": round(tf, 2),
                                   "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                                  "traffic": load_traffic("v2_gqa_8k", ["fwd_mfma.hip", "mfma_tile.hpp", "common.hpp"])}
+                                  "traffic": load_traffic("v2_gqa_8k", FWD_LONG_SOURCES)}
         log(f"[bench]   {avg:.3f} ms -> {tf:.1f} TFLOP/s")
         # lambda from its logits inside the kernel (sigmoid per query row)
         z5 = W.lambda_logits((c5.B, c5.N, c5.hq // 2), seed=c5.seed + 2000, device=dev)

@@ -84,7 +84,7 @@ def assembly(tmp_path_factory):
 
 def test_sources_with_inline_asm_are_found():
     srcs = _asm_sources()
-    for s in ("fwd_mfma.hip", "bwd.hip", "bwd_v2.hip", "decode_v2.hip"):
+    for s in ("fwd_mfma.hip", "fwd_mfma_long.hip", "bwd.hip", "bwd_v2.hip", "decode_v2.hip"):
         assert s in srcs
 
 
