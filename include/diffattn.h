@@ -424,7 +424,8 @@ diffattn_status diffattn_v2_bwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
 /*
  * Bytes of device workspace diffattn_v2_decode needs for these sizes (0 on invalid sizes). The
  * workspace holds, per cache slice and query head, the slice's shift, weight sum and 128-wide
- * accumulator in fp32.
+ * accumulator in fp32. The slice count depends on how many blocks the current device holds at
+ * once (its CU count), so query the size on the device that will run the decode.
  */
 size_t diffattn_v2_decode_workspace_size(int batch, int h, int h_kv, int cache_len);
 
