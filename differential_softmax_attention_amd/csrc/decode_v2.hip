@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
-    const int n = lane & 31;   // head column within the group
+    const int n = lane & 31;   // column of the 32x32 tiles: the key of S, the channel of O; the head of the Q fragment
     const int h2 = lane >> 5;  // which half of the MFMA k-dimension this lane feeds
     const int G = a.group;
 
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64) void v2_decode_split_kernel(V2DecodeArgs a) {
     const int ntiles = ke > ks ? (ke - ks + kBN - 1) / kBN : 0;
 
     // ---- Q fragments (A operand of S = Q K^T): lane (n, h2) holds q[head n][16kk + 8h2 .. +7]
-    //      as given, zero for columns past the group; the scale is applied to the fp32 scores.
+    //      as given, zero for rows past the group; the scale is applied to the fp32 scores.
     bf16x8 bq[kD / 16];
     {
         const bool ok = n < G;
