@@ -193,6 +193,27 @@ def test_v2_decode_workspace_size(L):
     assert 0 < small < big < 64 << 20      # slice partials only
 
 
+def _v2_slices(L, B, h, h_kv, Lc):
+    """Cache slices per (batch, KV head) of the V2 decode, read back from its workspace size: one
+    partial of 132 floats (shift, sum, two pad words, 128 channels) per slice and query head."""
+    G = 2 * h // h_kv
+    ws = L.diffattn_v2_decode_workspace_size(B, h, h_kv, Lc)
+    per = B * h_kv * G * 132 * 4
+    assert ws % per == 0, (ws, per)
+    return ws // per
+
+
+def test_v2_decode_slices_fill_whole_rounds(L):
+    # 768 blocks resident at once (three per CU on a 256-CU device; the size query falls back to
+    # that without a device): the slice count fills whole rounds of them with long slices
+    assert _v2_slices(L, 32, 32, 8, 65536) == 3        # the 64K workload: 768 blocks, one round
+    assert _v2_slices(L, 1, 4, 1, 65536) == 256        # one (batch, KV head): 256 slices of 8 tiles
+    assert _v2_slices(L, 2, 32, 8, 65536) == 48        # 16 units x 48 = 768 blocks
+    for B, h, h_kv, Lc in ((3, 8, 2, 300), (4, 8, 4, 3000), (1, 16, 1, 1), (32, 32, 8, 1000)):
+        n = _v2_slices(L, B, h, h_kv, Lc)
+        assert 1 <= n <= max(1, (Lc + 255) // 256), (B, h, h_kv, Lc, n)   # at least 8 tiles a slice
+
+
 def _bwd(L, B=1, H=2, N=64, d=64, dv=128, dtype=1, lse=FAKE, maps=FAKE, lam=FAKE, ws=FAKE, ws_bytes=1 << 30, epi=1,
          causal=1, Nk=None):
     Nk = N if Nk is None else Nk
