@@ -60,7 +60,7 @@ def test_v1_paged_decode(page):
     assert maxerr(f64(out), ref) <= TOL_BF16
 
 
-@pytest.mark.parametrize("page,hq,hkv", [(32, 16, 4), (128, 16, 4), (64, 64, 8)])
+@pytest.mark.parametrize("page,hq,hkv", [(32, 16, 4), (128, 16, 4), (64, 64, 8), (64, 32, 2), (32, 48, 2)])
 def test_v2_paged_decode(page, hq, hkv):
     B, L = 3, 1500
     lens = [1500, 33, 640]

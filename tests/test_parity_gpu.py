@@ -340,6 +340,14 @@ def test_v2_decode_logits_grow_along_the_cache(hq, hkv):
     assert maxerr(out, ref) <= TOL_BF16
 
 
+def test_v2_decode_many_slices_ragged_tail():
+    # one (batch, KV head) unit per group and a cache that is no multiple of 32: the slice count
+    # rule gives many slices, the last of them ending in a partial tile; a second batch row with a
+    # short length leaves most of its slices empty
+    out, ref = v2_decode_case(2, 40001, 16, 2, 128, 1580, lens=[40001, 700])
+    assert maxerr(out, ref) <= TOL_BF16
+
+
 def test_v2_decode_large_logits_wide_group():
     out, ref = v2_decode_case(2, 900, 48, 2, 128, 1560, qscale=12.0)
     assert maxerr(out, ref) <= TOL_BF16
