@@ -42,7 +42,7 @@ constexpr int kD = 64;
 constexpr int kDV = 128;
 constexpr int kKTile = kBN * kD * 2;    // bytes of one 32-row, 64-wide tile
 constexpr int kVTile = kBN * kDV * 2;   // bytes of one 32-row, 128-wide tile
-constexpr int kPreRows = 16;            // rows per bwd_pre block (4 waves x 4 rows)
+constexpr int kPreRows = 64;            // rows per bwd_pre block (4 waves x 16 rows)
 // dK/dV query-tile stage: Q1 | Q2 (64 wide) | go (128 wide) | lse [32][2] | dd [32][2]
 constexpr int kQStats = 2 * kKTile + kVTile;
 constexpr int kQStage = kQStats + 2 * kBN * 2 * 4;
