@@ -64,61 +64,72 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     float w0 = 1.f, w1 = 1.f;
     if (a.epi && a.norm_w) { w0 = a.norm_w[lane]; w1 = a.norm_w[lane + 64]; }
     float gw0 = 0.f, gw1 = 0.f, glam = 0.f;   // this wave's partial dL/dw (2 channels) and dlambda
-    // the wave's rows: every load issued first (rows past the end read row 0 and are not used),
-    // so the rows' memory latencies overlap and their reductions interleave
-    constexpr int R = kPreRows / 4;
-    float a1x[R], a1y[R], a2x[R], a2y[R], dy0[R], dy1[R];
+    // the wave's rows in chunks of four: a chunk's loads are issued while the previous chunk is
+    // reduced (rows past the end read row 0 and are not used)
+    constexpr int R = kPreRows / 4, CH = 4;
+    struct Chunk { float a1x[CH], a1y[CH], a2x[CH], a2y[CH], dy0[CH], dy1[CH]; };
+    auto load_chunk = [&](int c, Chunk& r) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const int i = blk * kPreRows + wave * R + k;
-        const int ii = i < a.seq_q ? i : 0;
-        const float* mp = a.maps + (((int64_t)b * a.seq_q + ii) * a.heads + h) * 2 * kDV;
-        a1x[k] = mp[lane];
-        a1y[k] = mp[lane + 64];
-        a2x[k] = mp[kDV + lane];
-        a2y[k] = mp[kDV + lane + 64];
-        const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)ii * a.dos[1] + (int64_t)h * a.dos[2];
-        dy0[k] = (float)dyp[lane];
-        dy1[k] = (float)dyp[lane + 64];
-    }
+        for (int k = 0; k < CH; ++k) {
+            const int i = blk * kPreRows + wave * R + c * CH + k;
+            const int ii = i < a.seq_q ? i : 0;
+            const float* mp = a.maps + (((int64_t)b * a.seq_q + ii) * a.heads + h) * 2 * kDV;
+            r.a1x[k] = mp[lane];
+            r.a1y[k] = mp[lane + 64];
+            r.a2x[k] = mp[kDV + lane];
+            r.a2y[k] = mp[kDV + lane + 64];
+            const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)ii * a.dos[1] + (int64_t)h * a.dos[2];
+            r.dy0[k] = (float)dyp[lane];
+            r.dy1[k] = (float)dyp[lane + 64];
+        }
+    };
+    auto reduce_chunk = [&](int c, const Chunk& r) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const int i = blk * kPreRows + wave * R + k;
-        if (i >= a.seq_q) continue;
-        const int64_t row = ((int64_t)b * a.heads + h) * a.seq_q + i;
-        float g0 = dy0[k], g1 = dy1[k];
-        if (a.epi) {
-            float o0, o1;
-            {
+        for (int k = 0; k < CH; ++k) {
+            const int i = blk * kPreRows + wave * R + c * CH + k;
+            if (i >= a.seq_q) continue;
+            const int64_t row = ((int64_t)b * a.heads + h) * a.seq_q + i;
+            float g0 = r.dy0[k], g1 = r.dy1[k];
+            if (a.epi) {
+                float o0, o1;
+                {
 #pragma clang fp contract(off)
-                o0 = a1x[k] - lam * a2x[k];
-                o1 = a1y[k] - lam * a2y[k];
+                    o0 = r.a1x[k] - lam * r.a2x[k];
+                    o1 = r.a1y[k] - lam * r.a2y[k];
+                }
+                const float ms = wave_sum(o0 * o0 + o1 * o1) * (1.f / kDV);
+                const float inv = 1.f / sqrtf(ms + a.eps);
+                const float u0 = o0 * inv, u1 = o1 * inv;
+                const float du0 = kappa * w0 * r.dy0[k], du1 = kappa * w1 * r.dy1[k];
+                const float t = wave_sum(du0 * u0 + du1 * u1) * (1.f / kDV);
+                g0 = (du0 - u0 * t) * inv;
+                g1 = (du1 - u1 * t) * inv;
+                gw0 += r.dy0[k] * kappa * u0;
+                gw1 += r.dy1[k] * kappa * u1;
             }
-            const float ms = wave_sum(o0 * o0 + o1 * o1) * (1.f / kDV);
-            const float inv = 1.f / sqrtf(ms + a.eps);
-            const float u0 = o0 * inv, u1 = o1 * inv;
-            const float du0 = kappa * w0 * dy0[k], du1 = kappa * w1 * dy1[k];
-            const float t = wave_sum(du0 * u0 + du1 * u1) * (1.f / kDV);
-            g0 = (du0 - u0 * t) * inv;
-            g1 = (du1 - u1 * t) * inv;
-            gw0 += dy0[k] * kappa * u0;
-            gw1 += dy1[k] * kappa * u1;
+            // dlambda takes go in fp32; go enters the MFMA kernels rounded to bf16, and D_k takes the
+            // same rounded values, so that each row of dS_k sums to zero as the softmax Jacobian's do
+            glam -= wave_sum(g0 * r.a2x[k] + g1 * r.a2y[k]);
+            const bf16 gb0 = (bf16)g0, gb1 = (bf16)g1;
+            g0 = (float)gb0;
+            g1 = (float)gb1;
+            const float D1 = wave_sum(g0 * r.a1x[k] + g1 * r.a1y[k]);
+            const float D2 = wave_sum(g0 * r.a2x[k] + g1 * r.a2y[k]);
+            bf16* gp = a.go + row * kDV;
+            gp[lane] = gb0;
+            gp[lane + 64] = gb1;
+            if (lane == 0) {
+                a.dd[2 * row] = D1;
+                a.dd[2 * row + 1] = D2;
+            }
         }
-        // dlambda takes go in fp32; go enters the MFMA kernels rounded to bf16, and D_k takes the
-        // same rounded values, so that each row of dS_k sums to zero as the softmax Jacobian's do
-        glam -= wave_sum(g0 * a2x[k] + g1 * a2y[k]);
-        const bf16 gb0 = (bf16)g0, gb1 = (bf16)g1;
-        g0 = (float)gb0;
-        g1 = (float)gb1;
-        const float D1 = wave_sum(g0 * a1x[k] + g1 * a1y[k]);
-        const float D2 = wave_sum(g0 * a2x[k] + g1 * a2y[k]);
-        bf16* gp = a.go + row * kDV;
-        gp[lane] = gb0;
-        gp[lane + 64] = gb1;
-        if (lane == 0) {
-            a.dd[2 * row] = D1;
-            a.dd[2 * row + 1] = D2;
-        }
+    };
+    Chunk buf[2];
+    load_chunk(0, buf[0]);
+#pragma unroll
+    for (int c = 0; c < R / CH; ++c) {
+        if (c + 1 < R / CH) load_chunk(c + 1, buf[(c + 1) & 1]);
+        reduce_chunk(c, buf[c & 1]);
     }
     // block partials in a fixed order: waves 0..3
     __shared__ float sw[4][kDV];
