@@ -40,7 +40,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kTile = kBN * kD * 2;          // bytes of one 32-row, 128-wide tile
-constexpr int kPreRows = 16;                 // rows per pre block (4 waves x 4 rows)
+constexpr int kPreRows = 64;                 // rows per pre block (4 waves x 16 rows)
 // dQ key-tile stage: K | V
 constexpr int kKStage = 2 * kTile;
 // dK/dV LDS by operand type, four ring slots per region: Q_{2p} | Q_{2p+1} | go_p | statistics
@@ -56,45 +56,56 @@ constexpr int kDkdvLds = kStOff + kQRing * kStSlot;
 __global__ __launch_bounds__(256) void bwd_v2_pre_kernel(V2BwdArgs a) {
     const int blk = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // the wave's rows: every load issued first (rows past the end read row 0 and are not used)
-    constexpr int R = kPreRows / 4;
-    float a1x[R], a1y[R], a2x[R], a2y[R];
-    bf16 g0[R], g1[R];
+    // the wave's rows in chunks of four: a chunk's loads are issued while the previous chunk is
+    // reduced (rows past the end read row 0 and are not used)
+    constexpr int R = kPreRows / 4, CH = 4;
+    struct Chunk { float a1x[CH], a1y[CH], a2x[CH], a2y[CH]; bf16 g0[CH], g1[CH]; };
+    auto load_chunk = [&](int c, Chunk& r) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const int i = blk * kPreRows + wave * R + k;
-        const int ii = i < a.seq ? i : 0;
-        const int64_t tok = ((int64_t)b * a.seq + ii) * a.h + p;     // token-major (lam, maps)
-        const float* mp = a.maps + tok * 2 * kD;
-        a1x[k] = mp[lane];
-        a1y[k] = mp[lane + 64];
-        a2x[k] = mp[kD + lane];
-        a2y[k] = mp[kD + lane + 64];
-        const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)ii * a.dos[1] + (int64_t)p * a.dos[2];
-        g0[k] = dyp[lane];
-        g1[k] = dyp[lane + 64];
-    }
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const int i = blk * kPreRows + wave * R + k;
-        if (i >= a.seq) continue;
-        const int64_t row = ((int64_t)b * a.h + p) * a.seq + i;      // head-major row
-        const int64_t tok = ((int64_t)b * a.seq + i) * a.h + p;      // token-major (lam, maps)
-        const float y0 = (float)g0[k], y1 = (float)g1[k];
-        const float D1 = wave_sum(y0 * a1x[k] + y1 * a1y[k]);
-        const float D2 = wave_sum(y0 * a2x[k] + y1 * a2y[k]);
-        bf16* gp = a.go + row * kD;
-        gp[lane] = g0[k];
-        gp[lane + 64] = g1[k];
-        if (lane == 0) {
-            const float z = a.lam[tok];
-            const float lam = a.lam_sigmoid ? sigmoid_f32(z) : z;
-            const float dl = -D2;
-            a.dlam[tok] = a.lam_sigmoid ? dl * lam * (1.f - lam) : dl;
-            a.lamr[row] = lam;
-            a.dd[2 * row] = D1;
-            a.dd[2 * row + 1] = D2;
+        for (int k = 0; k < CH; ++k) {
+            const int i = blk * kPreRows + wave * R + c * CH + k;
+            const int ii = i < a.seq ? i : 0;
+            const int64_t tok = ((int64_t)b * a.seq + ii) * a.h + p;     // token-major (lam, maps)
+            const float* mp = a.maps + tok * 2 * kD;
+            r.a1x[k] = mp[lane];
+            r.a1y[k] = mp[lane + 64];
+            r.a2x[k] = mp[kD + lane];
+            r.a2y[k] = mp[kD + lane + 64];
+            const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)ii * a.dos[1] + (int64_t)p * a.dos[2];
+            r.g0[k] = dyp[lane];
+            r.g1[k] = dyp[lane + 64];
         }
+    };
+    auto reduce_chunk = [&](int c, const Chunk& r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int i = blk * kPreRows + wave * R + c * CH + k;
+            if (i >= a.seq) continue;
+            const int64_t row = ((int64_t)b * a.h + p) * a.seq + i;      // head-major row
+            const int64_t tok = ((int64_t)b * a.seq + i) * a.h + p;      // token-major (lam, maps)
+            const float y0 = (float)r.g0[k], y1 = (float)r.g1[k];
+            const float D1 = wave_sum(y0 * r.a1x[k] + y1 * r.a1y[k]);
+            const float D2 = wave_sum(y0 * r.a2x[k] + y1 * r.a2y[k]);
+            bf16* gp = a.go + row * kD;
+            gp[lane] = r.g0[k];
+            gp[lane + 64] = r.g1[k];
+            if (lane == 0) {
+                const float z = a.lam[tok];
+                const float lam = a.lam_sigmoid ? sigmoid_f32(z) : z;
+                const float dl = -D2;
+                a.dlam[tok] = a.lam_sigmoid ? dl * lam * (1.f - lam) : dl;
+                a.lamr[row] = lam;
+                a.dd[2 * row] = D1;
+                a.dd[2 * row + 1] = D2;
+            }
+        }
+    };
+    Chunk buf[2];
+    load_chunk(0, buf[0]);
+#pragma unroll
+    for (int c = 0; c < R / CH; ++c) {
+        if (c + 1 < R / CH) load_chunk(c + 1, buf[(c + 1) & 1]);
+        reduce_chunk(c, buf[c & 1]);
     }
 }
 
