@@ -59,83 +59,101 @@ __device__ __forceinline__ int trop_v(int lane, int kb, int ct, int hi) { return
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // a wave takes its rows two at a time: lanes 0-31 one row, lanes 32-63 the next, each lane
+    // the four channels c0 .. c0 + 3 (16-byte map loads, 8-byte dout loads and go stores)
+    const int hl = lane >> 5, c0 = 4 * (lane & 31);
     const float lam = a.lam[h];
     const float kappa = 1.f - a.lambda_init;
-    float w0 = 1.f, w1 = 1.f;
-    if (a.epi && a.norm_w) { w0 = a.norm_w[lane]; w1 = a.norm_w[lane + 64]; }
-    float gw0 = 0.f, gw1 = 0.f, glam = 0.f;   // this wave's partial dL/dw (2 channels) and dlambda
-    // the wave's rows in chunks of four: a chunk's loads are issued while the previous chunk is
-    // reduced (rows past the end read row 0 and are not used)
-    constexpr int R = kPreRows / 4, CH = 4;
-    struct Chunk { float a1x[CH], a1y[CH], a2x[CH], a2y[CH], dy0[CH], dy1[CH]; };
+    float w[4] = {1.f, 1.f, 1.f, 1.f};
+    if (a.epi && a.norm_w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = a.norm_w[c0 + j];
+    float gw[4] = {0.f, 0.f, 0.f, 0.f}, glam = 0.f;   // partial dL/dw (4 channels) and dlambda
+    // steps of two rows in chunks of two steps: a chunk's loads are issued while the previous
+    // chunk is reduced (rows past the end read row 0 and are not used)
+    constexpr int R = kPreRows / 4, CH = 2, NC = R / (2 * CH);
+    struct Chunk { f32x4 a1[CH], a2[CH]; bf16x4 dy[CH]; };
+    auto row_of = [&](int c, int k) { return blk * kPreRows + wave * R + 2 * (c * CH + k) + hl; };
     auto load_chunk = [&](int c, Chunk& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
-            const int i = blk * kPreRows + wave * R + c * CH + k;
+            const int i = row_of(c, k);
             const int ii = i < a.seq_q ? i : 0;
             const float* mp = a.maps + (((int64_t)b * a.seq_q + ii) * a.heads + h) * 2 * kDV;
-            r.a1x[k] = mp[lane];
-            r.a1y[k] = mp[lane + 64];
-            r.a2x[k] = mp[kDV + lane];
-            r.a2y[k] = mp[kDV + lane + 64];
+            r.a1[k] = *(const f32x4*)(mp + c0);
+            r.a2[k] = *(const f32x4*)(mp + kDV + c0);
             const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)ii * a.dos[1] + (int64_t)h * a.dos[2];
-            r.dy0[k] = (float)dyp[lane];
-            r.dy1[k] = (float)dyp[lane + 64];
+            r.dy[k] = *(const bf16x4*)(dyp + c0);
         }
     };
     auto reduce_chunk = [&](int c, const Chunk& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
-            const int i = blk * kPreRows + wave * R + c * CH + k;
-            if (i >= a.seq_q) continue;
-            const int64_t row = ((int64_t)b * a.heads + h) * a.seq_q + i;
-            float g0 = r.dy0[k], g1 = r.dy1[k];
+            const int i = row_of(c, k);
+            const bool ok = i < a.seq_q;   // the half-wave sums run on every lane; only valid rows count
+            float dy[4], g[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dy[j] = (float)r.dy[k][j];
             if (a.epi) {
-                float o0, o1;
+                float o[4];
                 {
 #pragma clang fp contract(off)
-                    o0 = r.a1x[k] - lam * r.a2x[k];
-                    o1 = r.a1y[k] - lam * r.a2y[k];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = r.a1[k][j] - lam * r.a2[k][j];
                 }
-                const float ms = wave_sum(o0 * o0 + o1 * o1) * (1.f / kDV);
+                const float ms = half_sum((o[0] * o[0] + o[1] * o[1]) + (o[2] * o[2] + o[3] * o[3])) * (1.f / kDV);
                 const float inv = 1.f / sqrtf(ms + a.eps);
-                const float u0 = o0 * inv, u1 = o1 * inv;
-                const float du0 = kappa * w0 * r.dy0[k], du1 = kappa * w1 * r.dy1[k];
-                const float t = wave_sum(du0 * u0 + du1 * u1) * (1.f / kDV);
-                g0 = (du0 - u0 * t) * inv;
-                g1 = (du1 - u1 * t) * inv;
-                gw0 += r.dy0[k] * kappa * u0;
-                gw1 += r.dy1[k] * kappa * u1;
+                float u[4], du[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u[j] = o[j] * inv;
+                    du[j] = kappa * w[j] * dy[j];
+                }
+                const float t = half_sum((du[0] * u[0] + du[1] * u[1]) + (du[2] * u[2] + du[3] * u[3])) * (1.f / kDV);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    g[j] = (du[j] - u[j] * t) * inv;
+                    if (ok) gw[j] += dy[j] * kappa * u[j];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) g[j] = dy[j];
             }
             // dlambda takes go in fp32; go enters the MFMA kernels rounded to bf16, and D_k takes the
             // same rounded values, so that each row of dS_k sums to zero as the softmax Jacobian's do
-            glam -= wave_sum(g0 * r.a2x[k] + g1 * r.a2y[k]);
-            const bf16 gb0 = (bf16)g0, gb1 = (bf16)g1;
-            g0 = (float)gb0;
-            g1 = (float)gb1;
-            const float D1 = wave_sum(g0 * r.a1x[k] + g1 * r.a1y[k]);
-            const float D2 = wave_sum(g0 * r.a2x[k] + g1 * r.a2y[k]);
-            bf16* gp = a.go + row * kDV;
-            gp[lane] = gb0;
-            gp[lane + 64] = gb1;
-            if (lane == 0) {
-                a.dd[2 * row] = D1;
-                a.dd[2 * row + 1] = D2;
+            const float gl = half_sum((g[0] * r.a2[k][0] + g[1] * r.a2[k][1]) + (g[2] * r.a2[k][2] + g[3] * r.a2[k][3]));
+            if (ok) glam -= gl;
+            bf16x4 gb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                gb[j] = (bf16)g[j];
+                g[j] = (float)gb[j];
+            }
+            const float D1 = half_sum((g[0] * r.a1[k][0] + g[1] * r.a1[k][1]) + (g[2] * r.a1[k][2] + g[3] * r.a1[k][3]));
+            const float D2 = half_sum((g[0] * r.a2[k][0] + g[1] * r.a2[k][1]) + (g[2] * r.a2[k][2] + g[3] * r.a2[k][3]));
+            if (ok) {
+                const int64_t row = ((int64_t)b * a.heads + h) * a.seq_q + i;
+                *(bf16x4*)(a.go + row * kDV + c0) = gb;
+                if ((lane & 31) == 0) *(float2*)(a.dd + 2 * row) = make_float2(D1, D2);
             }
         }
     };
     Chunk buf[2];
     load_chunk(0, buf[0]);
 #pragma unroll
-    for (int c = 0; c < R / CH; ++c) {
-        if (c + 1 < R / CH) load_chunk(c + 1, buf[(c + 1) & 1]);
+    for (int c = 0; c < NC; ++c) {
+        if (c + 1 < NC) load_chunk(c + 1, buf[(c + 1) & 1]);
         reduce_chunk(c, buf[c & 1]);
     }
-    // block partials in a fixed order: waves 0..3
+    // block partials in a fixed order: the two halves of each wave, then waves 0..3
     __shared__ float sw[4][kDV];
     __shared__ float sl[4];
-    sw[wave][lane] = gw0;
-    sw[wave][lane + 64] = gw1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gw[j] = sum_halves(gw[j]);
+    glam = sum_halves(glam);
+    if (hl == 0)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sw[wave][c0 + j] = gw[j];
     if (lane == 0) sl[wave] = glam;
     __syncthreads();
     const int64_t pb = ((int64_t)b * a.heads + h) * gridDim.x + blk;   // partial index

@@ -56,55 +56,55 @@ constexpr int kDkdvLds = kStOff + kQRing * kStSlot;
 __global__ __launch_bounds__(256) void bwd_v2_pre_kernel(V2BwdArgs a) {
     const int blk = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // the wave's rows in chunks of four: a chunk's loads are issued while the previous chunk is
-    // reduced (rows past the end read row 0 and are not used)
-    constexpr int R = kPreRows / 4, CH = 4;
-    struct Chunk { float a1x[CH], a1y[CH], a2x[CH], a2y[CH]; bf16 g0[CH], g1[CH]; };
+    // a wave takes its rows two at a time: lanes 0-31 one row, lanes 32-63 the next, each lane
+    // the four channels c0 .. c0 + 3 (16-byte map loads, 8-byte dout loads and go stores)
+    const int hl = lane >> 5, c0 = 4 * (lane & 31);
+    // steps of two rows in chunks of two steps: a chunk's loads are issued while the previous
+    // chunk is reduced (rows past the end read row 0 and are not used)
+    constexpr int R = kPreRows / 4, CH = 2, NC = R / (2 * CH);
+    struct Chunk { f32x4 a1[CH], a2[CH]; bf16x4 dy[CH]; };
+    auto row_of = [&](int c, int k) { return blk * kPreRows + wave * R + 2 * (c * CH + k) + hl; };
     auto load_chunk = [&](int c, Chunk& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
-            const int i = blk * kPreRows + wave * R + c * CH + k;
+            const int i = row_of(c, k);
             const int ii = i < a.seq ? i : 0;
-            const int64_t tok = ((int64_t)b * a.seq + ii) * a.h + p;     // token-major (lam, maps)
-            const float* mp = a.maps + tok * 2 * kD;
-            r.a1x[k] = mp[lane];
-            r.a1y[k] = mp[lane + 64];
-            r.a2x[k] = mp[kD + lane];
-            r.a2y[k] = mp[kD + lane + 64];
+            const float* mp = a.maps + (((int64_t)b * a.seq + ii) * a.h + p) * 2 * kD;   // token-major
+            r.a1[k] = *(const f32x4*)(mp + c0);
+            r.a2[k] = *(const f32x4*)(mp + kD + c0);
             const bf16* dyp = (const bf16*)a.dout + b * a.dos[0] + (int64_t)ii * a.dos[1] + (int64_t)p * a.dos[2];
-            r.g0[k] = dyp[lane];
-            r.g1[k] = dyp[lane + 64];
+            r.dy[k] = *(const bf16x4*)(dyp + c0);
         }
     };
     auto reduce_chunk = [&](int c, const Chunk& r) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
-            const int i = blk * kPreRows + wave * R + c * CH + k;
+            const int i = row_of(c, k);
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = (float)r.dy[k][j];
+            // the half-wave sums run on every lane; only valid rows are stored
+            const float D1 = half_sum((y[0] * r.a1[k][0] + y[1] * r.a1[k][1]) + (y[2] * r.a1[k][2] + y[3] * r.a1[k][3]));
+            const float D2 = half_sum((y[0] * r.a2[k][0] + y[1] * r.a2[k][1]) + (y[2] * r.a2[k][2] + y[3] * r.a2[k][3]));
             if (i >= a.seq) continue;
             const int64_t row = ((int64_t)b * a.h + p) * a.seq + i;      // head-major row
             const int64_t tok = ((int64_t)b * a.seq + i) * a.h + p;      // token-major (lam, maps)
-            const float y0 = (float)r.g0[k], y1 = (float)r.g1[k];
-            const float D1 = wave_sum(y0 * r.a1x[k] + y1 * r.a1y[k]);
-            const float D2 = wave_sum(y0 * r.a2x[k] + y1 * r.a2y[k]);
-            bf16* gp = a.go + row * kD;
-            gp[lane] = r.g0[k];
-            gp[lane + 64] = r.g1[k];
-            if (lane == 0) {
+            *(bf16x4*)(a.go + row * kD + c0) = r.dy[k];
+            if ((lane & 31) == 0) {
                 const float z = a.lam[tok];
                 const float lam = a.lam_sigmoid ? sigmoid_f32(z) : z;
                 const float dl = -D2;
                 a.dlam[tok] = a.lam_sigmoid ? dl * lam * (1.f - lam) : dl;
                 a.lamr[row] = lam;
-                a.dd[2 * row] = D1;
-                a.dd[2 * row + 1] = D2;
+                *(float2*)(a.dd + 2 * row) = make_float2(D1, D2);
             }
         }
     };
     Chunk buf[2];
     load_chunk(0, buf[0]);
 #pragma unroll
-    for (int c = 0; c < R / CH; ++c) {
-        if (c + 1 < R / CH) load_chunk(c + 1, buf[(c + 1) & 1]);
+    for (int c = 0; c < NC; ++c) {
+        if (c + 1 < NC) load_chunk(c + 1, buf[(c + 1) & 1]);
         reduce_chunk(c, buf[c & 1]);
     }
 }

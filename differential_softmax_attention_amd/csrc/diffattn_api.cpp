@@ -436,6 +436,7 @@ diffattn_status diffattn_v2_bwd(diffattn_dtype dtype, diffattn_tensor q, diffatt
         if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
     if (!lam || !lse || !maps || !dlam)
         return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: lam, lse, maps and dlam must be non-null");
+    if (((uintptr_t)maps) % 16 != 0) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: maps must be 16-byte aligned");
     if (!valid_lam_mode(lam_mode)) return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: unknown lam_mode %d", (int)lam_mode);
     if (batch < 1 || seq < 1 || h < 1 || h_kv < 1 || d < 1)
         return fail(DIFFATTN_ERR_ARG, "diffattn_v2_bwd: sizes must be >= 1 (batch=%d seq=%d h=%d h_kv=%d d=%d)", batch,
@@ -608,6 +609,7 @@ diffattn_status diffattn_bwd(diffattn_dtype dtype, diffattn_tensor q1, diffattn_
     for (int i = 0; i < 11; ++i)
         if (diffattn_status s = check_tensor(*ts[i], names[i], dtype)) return s;
     if (!lambda || !lse || !maps) return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: lambda, lse and maps must be non-null");
+    if (((uintptr_t)maps) % 16 != 0) return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: maps must be 16-byte aligned");
     if (batch < 1 || heads < 1 || seq_q < 1 || seq_k < 1 || d < 1 || dv < 1)
         return fail(DIFFATTN_ERR_ARG, "diffattn_bwd: sizes must be >= 1 (batch=%d heads=%d seq_q=%d seq_k=%d d=%d dv=%d)",
                     batch, heads, seq_q, seq_k, d, dv);

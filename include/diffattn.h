@@ -346,7 +346,8 @@ size_t diffattn_bwd_workspace_size(int batch, int heads, int seq_q);
  * (same inputs and options), by the chain rule through "Noise-Canceling Attention by
  * Subtraction", sections "The mechanism" and "Making lambda learnable and stable": the RMSNorm *
  * (1 - lambda_init) epilogue, the difference of the two maps, the two softmaxes and the products.
- *  dout: [batch, seq_q, heads, dv];  lse, maps: the training forward's outputs for these inputs.
+ *  dout: [batch, seq_q, heads, dv];  lse, maps: the training forward's outputs for these inputs
+ *  (maps 16-byte aligned, as diffattn_fwd_train requires).
  *  dq1, dq2: [batch, seq_q, heads, d];  dk1, dk2: [batch, seq_k, heads, d];  dv: like v; all
  *  written (bf16), fp32 accumulation inside.
  *  dlambda: DEVICE fp32 [heads] or NULL, written with dL/dlambda_h.  dnorm_w: DEVICE fp32 [dv] or
@@ -401,7 +402,8 @@ size_t diffattn_v2_bwd_workspace_size(int batch, int h, int seq);
  * (same inputs and options), by the chain rule through "softmax can't say zero, so it subtracts",
  * section "DIFF V2: what the authors changed" (out_p = A_{2p} V - lambda A_{2p+1} V with the
  * pair's GQA K and V, no norm): both softmaxes, the difference and the products.
- *  dout: [batch, seq, h, d];  lse, maps: the training forward's outputs for these inputs.
+ *  dout: [batch, seq, h, d];  lse, maps: the training forward's outputs for these inputs
+ *  (maps 16-byte aligned, as diffattn_v2_fwd_train requires).
  *  dq: like q ([batch, seq, 2h, d]);  dk, dv: like k and v ([batch, seq, h_kv, d]), each summed
  *  over the query heads of its group; all written (bf16), fp32 accumulation inside.
  *  dlam: DEVICE fp32 [batch, seq, h], written with dL/dlam for what lam holds: dL/dlambda for
