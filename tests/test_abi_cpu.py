@@ -225,6 +225,7 @@ def _bwd(L, B=1, H=2, N=64, d=64, dv=128, dtype=1, lse=FAKE, maps=FAKE, lam=FAKE
 def test_bwd_rejects(L):
     assert _bwd(L, lse=None) == da.DIFFATTN_ERR_ARG
     assert _bwd(L, maps=None) == da.DIFFATTN_ERR_ARG
+    assert _bwd(L, maps=FAKE + 4) == da.DIFFATTN_ERR_ARG                 # maps not 16-byte aligned
     assert _bwd(L, lam=None) == da.DIFFATTN_ERR_ARG
     assert _bwd(L, N=0) == da.DIFFATTN_ERR_ARG
     assert _bwd(L, N=65, Nk=64) == da.DIFFATTN_ERR_ARG                   # causal with seq_q > seq_k
@@ -236,6 +237,22 @@ def test_bwd_rejects(L):
     assert _bwd(L, d=32) == da.DIFFATTN_ERR_UNSUPPORTED
     assert _bwd(L, dtype=0) == da.DIFFATTN_ERR_UNSUPPORTED               # fp32: no backward kernel
     assert L.diffattn_bwd_workspace_size(0, 2, 64) == 0
+
+
+def _v2_bwd(L, lse=FAKE, maps=FAKE, lam=FAKE, dlam=FAKE, h=4, h_kv=2, d=128, seq=64, ws_bytes=1 << 30, ws=FAKE):
+    ts = [_t(FAKE, 1 << 20, 1024, 128) for _ in range(7)]
+    return L.diffattn_v2_bwd(1, *ts[:4], lam, 0, 1, seq, h, h_kv, d, 1, 0.0, lse, maps, *ts[4:], dlam, ws, ws_bytes,
+                             None)
+
+
+def test_v2_bwd_rejects(L):
+    for kw in ({"lse": None}, {"maps": None}, {"lam": None}, {"dlam": None}, {"seq": 0}, {"h_kv": 3},
+               {"maps": FAKE + 4}, {"ws": FAKE + 32}):
+        assert _v2_bwd(L, **kw) == da.DIFFATTN_ERR_ARG, kw
+    need = L.diffattn_v2_bwd_workspace_size(1, 4, 64)
+    assert need > 0
+    assert _v2_bwd(L, ws_bytes=need - 1) == da.DIFFATTN_ERR_WORKSPACE
+    assert _v2_bwd(L, d=64) == da.DIFFATTN_ERR_UNSUPPORTED
 
 
 def test_fwd_train_rejects(L):
