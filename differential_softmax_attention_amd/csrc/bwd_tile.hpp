@@ -14,6 +14,19 @@
 #include <utility>
 
 namespace diffattn {
+
+// Sum over the 32 lanes of the lane's half of the wave (lanes 0-31 or 32-63), for the row passes
+// that take two rows per wave: the DPP steps of wave_sum within each 16-lane row, then the row
+// swap with lane ^ 16. Every lane of a half ends with the same value.
+__device__ __forceinline__ float half_sum(float x) {
+    x += dpp_partner<0xB1>(x);
+    x += dpp_partner<0x4E>(x);
+    x += dpp_partner<0x141>(x);
+    x += dpp_partner<0x140>(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+}
+
 namespace bwdt {
 
 constexpr int kBN = 32;   // rows per tile

@@ -62,17 +62,6 @@ __device__ __forceinline__ float wave_sum(float x) {
     return combine_rows(x, [](float a, float b) { return a + b; });
 }
 
-// Sum over the 32 lanes of the lane's half of the wave (lanes 0-31 or 32-63): the DPP steps of
-// wave_sum within each 16-lane row, then the row swap with lane ^ 16. Every lane of a half ends
-// with the same value.
-__device__ __forceinline__ float half_sum(float x) {
-    x += dpp_partner<0xB1>(x);
-    x += dpp_partner<0x4E>(x);
-    x += dpp_partner<0x141>(x);
-    x += dpp_partner<0x140>(x);
-    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-}
 // 1 / (1 + e^-z): DIFF V2's per-token lambda from its projected logit. Saturates to 0 and 1 for
 // large |z| (e^-z overflowing to +inf gives 0).
 __device__ __forceinline__ float sigmoid_f32(float z) { return 1.f / (1.f + __expf(-z)); }
