@@ -250,15 +250,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int k_row = slot_row<kD>(tid), k_col = slot_chunk<kD>(tid);
     const int v_row0 = slot_row<kDV>(tid), v_row1 = v_row0 + 16;
     const int v_col0 = slot_chunk<kDV>(tid), v_col1 = slot_chunk<kDV>(tid + 256);
+    // the slots' byte offsets within a full tile, computed once; a ragged last tile recomputes them
+    // with its rows clamped
+    auto slot_offsets = [&](int last, uint32_t* o) __attribute__((always_inline)) {
+        o[0] = (uint32_t)(min(k_row, last) * a.k1s[1] + k_col * 8) * 2u;
+        o[1] = (uint32_t)(min(k_row, last) * a.k2s[1] + k_col * 8) * 2u;
+        o[2] = (uint32_t)(min(v_row0, last) * a.vs[1] + v_col0 * 8) * 2u;
+        o[3] = (uint32_t)(min(v_row1, last) * a.vs[1] + v_col1 * 8) * 2u;
+    };
+    uint32_t full_off[4];
+    slot_offsets(kBN - 1, full_off);
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         const int last = min(kBN, a.seq_k - kt * kBN) - 1;
         const uint32_t st = lds0 + stage * kKStage + wave_u * 1024;
-        const int kr = min(k_row, last);
-        dma16(k1b + (int64_t)kt * kBN * a.k1s[1], (uint32_t)(kr * a.k1s[1] + k_col * 8) * 2u, st);
-        dma16(k2b + (int64_t)kt * kBN * a.k2s[1], (uint32_t)(kr * a.k2s[1] + k_col * 8) * 2u, st + kKTile);
+        uint32_t o[4] = {full_off[0], full_off[1], full_off[2], full_off[3]};
+        if (__builtin_expect(last < kBN - 1, 0)) slot_offsets(last, o);
+        dma16(k1b + (int64_t)kt * kBN * a.k1s[1], o[0], st);
+        dma16(k2b + (int64_t)kt * kBN * a.k2s[1], o[1], st + kKTile);
         const bf16* vt = vb + (int64_t)kt * kBN * a.vs[1];
-        dma16(vt, (uint32_t)(min(v_row0, last) * a.vs[1] + v_col0 * 8) * 2u, st + 2 * kKTile);
-        dma16(vt, (uint32_t)(min(v_row1, last) * a.vs[1] + v_col1 * 8) * 2u, st + 2 * kKTile + 4096);
+        dma16(vt, o[2], st + 2 * kKTile);
+        dma16(vt, o[3], st + 2 * kKTile + 4096);
     };
 
     // one key tile; !full: some (query, key) pair of the wave's 32 x 32 block is not visible
@@ -405,16 +416,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int q_row = slot_row<kD>(tid), q_col = slot_chunk<kD>(tid);
     const int g_row0 = slot_row<kDV>(tid), g_row1 = g_row0 + 16;
     const int g_col0 = slot_chunk<kDV>(tid), g_col1 = slot_chunk<kDV>(tid + 256);
+    // the slots' byte offsets within a full tile, computed once; a ragged last tile recomputes them
+    // with its rows clamped
+    auto slot_offsets = [&](int last, uint32_t* o) __attribute__((always_inline)) {
+        o[0] = (uint32_t)(min(q_row, last) * a.q1s[1] + q_col * 8) * 2u;
+        o[1] = (uint32_t)(min(q_row, last) * a.q2s[1] + q_col * 8) * 2u;
+        o[2] = (uint32_t)(min(g_row0, last) * kDV + g_col0 * 8) * 2u;
+        o[3] = (uint32_t)(min(g_row1, last) * kDV + g_col1 * 8) * 2u;
+    };
+    uint32_t full_off[4];
+    slot_offsets(kBN - 1, full_off);
     auto issue_q = [&](int qt, int stage) __attribute__((always_inline)) {
         const int i0 = qt * kBN;
         const int last = min(kBN, a.seq_q - i0) - 1;
         const uint32_t st = lds_sq + stage * kQStage + wave * 1024;
-        const int qr = min(q_row, last);
-        dma16(q1b + (int64_t)i0 * a.q1s[1], (uint32_t)(qr * a.q1s[1] + q_col * 8) * 2u, st);
-        dma16(q2b + (int64_t)i0 * a.q2s[1], (uint32_t)(qr * a.q2s[1] + q_col * 8) * 2u, st + kKTile);
+        uint32_t o[4] = {full_off[0], full_off[1], full_off[2], full_off[3]};
+        if (__builtin_expect(last < kBN - 1, 0)) slot_offsets(last, o);
+        dma16(q1b + (int64_t)i0 * a.q1s[1], o[0], st);
+        dma16(q2b + (int64_t)i0 * a.q2s[1], o[1], st + kKTile);
         const bf16* gb = a.go + (rowb + i0) * kDV;
-        dma16(gb, (uint32_t)(min(g_row0, last) * kDV + g_col0 * 8) * 2u, st + 2 * kKTile);
-        dma16(gb, (uint32_t)(min(g_row1, last) * kDV + g_col1 * 8) * 2u, st + 2 * kKTile + 4096);
+        dma16(gb, o[2], st + 2 * kKTile);
+        dma16(gb, o[3], st + 2 * kKTile + 4096);
         if (wave == 0) {
             // lane i fetches float i of the tile's 32 rows x 2 (clamped to the last row)
             const uint32_t sst = lds_sq + stage * kQStage + kQStats;

@@ -165,15 +165,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int r0 = slot_row<kD>(tid), r1 = r0 + 16;
     const int c0 = slot_chunk<kD>(tid), c1 = slot_chunk<kD>(tid + 256);
+    // the slots' byte offsets within a full tile, computed once; a ragged last tile recomputes them
+    // with its rows clamped
+    auto slot_offsets = [&](int last, uint32_t* o) __attribute__((always_inline)) {
+        o[0] = (uint32_t)(min(r0, last) * a.ks[1] + c0 * 8) * 2u;
+        o[1] = (uint32_t)(min(r1, last) * a.ks[1] + c1 * 8) * 2u;
+        o[2] = (uint32_t)(min(r0, last) * a.vs[1] + c0 * 8) * 2u;
+        o[3] = (uint32_t)(min(r1, last) * a.vs[1] + c1 * 8) * 2u;
+    };
+    uint32_t full_off[4];
+    slot_offsets(kBN - 1, full_off);
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         const int last = min(kBN, a.seq - kt * kBN) - 1;
         const uint32_t st = lds0 + stage * kKStage + wave_u * 1024;
         const bf16* kt_p = kb0 + (int64_t)kt * kBN * a.ks[1];
         const bf16* vt_p = vb0 + (int64_t)kt * kBN * a.vs[1];
-        dma16(kt_p, (uint32_t)(min(r0, last) * a.ks[1] + c0 * 8) * 2u, st);
-        dma16(kt_p, (uint32_t)(min(r1, last) * a.ks[1] + c1 * 8) * 2u, st + 4096);
-        dma16(vt_p, (uint32_t)(min(r0, last) * a.vs[1] + c0 * 8) * 2u, st + kTile);
-        dma16(vt_p, (uint32_t)(min(r1, last) * a.vs[1] + c1 * 8) * 2u, st + kTile + 4096);
+        uint32_t o[4] = {full_off[0], full_off[1], full_off[2], full_off[3]};
+        if (__builtin_expect(last < kBN - 1, 0)) slot_offsets(last, o);
+        dma16(kt_p, o[0], st);
+        dma16(kt_p, o[1], st + 4096);
+        dma16(vt_p, o[2], st + kTile);
+        dma16(vt_p, o[3], st + kTile + 4096);
     };
 
     auto compute = [&](int slot, bool full, int k0) __attribute__((always_inline)) {
@@ -409,6 +421,16 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
     const uint32_t lds_sq = (uint32_t)(uintptr_t)(lds_u8_t*)sq;
     const int r0 = slot_row<kD>(tid), r1 = r0 + 16;
     const int c0 = slot_chunk<kD>(tid), c1 = slot_chunk<kD>(tid + 256);
+    // the slots' byte offsets within a full tile, computed once; a ragged last tile recomputes them
+    // with its rows clamped (Q_{2p} and Q_{2p+1} share theirs)
+    auto slot_offsets = [&](int last, uint32_t* o) __attribute__((always_inline)) {
+        o[0] = (uint32_t)(min(r0, last) * a.qs[1] + c0 * 8) * 2u;
+        o[1] = (uint32_t)(min(r1, last) * a.qs[1] + c1 * 8) * 2u;
+        o[2] = (uint32_t)(min(r0, last) * kD + c0 * 8) * 2u;
+        o[3] = (uint32_t)(min(r1, last) * kD + c1 * 8) * 2u;
+    };
+    uint32_t full_off[4];
+    slot_offsets(kBN - 1, full_off);
     auto issue = [&](int it, int stage) __attribute__((always_inline)) {
         const int qt = qbase + qstep * (it / npair), p = g * npair + it % npair;
         const int i0 = qt * kBN;
@@ -418,13 +440,14 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
         const bf16* q2b = q1b + a.qs[2];
         const int64_t rowb = ((int64_t)b * a.h + p) * a.seq + i0;
         const bf16* gb = a.go + rowb * kD;
-        const int ra = min(r0, last), rb = min(r1, last);
-        dma16(q1b, (uint32_t)(ra * a.qs[1] + c0 * 8) * 2u, st);
-        dma16(q1b, (uint32_t)(rb * a.qs[1] + c1 * 8) * 2u, st + 4096);
-        dma16(q2b, (uint32_t)(ra * a.qs[1] + c0 * 8) * 2u, st + kQ2Off);
-        dma16(q2b, (uint32_t)(rb * a.qs[1] + c1 * 8) * 2u, st + kQ2Off + 4096);
-        dma16(gb, (uint32_t)(ra * kD + c0 * 8) * 2u, st + kGOff);
-        dma16(gb, (uint32_t)(rb * kD + c1 * 8) * 2u, st + kGOff + 4096);
+        uint32_t o[4] = {full_off[0], full_off[1], full_off[2], full_off[3]};
+        if (__builtin_expect(last < kBN - 1, 0)) slot_offsets(last, o);
+        dma16(q1b, o[0], st);
+        dma16(q1b, o[1], st + 4096);
+        dma16(q2b, o[0], st + kQ2Off);
+        dma16(q2b, o[1], st + kQ2Off + 4096);
+        dma16(gb, o[2], st + kGOff);
+        dma16(gb, o[3], st + kGOff + 4096);
         if (wave == 0) {
             const uint32_t sst = lds_sq + kStOff + stage * kStSlot;
             const uint32_t fo = (uint32_t)min(lane, 2 * last + 1) * 4u;
