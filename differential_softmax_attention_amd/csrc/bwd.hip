@@ -409,9 +409,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16* q2b = (const bf16*)a.q2 + b * a.q2s[0] + (int64_t)h * a.q2s[2];
     const int64_t rowb = ((int64_t)b * a.heads + h) * a.seq_q;
 
-    // query-tile DMA: thread tid fills Q1 and Q2 slot tid and go slots tid, tid + 256; wave 0 also
-    // fetches the rows' log-sum-exp and D values (64 floats each). Rows past the last query are
-    // fetched from the last one (their weights are masked to zero).
+    // query-tile DMA: thread tid fills Q1 and Q2 slot tid and go slots tid, tid + 256; waves 1 and
+    // 2 also fetch the rows' log-sum-exp and D values (64 floats each). Rows past the last query
+    // are fetched from the last one (their weights are masked to zero).
     const uint32_t lds_sq = (uint32_t)(uintptr_t)(lds_u8_t*)sq;
     const int q_row = slot_row<kD>(tid), q_col = slot_chunk<kD>(tid);
     const int g_row0 = slot_row<kDV>(tid), g_row1 = g_row0 + 16;
@@ -437,12 +437,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bf16* gb = a.go + (rowb + i0) * kDV;
         dma16(gb, o[2], st + 2 * kKTile);
         dma16(gb, o[3], st + 2 * kKTile + 4096);
-        if (wave == 0) {
-            // lane i fetches float i of the tile's 32 rows x 2 (clamped to the last row)
-            const uint32_t sst = lds_sq + stage * kQStage + kQStats;
+        if (wave == 1 || wave == 2) {
+            // lane i fetches float i of the tile's 32 rows x 2 (clamped to the last row): the
+            // log-sum-exp by wave 1 and D by wave 2, so that no wave issues more DMA than the rest
+            const uint32_t sst = lds_sq + stage * kQStage + kQStats + (wave - 1) * 256;
             const uint32_t fo = (uint32_t)min(lane, 2 * last + 1) * 4u;
-            dma4(a.lse + 2 * (rowb + i0), fo, sst);
-            dma4(a.dd + 2 * (rowb + i0), fo, sst + 256);
+            dma4((wave == 1 ? a.lse : a.dd) + 2 * (rowb + i0), fo, sst);
         }
     };
 

@@ -415,9 +415,9 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
     const int nit = (nqt - qt0) * npair;
     const int qbase = down ? nqt - 1 : qt0, qstep = down ? -1 : 1;
 
-    // stage DMA: thread tid fills Q_{2p}, Q_{2p+1} and go_p slots tid and tid + 256; wave 0 also
-    // fetches the rows' log-sum-exp and D (64 floats each) and lambda (32 floats). Rows past the
-    // last query are fetched from the last one (their weights are masked to zero).
+    // stage DMA: thread tid fills Q_{2p}, Q_{2p+1} and go_p slots tid and tid + 256; waves 1, 2 and
+    // 3 also fetch the rows' log-sum-exp and D (64 floats each) and lambda (32 floats), one each.
+    // Rows past the last query are fetched from the last one (their weights are masked to zero).
     const uint32_t lds_sq = (uint32_t)(uintptr_t)(lds_u8_t*)sq;
     const int r0 = slot_row<kD>(tid), r1 = r0 + 16;
     const int c0 = slot_chunk<kD>(tid), c1 = slot_chunk<kD>(tid + 256);
@@ -448,12 +448,14 @@ __device__ __attribute__((always_inline)) inline void dkdv_key_tile(const V2BwdA
         dma16(q2b, o[1], st + kQ2Off + 4096);
         dma16(gb, o[2], st + kGOff);
         dma16(gb, o[3], st + kGOff + 4096);
-        if (wave == 0) {
-            const uint32_t sst = lds_sq + kStOff + stage * kStSlot;
-            const uint32_t fo = (uint32_t)min(lane, 2 * last + 1) * 4u;
-            dma4(a.lse + 2 * rowb, fo, sst);
-            dma4(a.dd + 2 * rowb, fo, sst + 256);
-            dma4(a.lamr + rowb, (uint32_t)min(lane, last) * 4u, sst + 512);
+        if (wave != 0) {   // one statistics DMA each for waves 1, 2 and 3
+            const uint32_t sst = lds_sq + kStOff + stage * kStSlot + (wave - 1) * 256;
+            if (wave == 3) {
+                dma4(a.lamr + rowb, (uint32_t)min(lane, last) * 4u, sst);
+            } else {
+                const uint32_t fo = (uint32_t)min(lane, 2 * last + 1) * 4u;
+                dma4((wave == 1 ? a.lse : a.dd) + 2 * rowb, fo, sst);
+            }
         }
     };
 
