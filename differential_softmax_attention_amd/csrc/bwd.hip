@@ -13,7 +13,7 @@
 // from the scores) and A_k V (for D_k and o).
 //
 // Kernels (no atomics; every sum is taken in a fixed order):
-//  - bwd_pre: one wave per row: o, go (stored bf16 as an MFMA operand), D1, D2, and per-block
+//  - bwd_pre: half a wave per row: o, go (stored bf16 as an MFMA operand), D1, D2, and per-block
 //    partial sums of dL/dw and dlambda.
 //  - bwd_dq: query-tile parallel like the forward (S^T = K Q^T, lane = query): K1, K2, V tiles of
 //    32 keys staged through LDS, one block barrier per pair of tiles; dP^T = V go^T;

@@ -12,7 +12,7 @@
 // The training forward supplies each head's log-sum-exp and A_k V.
 //
 // Kernels (no atomics; every sum in a fixed order):
-//  - bwd_v2_pre: one wave per (row, pair): go (a copy of dout, head-major for the DMA), D_1, D_2,
+//  - bwd_v2_pre: half a wave per (row, pair): go (a copy of dout, head-major for the DMA), D_1, D_2,
 //    lambda after the sigmoid, and dlambda.
 //  - bwd_v2_dq: 32 queries of one pair per wave, walking key tiles (K and V of the group through
 //    a four-slot LDS ring, two tiles per block barrier); each K row fragment feeds both heads'
