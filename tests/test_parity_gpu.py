@@ -118,6 +118,14 @@ def test_bf16_v1_rect(Nq, Nk, causal):
     assert maxerr(out, ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("Nq,Nk,causal", [(50, 4500, True), (50, 4500, False), (300, 4133, True)])
+def test_bf16_v1_rect_long_keys(Nq, Nk, causal):
+    # from 4096 keys the launches take the kernels built under the max-ilp schedule; a few query
+    # tiles against a ragged key range
+    out, ref = v1_case(1, Nq, Nk, 2, 64, 128, torch.bfloat16, 450 + Nq, causal=causal, epilogue=True)
+    assert maxerr(out, ref) <= TOL_BF16
+
+
 def test_bf16_v1_options():
     out, ref = v1_case(2, 150, 150, 2, 64, 128, torch.bfloat16, 500, causal=True, epilogue=True,
                        norm=True, scale=0.2, li=0.6, eps=1e-3, lam=[-0.4, 1.3])
@@ -277,6 +285,13 @@ def test_v2_shapes(N):
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 4), (32, 2), (8, 1)])
 def test_v2_groupings(hq, hkv):
     out, ref = v2_case(1, 70, hq, hkv, 128, 1100 + hq, causal=(hq != 8))
+    assert maxerr(out, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("N,causal", [(4200, True), (4133, False)])
+def test_v2_long_keys(N, causal):
+    # the V2 kernel built under the max-ilp schedule (4096 keys and more), ragged last tile
+    out, ref = v2_case(1, N, 4, 2, 128, 1300 + N, causal=causal)
     assert maxerr(out, ref) <= TOL_BF16
 
 
