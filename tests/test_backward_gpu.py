@@ -83,6 +83,17 @@ def test_bwd_causal_epilogue(N):
     close(g["dnorm_w"], ref["dg"], "dnorm_w")
 
 
+@pytest.mark.parametrize("B,H,N", [(3, 5, 97), (2, 7, 65)])
+def test_bwd_batches_and_heads(B, H, N):
+    # several (batch, head) slices, row counts that leave a row pass block part full: the
+    # per-block partials of dlambda and dL/dw and their fixed-order sums over batch and heads
+    out, lse, maps, g, ref = run(case(B, N, N, H, 3400 + 10 * B + H, causal=True, epilogue=True, norm=True))
+    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
+        close(g[k], ref[k], k)
+    close(g["dlam"], ref["dlam"], "dlam")
+    close(g["dnorm_w"], ref["dg"], "dnorm_w")
+
+
 @pytest.mark.parametrize("Nq,Nk,causal", [(64, 64, False), (70, 130, True), (40, 200, False), (300, 260, False), (200, 330, True)])
 def test_bwd_noepi_and_rect(Nq, Nk, causal):
     out, lse, maps, g, ref = run(case(1, Nq, Nk, 3, 3200 + Nq + Nk, causal=causal, epilogue=False))

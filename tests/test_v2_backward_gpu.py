@@ -77,6 +77,12 @@ def test_v2_bwd_causal(N):
     check(g, ref)
 
 
+def test_v2_bwd_batches():
+    # three batch items and a row count that leaves a row pass block part full
+    *_, g, ref = run(case(3, 97, 8, 2, 5600))
+    check(g, ref)
+
+
 @pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (16, 2), (32, 2)])
 def test_v2_bwd_groupings(hq, hkv):
     # 1, 4, 4 and 8 pairs per KV head: dK and dV sum over every head of the group
